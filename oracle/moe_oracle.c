@@ -1,0 +1,427 @@
+/*
+ * moe_oracle.c -- plain CPU reference of the sparse-MoE FFN layer forward
+ * pass.  TEST INFRASTRUCTURE ONLY (see moe_oracle.h): used by the tests, the
+ * smoke check and the benchmark's CPU-baseline leg, never by the product.
+ *
+ * Sources (web pages on sparse Mixture-of-Experts):
+ *  [MoE-notes]  "Mixture-of-Experts (MoE)", ML notes quoting DeepSeekMoE:
+ *               the MoE-layer equation h_t = sum_i g_{i,t} FFN_i(u_t) + u_t,
+ *               g = s if s is among the Top-K affinities else 0,
+ *               s = Softmax_i(u_t^T e_i).
+ *  [LLM-sys]    "MoE: Choosing Which MLPs to Use for Each Token":
+ *               Figure 1 (gated-MLP experts with Gate, Up, Down weights),
+ *               Figure 2 (Router: top-2 then softmax over the two scores),
+ *               Figure 3 (Router -> Dispatch -> Expert -> Combine),
+ *               Figure 4 (shared expert: y = S(x) + R(x)).
+ *  [Noisy-topk] "Noise Top-k Gating": Gaussian noise scaled by W_noise is
+ *               added to the logits before the top-k selection.
+ *  [Glossary]   "Mixture of Experts (MoE)" glossary: expert capacity =
+ *               (tokens per batch / experts) * capacity factor; overflow is
+ *               dropped and takes the residual bypass.
+ *  [Switch]     "Switch Transformers ... explained", "Making it work":
+ *               overflow tokens skip the layer; higher router precision.
+ *
+ * Build: plain C11, -O2 -ffp-contract=off, no fast-math (oracle/build.py).
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* element access                                                      */
+/* ------------------------------------------------------------------ */
+
+/* A bf16 value is the upper half of an IEEE binary32 pattern. */
+static double bf16_to_double(uint16_t h) {
+  uint32_t w = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+static double load_elem(const void* base, int dtype, size_t i) {
+  if (dtype == OR_BF16) return bf16_to_double(((const uint16_t*)base)[i]);
+  return (double)((const float*)base)[i];
+}
+
+/* dot(a[0..n), b[0..n)) in double, summed left to right */
+static double dot_elems(const void* a, size_t a_off, const void* b,
+                        size_t b_off, int dtype, int n) {
+  double acc = 0.0;
+  if (dtype == OR_BF16) {
+    const uint16_t* pa = (const uint16_t*)a + a_off;
+    const uint16_t* pb = (const uint16_t*)b + b_off;
+    for (int j = 0; j < n; ++j) acc += bf16_to_double(pa[j]) * bf16_to_double(pb[j]);
+  } else {
+    const float* pa = (const float*)a + a_off;
+    const float* pb = (const float*)b + b_off;
+    for (int j = 0; j < n; ++j) acc += (double)pa[j] * (double)pb[j];
+  }
+  return acc;
+}
+
+/* dot of a double vector with stored elements */
+static double dot_dbl_elems(const double* a, const void* b, size_t b_off,
+                            int dtype, int n) {
+  double acc = 0.0;
+  if (dtype == OR_BF16) {
+    const uint16_t* pb = (const uint16_t*)b + b_off;
+    for (int j = 0; j < n; ++j) acc += a[j] * bf16_to_double(pb[j]);
+  } else {
+    const float* pb = (const float*)b + b_off;
+    for (int j = 0; j < n; ++j) acc += a[j] * (double)pb[j];
+  }
+  return acc;
+}
+
+double oracle_round_bf16(double v) {
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  int e;
+  (void)frexp(fabs(v), &e);          /* |v| = m * 2^e, m in [0.5, 1) */
+  int q = e - 8;                     /* weight of the 8th significant bit */
+  if (q < -133) q = -133;            /* below 2^-126: subnormal step 2^-133 */
+  double r = nearbyint(ldexp(fabs(v), -q));  /* default mode: ties to even */
+  double out = ldexp(r, q);
+  if (out >= ldexp(1.0, 128)) out = INFINITY;
+  return copysign(out, v);
+}
+
+/* round a value to the storage type of the expert path */
+static double round_storage(double v, int dtype) {
+  if (dtype == OR_BF16) return oracle_round_bf16(v);
+  return (double)(float)v;
+}
+
+/* ------------------------------------------------------------------ */
+/* threads: contiguous static partition of [0, n)                       */
+/* ------------------------------------------------------------------ */
+
+typedef void (*range_fn)(void* ctx, int begin, int end);
+typedef struct { range_fn fn; void* ctx; int begin, end; } range_job;
+
+static void* range_entry(void* arg) {
+  range_job* j = (range_job*)arg;
+  j->fn(j->ctx, j->begin, j->end);
+  return NULL;
+}
+
+static void parallel_for(int n, int nthreads, range_fn fn, void* ctx) {
+  if (n <= 0) return;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n) nthreads = n;
+  if (nthreads == 1) { fn(ctx, 0, n); return; }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  range_job* jobs = (range_job*)malloc(sizeof(range_job) * (size_t)nthreads);
+  int started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i].fn = fn;
+    jobs[i].ctx = ctx;
+    jobs[i].begin = (int)((long long)n * i / nthreads);
+    jobs[i].end = (int)((long long)n * (i + 1) / nthreads);
+    if (pthread_create(&th[i], NULL, range_entry, &jobs[i]) == 0) {
+      ++started;
+    } else {                         /* no thread: do the range here */
+      fn(ctx, jobs[i].begin, jobs[i].end);
+      th[i] = (pthread_t)0;
+      jobs[i].fn = NULL;
+    }
+  }
+  for (int i = 0; i < nthreads; ++i)
+    if (jobs[i].fn) pthread_join(th[i], NULL);
+  (void)started;
+  free(th);
+  free(jobs);
+}
+
+/* ------------------------------------------------------------------ */
+/* router logits  [MoE-notes] affinity u_t^T e_i; [Noisy-topk] noise    */
+/* ------------------------------------------------------------------ */
+
+typedef struct { const oracle_problem* p; const oracle_inputs* in; float* H; } logits_ctx;
+
+static void logits_range(void* vctx, int t0, int t1) {
+  logits_ctx* c = (logits_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  const oracle_inputs* in = c->in;
+  for (int t = t0; t < t1; ++t) {
+    for (int i = 0; i < p->N; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < p->d; ++j)
+        acc += load_elem(in->u, p->dtype, (size_t)t * p->d + j) *
+               (double)in->w_router[(size_t)i * p->d + j];
+      if (in->b_router) acc += (double)in->b_router[i];
+      if (in->noise)
+        acc += (double)p->noise_weight * (double)in->noise[(size_t)t * p->N + i];
+      c->H[(size_t)t * p->N + i] = (float)acc;   /* the router's fp32 output */
+    }
+  }
+}
+
+void oracle_router_logits(const oracle_problem* p, const oracle_inputs* in,
+                          float* H, int nthreads) {
+  logits_ctx c = {p, in, H};
+  parallel_for(p->T, nthreads, logits_range, &c);
+}
+
+/* ------------------------------------------------------------------ */
+/* routing  [MoE-notes] softmax, Top-K, gates; [LLM-sys] Figure 2       */
+/* ------------------------------------------------------------------ */
+
+void oracle_route(const oracle_problem* p, const float* H, int32_t* topk_idx,
+                  double* topk_gate, double* lse_sq, double* mean_prob,
+                  double* probs) {
+  const int N = p->N, K = p->K;
+  double* s = (double*)malloc(sizeof(double) * (size_t)N);
+  unsigned char* taken = (unsigned char*)malloc((size_t)N);
+  double* psum = (double*)calloc((size_t)N, sizeof(double));
+  for (int t = 0; t < p->T; ++t) {
+    const float* h = H + (size_t)t * N;
+    /* affinity s_i = softmax over all N experts */
+    double m = (double)h[0];
+    for (int i = 1; i < N; ++i)
+      if ((double)h[i] > m) m = (double)h[i];
+    double Z = 0.0;
+    for (int i = 0; i < N; ++i) Z += exp((double)h[i] - m);
+    for (int i = 0; i < N; ++i) {
+      s[i] = exp((double)h[i] - m) / Z;
+      psum[i] += s[i];
+      if (probs) probs[(size_t)t * N + i] = s[i];
+    }
+    if (lse_sq) {
+      double lse = m + log(Z);
+      lse_sq[t] = lse * lse;
+    }
+    /* the K highest scores: K rounds of "largest remaining, lowest index
+     * on ties" (a strict > while scanning upwards keeps the lower index) */
+    memset(taken, 0, (size_t)N);
+    for (int k = 0; k < K; ++k) {
+      int best = -1;
+      for (int i = 0; i < N; ++i) {
+        if (taken[i]) continue;
+        if (best < 0 || h[i] > h[best]) best = i;
+      }
+      taken[best] = 1;
+      topk_idx[(size_t)t * K + k] = best;
+    }
+    /* gates */
+    if (p->gating == OR_GATE_SOFTMAX_TOPK) {
+      for (int k = 0; k < K; ++k)
+        topk_gate[(size_t)t * K + k] = s[topk_idx[(size_t)t * K + k]];
+    } else {
+      const double h0 = (double)h[topk_idx[(size_t)t * K]];  /* the largest */
+      double zk = 0.0;
+      for (int k = 0; k < K; ++k) zk += exp((double)h[topk_idx[(size_t)t * K + k]] - h0);
+      for (int k = 0; k < K; ++k)
+        topk_gate[(size_t)t * K + k] = exp((double)h[topk_idx[(size_t)t * K + k]] - h0) / zk;
+    }
+  }
+  if (mean_prob)
+    for (int i = 0; i < N; ++i) mean_prob[i] = p->T > 0 ? psum[i] / (double)p->T : 0.0;
+  free(s);
+  free(taken);
+  free(psum);
+}
+
+/* ------------------------------------------------------------------ */
+/* capacity and dispatch  [Glossary] capacity; [LLM-sys] Figure 3       */
+/* ------------------------------------------------------------------ */
+
+int32_t oracle_capacity(int32_t T, int32_t K, int32_t N, float cf) {
+  if (!(cf > 0.0f)) return -1;
+  double c = ceil((double)cf * (double)((int64_t)T * K) / (double)N);
+  if (c > (double)T) c = (double)T;
+  return (int32_t)c;
+}
+
+void oracle_dispatch(const oracle_problem* p, const int32_t* topk_idx,
+                     int32_t capacity, int32_t* expert_counts,
+                     int32_t* kept_counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* token_of_row) {
+  const int N = p->N, K = p->K, T = p->T;
+  int32_t* rank = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+  for (int e = 0; e < N; ++e) expert_counts[e] = 0;
+  /* first come, first served in ascending token order */
+  for (int t = 0; t < T; ++t)
+    for (int k = 0; k < K; ++k) {
+      int e = topk_idx[(size_t)t * K + k];
+      rank[(size_t)t * K + k] = expert_counts[e]++;
+    }
+  for (int e = 0; e < N; ++e)
+    kept_counts[e] = (capacity >= 0 && expert_counts[e] > capacity) ? capacity : expert_counts[e];
+  offsets[0] = 0;
+  for (int e = 0; e < N; ++e) offsets[e + 1] = offsets[e] + kept_counts[e];
+  for (size_t r = 0; r < (size_t)T * K; ++r) token_of_row[r] = -1;
+  for (int t = 0; t < T; ++t)
+    for (int k = 0; k < K; ++k) {
+      int e = topk_idx[(size_t)t * K + k];
+      int32_t rk = rank[(size_t)t * K + k];
+      if (capacity >= 0 && rk >= capacity) {
+        row_of[(size_t)t * K + k] = -1;          /* overflow: dropped */
+      } else {
+        int32_t row = offsets[e] + rk;
+        row_of[(size_t)t * K + k] = row;
+        token_of_row[row] = t;
+      }
+    }
+  free(rank);
+}
+
+/* ------------------------------------------------------------------ */
+/* expert FFN  [LLM-sys] Figure 1 gated MLP; [MoE-notes] FFN_i          */
+/* ------------------------------------------------------------------ */
+
+/* Unrounded output of one FFN of width dff on vector x (stored at x_off
+ * elements into x): act rounded to storage, y in double. */
+static void ffn_one(int d, int dff, int act_kind, int dtype, const void* x,
+                    size_t x_off, const void* wg, const void* wu,
+                    const void* wd, size_t wg_off, size_t wd_off, double* act,
+                    double* y) {
+  for (int f = 0; f < dff; ++f) {
+    double a;
+    double g = dot_elems(x, x_off, wg, wg_off + (size_t)f * d, dtype, d);
+    if (act_kind == OR_ACT_SWIGLU) {
+      double up = dot_elems(x, x_off, wu, wg_off + (size_t)f * d, dtype, d);
+      double silu = g / (1.0 + exp(-g));
+      a = silu * up;
+    } else {
+      a = g > 0.0 ? g : 0.0;
+    }
+    act[f] = round_storage(a, dtype);
+  }
+  for (int j = 0; j < d; ++j)
+    y[j] = dot_dbl_elems(act, wd, wd_off + (size_t)j * dff, dtype, dff);
+}
+
+/* routed expert e (e >= 0) or the sum of all shared experts (e == -1),
+ * rounded once to storage */
+static void expert_output(const oracle_problem* p, const oracle_inputs* in,
+                          int e, const void* x, size_t x_off, double* act,
+                          double* ytmp, double* y) {
+  const int d = p->d;
+  if (e >= 0) {
+    ffn_one(d, p->d_ff, p->act, p->dtype, x, x_off, in->w_gate, in->w_up,
+            in->w_down, (size_t)e * p->d_ff * d, (size_t)e * d * p->d_ff, act, y);
+  } else {
+    for (int j = 0; j < d; ++j) y[j] = 0.0;
+    for (int s = 0; s < p->n_shared; ++s) {
+      ffn_one(d, p->d_ff_shared, p->act, p->dtype, x, x_off, in->ws_gate,
+              in->ws_up, in->ws_down, (size_t)s * p->d_ff_shared * d,
+              (size_t)s * d * p->d_ff_shared, act, ytmp);
+      for (int j = 0; j < d; ++j) y[j] += ytmp[j];
+    }
+  }
+  for (int j = 0; j < d; ++j) y[j] = round_storage(y[j], p->dtype);
+}
+
+static int max_width(const oracle_problem* p) {
+  int w = p->d_ff;
+  if (p->n_shared > 0 && p->d_ff_shared > w) w = p->d_ff_shared;
+  return w;
+}
+
+typedef struct {
+  const oracle_problem* p; const oracle_inputs* in;
+  const void* x; const int32_t* expert_of_row; double* y;
+} ffn_rows_ctx;
+
+static void ffn_rows_range(void* vctx, int r0, int r1) {
+  ffn_rows_ctx* c = (ffn_rows_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  double* act = (double*)malloc(sizeof(double) * (size_t)max_width(p));
+  double* ytmp = (double*)malloc(sizeof(double) * (size_t)p->d);
+  for (int r = r0; r < r1; ++r)
+    expert_output(p, c->in, c->expert_of_row[r], c->x, (size_t)r * p->d, act,
+                  ytmp, c->y + (size_t)r * p->d);
+  free(act);
+  free(ytmp);
+}
+
+void oracle_ffn_rows(const oracle_problem* p, const oracle_inputs* in,
+                     int32_t n_rows, const void* x, const int32_t* expert_of_row,
+                     double* y, int nthreads) {
+  ffn_rows_ctx c = {p, in, x, expert_of_row, y};
+  parallel_for(n_rows, nthreads, ffn_rows_range, &c);
+}
+
+/* ------------------------------------------------------------------ */
+/* combine  [MoE-notes] layer equation; [LLM-sys] Figures 3 and 4;     */
+/* [Glossary]/[Switch] dropped assignments contribute nothing           */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+  const oracle_problem* p; const oracle_inputs* in;
+  const int32_t* topk_idx; const double* topk_gate; const int32_t* row_of;
+  const int32_t* tokens; double* out;
+} layer_ctx;
+
+static void layer_range(void* vctx, int r0, int r1) {
+  layer_ctx* c = (layer_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  const int d = p->d, K = p->K;
+  double* act = (double*)malloc(sizeof(double) * (size_t)max_width(p));
+  double* ytmp = (double*)malloc(sizeof(double) * (size_t)d);
+  double* y = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int r = r0; r < r1; ++r) {
+    int t = c->tokens ? c->tokens[r] : r;
+    double* o = c->out + (size_t)r * d;
+    size_t u_off = (size_t)t * d;
+    for (int j = 0; j < d; ++j) o[j] = load_elem(c->in->u, p->dtype, u_off + j);
+    for (int k = 0; k < K; ++k) {
+      if (c->row_of[(size_t)t * K + k] < 0) continue;   /* dropped */
+      int e = c->topk_idx[(size_t)t * K + k];
+      double g = c->topk_gate[(size_t)t * K + k];
+      expert_output(p, c->in, e, c->in->u, u_off, act, ytmp, y);
+      for (int j = 0; j < d; ++j) o[j] += g * y[j];
+    }
+    if (p->n_shared > 0) {
+      expert_output(p, c->in, -1, c->in->u, u_off, act, ytmp, y);
+      for (int j = 0; j < d; ++j) o[j] += y[j];
+    }
+  }
+  free(act);
+  free(ytmp);
+  free(y);
+}
+
+void oracle_layer_rows(const oracle_problem* p, const oracle_inputs* in,
+                       const int32_t* topk_idx, const double* topk_gate,
+                       const int32_t* row_of, int32_t n_tokens,
+                       const int32_t* tokens, double* out, int nthreads) {
+  layer_ctx c = {p, in, topk_idx, topk_gate, row_of, tokens, out};
+  parallel_for(n_tokens, nthreads, layer_range, &c);
+}
+
+void oracle_layer_forward(const oracle_problem* p, const oracle_inputs* in,
+                          float* H, int32_t* topk_idx, double* topk_gate,
+                          double* lse_sq, double* mean_prob,
+                          int32_t* expert_counts, int32_t* kept_counts,
+                          int32_t* offsets, int32_t* row_of,
+                          int32_t* token_of_row, double* out, int nthreads) {
+  const size_t T = (size_t)p->T, N = (size_t)p->N, K = (size_t)p->K;
+  float* h = H ? H : (float*)malloc(sizeof(float) * (T * N + 1));
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)malloc(sizeof(int32_t) * (T * K + 1));
+  double* gate = topk_gate ? topk_gate : (double*)malloc(sizeof(double) * (T * K + 1));
+  int32_t* cnt = expert_counts ? expert_counts : (int32_t*)malloc(sizeof(int32_t) * N);
+  int32_t* kept = kept_counts ? kept_counts : (int32_t*)malloc(sizeof(int32_t) * N);
+  int32_t* off = offsets ? offsets : (int32_t*)malloc(sizeof(int32_t) * (N + 1));
+  int32_t* rof = row_of ? row_of : (int32_t*)malloc(sizeof(int32_t) * (T * K + 1));
+  int32_t* tor = token_of_row ? token_of_row : (int32_t*)malloc(sizeof(int32_t) * (T * K + 1));
+
+  oracle_router_logits(p, in, h, nthreads);
+  oracle_route(p, h, idx, gate, lse_sq, mean_prob, NULL);
+  int32_t C = oracle_capacity(p->T, p->K, p->N, p->capacity_factor);
+  oracle_dispatch(p, idx, C, cnt, kept, off, rof, tor);
+  oracle_layer_rows(p, in, idx, gate, rof, p->T, NULL, out, nthreads);
+
+  if (!H) free(h);
+  if (!topk_idx) free(idx);
+  if (!topk_gate) free(gate);
+  if (!expert_counts) free(cnt);
+  if (!kept_counts) free(kept);
+  if (!offsets) free(off);
+  if (!row_of) free(rof);
+  if (!token_of_row) free(tor);
+}

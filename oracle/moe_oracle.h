@@ -1,0 +1,134 @@
+/*
+ * moe_oracle.h -- plain CPU reference of the sparse Mixture-of-Experts FFN
+ * layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this code: only the test suite, the package's smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no source with the HIP
+ * library and includes no HIP header.
+ *
+ * What it computes (the pages it follows are cited on each function):
+ *   h_t = u_t + sum_k g_{k,t} * FFN_{e_k}(u_t) + sum_s FFN_s(u_t)
+ * with the router, gating variants, capacity/drop rule, dispatch maps and
+ * combine written out as their plain definitions, one token at a time.
+ *
+ * Precision.  Every dot product and every derived quantity is evaluated in
+ * double.  Values that the method materialises at a lower precision are
+ * rounded to that precision where they are stored, once:
+ *   - router scores H are fp32 (the router runs at fp32);
+ *   - the gated activation (act) and each expert output y are rounded to the
+ *     storage type of the expert path (bf16 round-to-nearest-even, or fp32);
+ *   - the sum of the shared experts' outputs is rounded once.
+ * The layer output is returned unrounded, in double.
+ *
+ * Every function is single-threaded per token; functions taking `nthreads`
+ * spread independent tokens (or rows) over that many POSIX threads.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1 };                        /* storage type */
+enum { OR_GATE_SOFTMAX_TOPK = 0, OR_GATE_TOPK_SOFTMAX = 1 };
+enum { OR_ACT_SWIGLU = 0, OR_ACT_RELU = 1 };
+
+typedef struct {
+  int32_t T, d, N, K, d_ff;     /* tokens, hidden width, experts, top-K, expert width */
+  int32_t n_shared, d_ff_shared;/* always-on experts and their width            */
+  float capacity_factor;        /* <= 0: no capacity limit                      */
+  float noise_weight;           /* W_noise scaling the Gaussian noise input     */
+  int32_t gating;               /* OR_GATE_*                                    */
+  int32_t act;                  /* OR_ACT_*                                     */
+  int32_t dtype;                /* OR_F32 / OR_BF16 for u and expert weights    */
+} oracle_problem;
+
+/* All weights row-major.  Element type of u and of the expert weights is
+ * problem.dtype (bf16 passed as its raw 16-bit pattern). */
+typedef struct {
+  const void*  u;         /* [T][d]                                   */
+  const float* w_router;  /* [N][d]   row i is expert i's centroid    */
+  const float* b_router;  /* [N] or NULL                              */
+  const float* noise;     /* [T][N] or NULL                           */
+  const void*  w_gate;    /* [N][d_ff][d]   (W1 for the ReLU FFN)     */
+  const void*  w_up;      /* [N][d_ff][d]   (NULL for the ReLU FFN)   */
+  const void*  w_down;    /* [N][d][d_ff]   (W2 for the ReLU FFN)     */
+  const void*  ws_gate;   /* [n_shared][d_ff_shared][d] or NULL       */
+  const void*  ws_up;     /* [n_shared][d_ff_shared][d] or NULL       */
+  const void*  ws_down;   /* [n_shared][d][d_ff_shared] or NULL       */
+} oracle_inputs;
+
+/* Round a double to the nearest bf16 value, ties to even (bf16 = the upper
+ * 16 bits of an IEEE binary32: 8 significant bits, binary32's exponent
+ * range).  Exposed so that tests can pin it against an independent
+ * conversion. */
+double oracle_round_bf16(double v);
+
+/* Router logits, one fp32 rounding of the exact value
+ *   H[t][i] = fp32( sum_j u[t][j]*w_router[i][j] + b[i] + W_noise*noise[t][i] ).
+ * MoE-layer equation (affinity u_t^T e_i) of the DeepSeekMoE notes; the
+ * router as a linear layer and noise added to the logits before selection
+ * (Noise Top-k Gating, "Key implementation details"). */
+void oracle_router_logits(const oracle_problem* p, const oracle_inputs* in,
+                          float* H, int nthreads);
+
+/* Softmax statistics, top-K selection and gates from fp32 scores H[T][N].
+ *   topk_idx[T][K]  experts ordered by (H descending, index ascending)
+ *   topk_gate[T][K] variant SOFTMAX_TOPK: the full softmax value s_i;
+ *                   variant TOPK_SOFTMAX: softmax over the K selected scores
+ *   lse_sq[T]       (log sum_i exp H_i)^2            (may be NULL)
+ *   mean_prob[N]    (1/T) sum_t s_{i,t}              (may be NULL)
+ *   probs[T][N]     s_{i,t}                          (may be NULL)        */
+void oracle_route(const oracle_problem* p, const float* H, int32_t* topk_idx,
+                  double* topk_gate, double* lse_sq, double* mean_prob,
+                  double* probs);
+
+/* Expert capacity ceil(cf*T*K/N) evaluated in double, capped at T (an expert
+ * can hold each token at most once); -1 when cf <= 0 (no limit). */
+int32_t oracle_capacity(int32_t T, int32_t K, int32_t N, float cf);
+
+/* Dispatch maps by one sequential walk over (t ascending, k ascending).
+ *   expert_counts[N]   assignments per expert before capacity
+ *   kept_counts[N]     min(count, C)
+ *   offsets[N+1]       exclusive prefix sum of kept_counts
+ *   row_of[T][K]       offsets[e] + rank, or -1 if dropped
+ *   token_of_row[T*K]  inverse map; -1 past offsets[N]                   */
+void oracle_dispatch(const oracle_problem* p, const int32_t* topk_idx,
+                     int32_t capacity, int32_t* expert_counts,
+                     int32_t* kept_counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* token_of_row);
+
+/* Expert FFN outputs for n rows.  Row r applies expert expert_of_row[r]
+ * (0..N-1: routed expert; -1: the sum of all shared experts) to the vector
+ * x + r*d (element type p->dtype).  y[r][d] receives the materialised
+ * output, i.e. rounded once to the storage type. */
+void oracle_ffn_rows(const oracle_problem* p, const oracle_inputs* in,
+                     int32_t n_rows, const void* x, const int32_t* expert_of_row,
+                     double* y, int nthreads);
+
+/* Layer outputs for a list of tokens, given routing and dispatch:
+ *   out[r][j] = u[t][j] + sum_{k kept} gate[t][k]*y_{t,k}[j] + y_shared[t][j]
+ * with t = tokens[r] (tokens == NULL: every token, n_tokens == T). */
+void oracle_layer_rows(const oracle_problem* p, const oracle_inputs* in,
+                       const int32_t* topk_idx, const double* topk_gate,
+                       const int32_t* row_of, int32_t n_tokens,
+                       const int32_t* tokens, double* out, int nthreads);
+
+/* The whole forward pass: logits, routing, capacity and dispatch, then the
+ * layer output of every token.  Outputs as above; any side output may be
+ * NULL except out. */
+void oracle_layer_forward(const oracle_problem* p, const oracle_inputs* in,
+                          float* H, int32_t* topk_idx, double* topk_gate,
+                          double* lse_sq, double* mean_prob,
+                          int32_t* expert_counts, int32_t* kept_counts,
+                          int32_t* offsets, int32_t* row_of,
+                          int32_t* token_of_row, double* out, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
