@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-MoE FFN layer forward pass on one MI355X.
+
+One step = moe_layer_forward over one batch (router, dispatch, grouped FFN,
+combine), inputs resident in HBM.  Default workload: the Mixtral-shaped
+layer (T=8192 tokens, d=4096, 8 experts, top-2, SwiGLU d_ff=14336, bf16,
+fp32 router), seeded synthetic inputs.
+
+Prints one JSON line: tokens/s of the whole pass, the roofline of the
+dominant stage (the grouped expert GEMMs, live HIP-event timing on the
+launch stream), per-stage times, and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer tokens/sec + grouped-GEMM % of bf16 MFMA peak (Mixtral-shaped)"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    """Hash of the grouped-GEMM kernel source (ties stored counters to it)."""
+    path = os.path.join(ROOT, "sparse_mixture_experts_42_amd", "csrc", "grouped_gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per grouped-FFN call from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("grouped_gemm_source") != source_hash():
+        return None
+    return e.get("bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--cpu-sample", type=int, default=96, help="tokens timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the layer shards over tokens with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_42_amd import moe as M
+    from sparse_mixture_experts_42_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    p = M.problem_of(w)
+    L = M.lib()
+    log(f"workload {w.name}: T={w.T} d={w.d} N={w.N} K={w.K} d_ff={w.d_ff} "
+        f"shared={w.n_shared}x{w.d_ff_shared} {w.dtype}")
+    t0 = time.time()
+    x = W.generate(w)
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    xg = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    weights = M.make_weights(p, xg["w_router"], xg["b_router"], xg["w_gate"], xg["w_up"],
+                             xg["w_down"], xg["ws_gate"], xg["ws_up"], xg["ws_down"])
+    bufs = M.LayerBuffers(p, dev, want_scores=False)
+    ws = M.workspace(p, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.byref(p)
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    layer_args = (P, vp(xg["u"]), vp(xg["noise"]), ctypes.byref(weights), ctypes.byref(bufs.c),
+                  vp(bufs.t["out"]), vp(ws), ws.numel(), sp)
+
+    def step():
+        st = L.moe_layer_forward(*layer_args)
+        if st != 0:
+            raise RuntimeError(M.moe_status_string(st))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` whole passes
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events {e0.elapsed_time(e1) / args.steps:.3f})")
+
+    # ---- per-stage live timing on the same stream (same buffers)
+    t = bufs.t
+    R = int(t["offsets"][-1].item())
+    stage_args = {
+        "route": ("moe_route", (P, vp(xg["u"]), vp(xg["w_router"]), vp(xg["b_router"]),
+                                vp(xg["noise"]), None, vp(t["topk_idx"]), vp(t["topk_gate"]),
+                                vp(t["mean_prob"]), vp(t["lse_sq"]), vp(ws), ws.numel(), sp)),
+        "dispatch": ("moe_dispatch", (P, vp(xg["u"]), vp(t["topk_idx"]), vp(t["expert_counts"]),
+                                      vp(t["kept_counts"]), vp(t["offsets"]), vp(t["row_of"]),
+                                      vp(t["token_of_row"]), vp(t["x_perm"]), vp(ws), ws.numel(), sp)),
+        "grouped_ffn": ("moe_grouped_ffn", (P, vp(t["x_perm"]), vp(t["offsets"]), vp(xg["w_gate"]),
+                                            vp(xg["w_up"]), vp(xg["w_down"]), vp(xg["u"]),
+                                            vp(xg["ws_gate"]), vp(xg["ws_up"]), vp(xg["ws_down"]),
+                                            vp(t["y_perm"]), vp(t["y_shared"]), vp(ws), ws.numel(), sp)),
+        "combine": ("moe_combine", (P, vp(xg["u"]), vp(t["y_perm"]), vp(t["row_of"]),
+                                    vp(t["topk_gate"]), vp(t["y_shared"]), vp(t["out"]), None, 0, sp)),
+    }
+    stages_ms = {}
+    for name, (fn, a) in stage_args.items():
+        f = getattr(L, fn)
+        for _ in range(2):
+            f(*a)
+        n = max(args.steps, 10)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            st = f(*a)
+            if st != 0:
+                raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stages_ms[name] = e0.elapsed_time(e1) / n
+    log("stages (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_ms.items()))
+
+    # ---- roofline of the grouped expert GEMMs (algorithmic flops per call)
+    mults = 3 if w.act == "swiglu" else 2
+    flops = 2.0 * R * w.d * w.d_ff * mults
+    flops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * mults
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops / (stages_ms["grouped_ffn"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name),
+                "kernel": "grouped expert GEMMs (moe_grouped_ffn: gate/up GEMM + down GEMM)",
+                "flops_per_call": flops, "rows": R}
+
+    # ---- HBM fractions of the memory-bound stages (algorithmic bytes)
+    es = w.es
+    route_bytes = w.T * w.d * es + w.N * w.d * 4 + w.T * (w.K * 8 + 4) \
+        + (w.T * w.N * 4 if w.noise else 0)
+    disp_bytes = w.T * w.d * es + R * w.d * es + w.T * w.K * 4 * 3 + R * 4
+    comb_bytes = w.T * w.d * es * 2 + R * w.d * es + w.T * w.K * 8 \
+        + (w.T * w.d * es if w.n_shared else 0)
+    hbm = {k: round(b / (stages_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+           for k, b in (("route", route_bytes), ("dispatch", disp_bytes), ("combine", comb_bytes))}
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        from tests import _io
+        n = min(args.cpu_sample, w.T)
+        ws_ = w.replace(T=n)
+        xs = dict(x)
+        xs["u"] = x["u"][:n].contiguous()
+        if x["noise"] is not None:
+            xs["noise"] = x["noise"][:n].contiguous()
+        po = _io.problem(ws_)
+        xi = _io.inputs(po, xs)
+        nth = O.nthreads_default()
+        log(f"cpu oracle: {n} tokens on {nth} threads")
+        c0 = time.perf_counter()
+        O.layer_forward(po, xi, nthreads=nth)
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"first {n} tokens of the {w.name} batch (same weights), whole oracle pass "
+                         f"(router, top-K, dispatch, expert FFNs, combine) in {cs:.1f} s"}
+        log(f"cpu oracle: {cs:.1f} s")
+
+    value = w.T * args.steps / wall
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "d_ff": w.d_ff,
+                   "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared, "gating": w.gating,
+                   "act": w.act, "capacity_factor": w.capacity_factor, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "grouped_gemm_pct_bf16_peak": round(100 * roofline["frac"], 2),
+        "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},
+        "hbm_frac": hbm,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

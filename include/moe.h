@@ -1,0 +1,219 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of one sparse Mixture-of-Experts
+ * FFN layer on an AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The layer (MoE-layer equation of the "Mixture-of-Experts (MoE)" ML notes,
+ * which quote DeepSeekMoE):
+ *     h_t = sum_{i=1..N} g_{i,t} FFN_i(u_t) + u_t,
+ *     g_{i,t} = s_{i,t} if s_{i,t} is among the K largest affinities, else 0,
+ *     s_{i,t} = Softmax_i(u_t^T e_i)
+ * computed in four stages, one entry point each, plus the chained pass:
+ *     moe_route        router GEMM (fp32), softmax, top-K, gates, statistics
+ *     moe_dispatch     per-expert histogram, capacity, prefix sum, stable
+ *                      permutation of token rows into expert-contiguous rows
+ *     moe_grouped_ffn  every expert's FFN over its ragged group of rows
+ *     moe_combine      gate-weighted un-permute and sum, plus the residual
+ *     moe_layer_forward  the four stages in order on one stream
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller (for example
+ *     a torch allocation).  Row-major, densely packed, 16-byte aligned.
+ *     The library allocates nothing and keeps no state between calls; it is
+ *     re-entrant.  Scratch memory is the caller's workspace `ws` of
+ *     `ws_bytes` bytes, at least moe_workspace_size(p) (256-byte aligned).
+ *   - `stream` is a hipStream_t (NULL: the null stream).  All work is
+ *     enqueued on it; nothing synchronises the host, and the host never reads
+ *     data back (ragged sizes stay on the device).
+ *   - Outputs are fully overwritten, never accumulated.
+ *   - "elem" is the problem's element type: fp32 for MOE_F32, bf16 (raw
+ *     16-bit pattern) for MOE_BF16.  It types u, the expert weights, x_perm,
+ *     y_perm, y_shared and out.  The router always runs in fp32 (router
+ *     weights, bias, noise, scores, gates, probabilities).
+ *   - Return value: MOE_OK or an error code.  Every argument check happens
+ *     before the first HIP call, so checks are testable without a GPU.
+ *     T == 0 returns MOE_OK and touches nothing (pointers are not checked).
+ *     NaN or Inf inside the data is undefined behaviour (results unspecified,
+ *     never a fault).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size or enum, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid problem outside what this build implements */
+  MOE_ERR_WORKSPACE = 3,    /* ws NULL or ws_bytes below moe_workspace_size() */
+  MOE_ERR_HIP = 4           /* a HIP launch failed (hipGetLastError) */
+} moe_status_t;
+
+/* Gating variant.
+ * MOE_GATE_SOFTMAX_TOPK: softmax over all N experts, the K largest kept with
+ *   their softmax values as gates, not renormalised (MoE-layer equation of
+ *   the DeepSeekMoE notes).
+ * MOE_GATE_TOPK_SOFTMAX: top-K of the scores, then softmax over the K
+ *   selected scores only; gates sum to 1 ("Router: Selecting Experts and
+ *   Computing Weights", Figure 2 of "MoE: Choosing Which MLPs to Use for
+ *   Each Token"). */
+enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_TOPK_SOFTMAX = 1 };
+
+/* Expert FFN.  Weights use the [out][in] layout, no biases.
+ * MOE_ACT_SWIGLU: y = W_down (SiLU(W_gate x) * (W_up x)), SiLU(z) = z/(1+e^-z)
+ *   (the gated MLP with Gate, Up and Down weights, Figure 1 of "MoE:
+ *   Choosing Which MLPs to Use for Each Token").
+ * MOE_ACT_RELU:   y = W_down ReLU(W_gate x)  (w_up unused, NULL). */
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 };
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+typedef struct moe_problem {
+  int32_t T;            /* tokens (rows of u), >= 0                           */
+  int32_t d;            /* hidden width, multiple of 64                       */
+  int32_t N;            /* routed experts, 1..256                             */
+  int32_t K;            /* experts per token, 1..min(N, 16)                   */
+  int32_t d_ff;         /* routed expert width, multiple of 64                */
+  int32_t n_shared;     /* always-on shared experts, >= 0                     */
+  int32_t d_ff_shared;  /* shared expert width (multiple of 64 if n_shared)   */
+  float capacity_factor;/* > 0: capacity C = moe_capacity(T,K,N,cf); <= 0: none */
+  float noise_weight;   /* W_noise: scores = logits + W_noise * noise         */
+  int32_t gating;       /* MOE_GATE_*                                         */
+  int32_t act;          /* MOE_ACT_*                                          */
+  int32_t dtype;        /* MOE_F32 or MOE_BF16                                */
+} moe_problem_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* Bytes of workspace that suffice for every entry point on problem p
+ * (0 when p is invalid or T == 0). */
+size_t moe_workspace_size(const moe_problem_t* p);
+
+/* Expert capacity: ceil(cf * (T*K) / N) evaluated in double in that order,
+ * capped at T (an expert holds each token at most once); -1 when cf <= 0 or
+ * cf is NaN (no limit).  Expert capacity = (tokens per batch / experts) *
+ * capacity factor, "Mixture of Experts (MoE)" glossary, expert-capacity
+ * entry; the K factor counts each (token, expert) assignment. */
+int32_t moe_capacity(int32_t T, int32_t K, int32_t N, float cf);
+
+/* Stage 1 -- router.
+ * scores H[t][i] = fp32(sum_j u[t][j] w_router[i][j] + b_router[i]) then
+ *   H = fmaf(W_noise, noise[t][i], H) if noise != NULL ("Noise Top-k
+ *   Gating": Gaussian noise scaled by W_noise is added to the logits before
+ *   the top-k selection; W_noise = 0 or noise == NULL: plain logits).
+ * topk_idx[t][k]: the K experts with the largest H, ordered by (H desc,
+ *   index asc); equal scores (+0 == -0) go to the lower index.
+ * topk_gate[t][k]: per p->gating (see above).
+ * lse_sq[t] = (log sum_i exp H[t][i])^2   (router z-loss term per token)
+ * mean_prob[i] = (1/T) sum_t softmax_i(H[t])  (load-balancing statistic P_i)
+ * In:  u [T][d] elem; w_router [N][d] fp32 (row i = centroid e_i);
+ *      b_router [N] fp32 or NULL; noise [T][N] fp32 or NULL.
+ * Out: scores [T][N] fp32 or NULL; topk_idx [T][K] int32; topk_gate [T][K]
+ *      fp32; mean_prob [N] fp32; lse_sq [T] fp32.
+ * Errors: INVALID_ARG for a NULL required pointer or a NaN W_noise with noise. */
+int moe_route(const moe_problem_t* p, const void* u, const float* w_router,
+              const float* b_router, const float* noise, float* scores,
+              int32_t* topk_idx, float* topk_gate, float* mean_prob,
+              float* lse_sq, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2 -- dispatch ("From Router to Combine", Figure 3 of "MoE: Choosing
+ * Which MLPs to Use for Each Token": inputs are grouped by expert, the same
+ * token vector appearing in each of its experts' groups).
+ * expert_counts[e]: assignments (t,k) with topk_idx[t][k] == e (before
+ *   capacity).
+ * Capacity ("Mixture of Experts (MoE)" glossary and "Switch Transformers
+ *   explained", "Making it work": overflow is dropped and the token keeps only
+ *   the residual): an assignment is kept iff its rank among expert e's
+ *   assignments in ascending token order is below C = moe_capacity(...).
+ * kept_counts[e] = min(expert_counts[e], C); offsets[0..N] exclusive prefix
+ *   sum of kept_counts (offsets[N] = kept rows R).
+ * row_of[t][k] = offsets[e] + rank, or -1 when dropped; token_of_row[r] = t
+ *   for r < R and -1 for R <= r < T*K.  Rows of one expert ascend in t.
+ * x_perm[r] = u[token_of_row[r]] for r < R (rows >= R unspecified).
+ * In:  u [T][d] elem; topk_idx [T][K] int32 (each row K distinct experts in
+ *      0..N-1; otherwise results are unspecified).
+ * Out: expert_counts [N], kept_counts [N], offsets [N+1], row_of [T][K],
+ *      token_of_row [T*K] int32; x_perm [T*K][d] elem. */
+int moe_dispatch(const moe_problem_t* p, const void* u, const int32_t* topk_idx,
+                 int32_t* expert_counts, int32_t* kept_counts, int32_t* offsets,
+                 int32_t* row_of, int32_t* token_of_row, void* x_perm, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* Stage 3 -- expert FFNs as grouped GEMMs over ragged groups: rows
+ * [offsets[e], offsets[e+1]) of x_perm through expert e ("each expert
+ * applies its MLP to the tokens assigned to it ... values of tokens are not
+ * mixed", "From Router to Combine").  Shared experts ("Shared Expert",
+ * Figure 4): every token u[t] through all n_shared experts, outputs summed.
+ * The gated activation is materialised in elem in the workspace; y is
+ * rounded to elem once (the shared experts' sum once).
+ * In:  x_perm [T*K][d] elem; offsets [N+1] int32 (as from moe_dispatch);
+ *      w_gate, w_up [N][d_ff][d] elem (w_up NULL for ReLU);
+ *      w_down [N][d][d_ff] elem; u [T][d] elem (shared experts' input, may
+ *      be NULL when n_shared == 0); ws_gate, ws_up [n_shared][d_ff_shared][d]
+ *      and ws_down [n_shared][d][d_ff_shared] elem (NULL when n_shared == 0).
+ * Out: y_perm [T*K][d] elem (rows >= offsets[N] unspecified);
+ *      y_shared [T][d] elem (NULL when n_shared == 0). */
+int moe_grouped_ffn(const moe_problem_t* p, const void* x_perm,
+                    const int32_t* offsets, const void* w_gate, const void* w_up,
+                    const void* w_down, const void* u, const void* ws_gate,
+                    const void* ws_up, const void* ws_down, void* y_perm,
+                    void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 4 -- combine: out[t] = u[t] + sum_k [row_of[t][k] >= 0]
+ *   topk_gate[t][k] * y_perm[row_of[t][k]] + y_shared[t], summed in fp32 in
+ *   that order and rounded to elem once ("Combine gathers each expert's
+ *   results by the original token", "From Router to Combine"; residual of the
+ *   MoE-layer equation; dropped assignments add nothing).
+ * In:  u [T][d], y_perm [T*K][d], y_shared [T][d] or NULL (elem);
+ *      row_of [T][K] int32; topk_gate [T][K] fp32.
+ * Out: out [T][d] elem. */
+int moe_combine(const moe_problem_t* p, const void* u, const void* y_perm,
+                const int32_t* row_of, const float* topk_gate,
+                const void* y_shared, void* out, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* The weights of one layer (all device pointers, layouts as above). */
+typedef struct moe_weights {
+  const float* w_router;  /* [N][d] fp32                          */
+  const float* b_router;  /* [N] fp32 or NULL                     */
+  const void* w_gate;     /* [N][d_ff][d] elem                    */
+  const void* w_up;       /* [N][d_ff][d] elem, NULL for ReLU     */
+  const void* w_down;     /* [N][d][d_ff] elem                    */
+  const void* ws_gate;    /* [n_shared][d_ff_shared][d] or NULL   */
+  const void* ws_up;      /* [n_shared][d_ff_shared][d] or NULL   */
+  const void* ws_down;    /* [n_shared][d][d_ff_shared] or NULL   */
+} moe_weights_t;
+
+/* Every output and intermediate of the chained pass (device pointers).
+ * scores may be NULL; y_shared must be non-NULL iff n_shared > 0. */
+typedef struct moe_layer_outputs {
+  float* scores;          /* [T][N] fp32 or NULL */
+  int32_t* topk_idx;      /* [T][K]              */
+  float* topk_gate;       /* [T][K]              */
+  float* mean_prob;       /* [N]                 */
+  float* lse_sq;          /* [T]                 */
+  int32_t* expert_counts; /* [N]                 */
+  int32_t* kept_counts;   /* [N]                 */
+  int32_t* offsets;       /* [N+1]               */
+  int32_t* row_of;        /* [T][K]              */
+  int32_t* token_of_row;  /* [T*K]               */
+  void* x_perm;           /* [T*K][d] elem       */
+  void* y_perm;           /* [T*K][d] elem       */
+  void* y_shared;         /* [T][d] elem or NULL */
+} moe_layer_outputs_t;
+
+/* The whole forward pass: moe_route, moe_dispatch, moe_grouped_ffn and
+ * moe_combine in order on `stream`, out [T][d] elem. */
+int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
+                      const moe_weights_t* w, moe_layer_outputs_t* o, void* out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

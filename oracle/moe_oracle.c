@@ -394,6 +394,24 @@ void oracle_layer_rows(const oracle_problem* p, const oracle_inputs* in,
   parallel_for(n_tokens, nthreads, layer_range, &c);
 }
 
+void oracle_combine(const oracle_problem* p, const void* u, const void* y,
+                    const int32_t* row_of, const double* gate, const void* y_shared,
+                    double* out) {
+  const int d = p->d, K = p->K;
+  for (int t = 0; t < p->T; ++t) {
+    double* o = out + (size_t)t * d;
+    for (int j = 0; j < d; ++j) o[j] = load_elem(u, p->dtype, (size_t)t * d + j);
+    for (int k = 0; k < K; ++k) {
+      const int32_t row = row_of[(size_t)t * K + k];
+      if (row < 0) continue;                       /* dropped */
+      const double g = gate[(size_t)t * K + k];
+      for (int j = 0; j < d; ++j) o[j] += g * load_elem(y, p->dtype, (size_t)row * d + j);
+    }
+    if (y_shared)
+      for (int j = 0; j < d; ++j) o[j] += load_elem(y_shared, p->dtype, (size_t)t * d + j);
+  }
+}
+
 void oracle_layer_forward(const oracle_problem* p, const oracle_inputs* in,
                           float* H, int32_t* topk_idx, double* topk_gate,
                           double* lse_sq, double* mean_prob,

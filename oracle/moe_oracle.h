@@ -118,6 +118,14 @@ void oracle_layer_rows(const oracle_problem* p, const oracle_inputs* in,
                        const int32_t* row_of, int32_t n_tokens,
                        const int32_t* tokens, double* out, int nthreads);
 
+/* Combine alone, from given expert outputs:
+ *   out[t][j] = u[t][j] + sum_{k: row_of[t][k] >= 0} gate[t][k]*y[row_of[t][k]][j]
+ *               + y_shared[t][j]
+ * y [T*K][d] and y_shared [T][d] (or NULL) in the problem's element type. */
+void oracle_combine(const oracle_problem* p, const void* u, const void* y,
+                    const int32_t* row_of, const double* gate, const void* y_shared,
+                    double* out);
+
 /* The whole forward pass: logits, routing, capacity and dispatch, then the
  * layer output of every token.  Outputs as above; any side output may be
  * NULL except out. */

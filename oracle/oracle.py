@@ -56,10 +56,12 @@ class Problem:
 
 
 def nthreads_default() -> int:
+    """Host threads for the oracle: the usable cores, at most 16."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def lib():
@@ -80,6 +82,7 @@ def lib():
         L.oracle_dispatch.argtypes = [P, vp, i32, vp, vp, vp, vp, vp]
         L.oracle_ffn_rows.argtypes = [P, I, i32, vp, vp, vp, ctypes.c_int]
         L.oracle_layer_rows.argtypes = [P, I, vp, vp, vp, i32, vp, vp, ctypes.c_int]
+        L.oracle_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.oracle_layer_forward.argtypes = [P, I] + [vp] * 11 + [ctypes.c_int]
         _lib = L
     return _lib
@@ -197,6 +200,19 @@ def layer_rows(p: Problem, x: Inputs, topk_idx, topk_gate, row_of, tokens=None,
     out = np.zeros((n, p.d), np.float64)
     lib().oracle_layer_rows(ctypes.byref(p.c()), ctypes.byref(x.c), _ptr(idx), _ptr(gate),
                             _ptr(rof), n, _ptr(tok), _ptr(out), nthreads or nthreads_default())
+    return out
+
+
+def combine(p: Problem, u, y, row_of, topk_gate, y_shared=None) -> np.ndarray:
+    u = _elem_array(u, p.dtype)
+    y = _elem_array(y, p.dtype)
+    ys = None if y_shared is None else _elem_array(y_shared, p.dtype)
+    rof = np.ascontiguousarray(row_of, dtype=np.int32)
+    gate = np.ascontiguousarray(topk_gate, dtype=np.float64)
+    assert u.shape == (p.T, p.d) and y.shape == (p.T * p.K, p.d) and rof.shape == (p.T, p.K)
+    out = np.zeros((p.T, p.d), np.float64)
+    lib().oracle_combine(ctypes.byref(p.c()), _ptr(u), _ptr(y), _ptr(rof), _ptr(gate), _ptr(ys),
+                         _ptr(out))
     return out
 
 

@@ -1,0 +1,281 @@
+// libmoe C ABI: argument checks, workspace layout and launch sequencing.
+// Every check runs before the first HIP call, so a bad argument never
+// reaches the device; all work is enqueued on the caller's stream.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+Workspace workspace_layout(const moe_problem_t& p) {
+  Workspace w{};
+  const size_t T = (size_t)p.T, N = (size_t)p.N, K = (size_t)p.K;
+  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
+  const int rt = route_tokens_per_block(p);
+  w.route_blocks = (int)((T + rt - 1) / rt);
+  w.disp_blocks = (int)((T + kDispatchTok - 1) / kDispatchTok);
+  size_t off = 0;
+  w.route_part = off;
+  off = align_up(off + (size_t)w.route_blocks * N * 4, kAlign);
+  w.disp_count = off;
+  off = align_up(off + (size_t)w.disp_blocks * N * 4, kAlign);
+  w.disp_base = off;
+  off = align_up(off + (size_t)w.disp_blocks * N * 4, kAlign);
+  w.tiles = off;
+  off = align_up(off + (N + 2) * 4, kAlign);
+  w.act = off;
+  off = align_up(off + T * K * (size_t)p.d_ff * es, kAlign);
+  w.act_shared = off;
+  if (p.n_shared > 0) off = align_up(off + T * (size_t)p.n_shared * p.d_ff_shared * es, kAlign);
+  w.total = off;
+  return w;
+}
+
+}  // namespace moe
+
+using moe::Workspace;
+
+namespace {
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Structural checks of the problem descriptor.
+int check_problem(const moe_problem_t* p) {
+  if (p == nullptr) return MOE_ERR_INVALID_ARG;
+  if (p->T < 0 || p->d <= 0 || p->N <= 0 || p->K <= 0 || p->d_ff <= 0 || p->n_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (p->K > p->N) return MOE_ERR_INVALID_ARG;
+  if (p->n_shared > 0 && p->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_GATE_SOFTMAX_TOPK && p->gating != MOE_GATE_TOPK_SOFTMAX)
+    return MOE_ERR_INVALID_ARG;
+  if (p->act != MOE_ACT_SWIGLU && p->act != MOE_ACT_RELU) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (isnan(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  // valid, but outside what the kernels implement
+  if (p->N > 256 || p->K > 16) return MOE_ERR_UNSUPPORTED;
+  if (p->d % 64 != 0 || p->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (p->n_shared > 0 && p->d_ff_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long rows = (long long)p->T * p->K;
+  if (rows > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)p->n_shared * p->d_ff_shared > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)p->d * p->d_ff > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Required device buffers: non-null and aligned (16 bytes for anything read
+// or written in 16-byte vectors, 4 bytes otherwise).
+int need(const void* ptr, size_t align) {
+  if (ptr == nullptr) return MOE_ERR_INVALID_ARG;
+  return aligned(ptr, align) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+int maybe(const void* ptr, size_t align) {
+  return (ptr == nullptr || aligned(ptr, align)) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+#define MOE_TRY(x)                 \
+  do {                             \
+    const int moe_s_ = (x);        \
+    if (moe_s_ != MOE_OK) return moe_s_; \
+  } while (0)
+
+int check_ws(void* ws, size_t ws_bytes, size_t required) {
+  if (required == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < required || !aligned(ws, moe::kAlign)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int check_route(const moe_problem_t* p, const void* u, const float* w_router,
+                const float* b_router, const float* noise, const float* scores,
+                const int32_t* topk_idx, const float* topk_gate, const float* mean_prob,
+                const float* lse_sq) {
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(w_router, 16));
+  MOE_TRY(maybe(b_router, 4));
+  MOE_TRY(maybe(noise, 4));
+  MOE_TRY(maybe(scores, 4));
+  MOE_TRY(need(topk_idx, 4));
+  MOE_TRY(need(topk_gate, 4));
+  MOE_TRY(need(mean_prob, 4));
+  MOE_TRY(need(lse_sq, 4));
+  if (noise != nullptr && !isfinite(p->noise_weight)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_dispatch(const void* u, const int32_t* topk_idx, const int32_t* expert_counts,
+                   const int32_t* kept_counts, const int32_t* offsets, const int32_t* row_of,
+                   const int32_t* token_of_row, const void* x_perm) {
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(topk_idx, 4));
+  MOE_TRY(need(expert_counts, 4));
+  MOE_TRY(need(kept_counts, 4));
+  MOE_TRY(need(offsets, 4));
+  MOE_TRY(need(row_of, 4));
+  MOE_TRY(need(token_of_row, 4));
+  MOE_TRY(need(x_perm, 16));
+  return MOE_OK;
+}
+
+int check_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* offsets,
+              const void* w_gate, const void* w_up, const void* w_down, const void* u,
+              const void* ws_gate, const void* ws_up, const void* ws_down, const void* y_perm,
+              const void* y_shared) {
+  MOE_TRY(need(x_perm, 16));
+  MOE_TRY(need(offsets, 4));
+  MOE_TRY(need(w_gate, 16));
+  if (p->act == MOE_ACT_SWIGLU) MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(w_down, 16));
+  MOE_TRY(need(y_perm, 16));
+  if (p->n_shared > 0) {
+    MOE_TRY(need(u, 16));
+    MOE_TRY(need(ws_gate, 16));
+    if (p->act == MOE_ACT_SWIGLU) MOE_TRY(need(ws_up, 16));
+    MOE_TRY(need(ws_down, 16));
+    MOE_TRY(need(y_shared, 16));
+  }
+  return MOE_OK;
+}
+
+int check_combine(const moe_problem_t* p, const void* u, const void* y_perm,
+                  const int32_t* row_of, const float* topk_gate, const void* y_shared,
+                  const void* out) {
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(y_perm, 16));
+  MOE_TRY(need(row_of, 4));
+  MOE_TRY(need(topk_gate, 4));
+  MOE_TRY(need(out, 16));
+  if (p->n_shared > 0) MOE_TRY(need(y_shared, 16));
+  else MOE_TRY(maybe(y_shared, 16));
+  return MOE_OK;
+}
+
+char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: problem outside the implemented range";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+size_t moe_workspace_size(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK || p->T == 0) return 0;
+  return moe::workspace_layout(*p).total;
+}
+
+int32_t moe_capacity(int32_t T, int32_t K, int32_t N, float cf) {
+  if (!(cf > 0.0f) || N <= 0 || T < 0 || K < 0) return -1;
+  double c = ceil((double)cf * (double)((int64_t)T * K) / (double)N);
+  if (c > (double)T) c = (double)T;
+  return (int32_t)c;
+}
+
+int moe_route(const moe_problem_t* p, const void* u, const float* w_router,
+              const float* b_router, const float* noise, float* scores, int32_t* topk_idx,
+              float* topk_gate, float* mean_prob, float* lse_sq, void* ws, size_t ws_bytes,
+              void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_route(p, u, w_router, b_router, noise, scores, topk_idx, topk_gate, mean_prob,
+                      lse_sq));
+  const Workspace w = moe::workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.disp_count));
+  return hip_status(moe::launch_route(*p, u, w_router, b_router, noise, scores, topk_idx,
+                                      topk_gate, mean_prob, lse_sq,
+                                      reinterpret_cast<float*>(ws_at(ws, w.route_part)),
+                                      w.route_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const moe_problem_t* p, const void* u, const int32_t* topk_idx,
+                 int32_t* expert_counts, int32_t* kept_counts, int32_t* offsets, int32_t* row_of,
+                 int32_t* token_of_row, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_dispatch(u, topk_idx, expert_counts, kept_counts, offsets, row_of, token_of_row,
+                         x_perm));
+  const Workspace w = moe::workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.tiles));
+  const int32_t C = moe_capacity(p->T, p->K, p->N, p->capacity_factor);
+  return hip_status(moe::launch_dispatch(
+      *p, u, topk_idx, C, expert_counts, kept_counts, offsets, row_of, token_of_row, x_perm,
+      reinterpret_cast<int32_t*>(ws_at(ws, w.disp_count)),
+      reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)), w.disp_blocks,
+      static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* offsets,
+                    const void* w_gate, const void* w_up, const void* w_down, const void* u,
+                    const void* ws_gate, const void* ws_up, const void* ws_down, void* y_perm,
+                    void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_ffn(p, x_perm, offsets, w_gate, w_up, w_down, u, ws_gate, ws_up, ws_down, y_perm,
+                    y_shared));
+  const Workspace w = moe::workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.total));
+  return hip_status(moe::launch_grouped_ffn(
+      *p, x_perm, offsets, w_gate, w_up, w_down, u, ws_gate, ws_up, ws_down, y_perm,
+      p->n_shared > 0 ? y_shared : nullptr, reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)),
+      ws_at(ws, w.act), ws_at(ws, w.act_shared), static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const moe_problem_t* p, const void* u, const void* y_perm, const int32_t* row_of,
+                const float* topk_gate, const void* y_shared, void* out, void* ws,
+                size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_combine(p, u, y_perm, row_of, topk_gate, y_shared, out));
+  return hip_status(moe::launch_combine(*p, u, y_perm, row_of, topk_gate,
+                                        p->n_shared > 0 ? y_shared : nullptr, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
+                      const moe_weights_t* wt, moe_layer_outputs_t* o, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  if (wt == nullptr || o == nullptr) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_route(p, u, wt->w_router, wt->b_router, noise, o->scores, o->topk_idx,
+                      o->topk_gate, o->mean_prob, o->lse_sq));
+  MOE_TRY(check_dispatch(u, o->topk_idx, o->expert_counts, o->kept_counts, o->offsets,
+                         o->row_of, o->token_of_row, o->x_perm));
+  MOE_TRY(check_ffn(p, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u, wt->ws_gate,
+                    wt->ws_up, wt->ws_down, o->y_perm, o->y_shared));
+  MOE_TRY(check_combine(p, u, o->y_perm, o->row_of, o->topk_gate, o->y_shared, out));
+  const Workspace w = moe::workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_route(*p, u, wt->w_router, wt->b_router, noise, o->scores,
+                                   o->topk_idx, o->topk_gate, o->mean_prob, o->lse_sq,
+                                   reinterpret_cast<float*>(ws_at(ws, w.route_part)),
+                                   w.route_blocks, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int32_t C = moe_capacity(p->T, p->K, p->N, p->capacity_factor);
+  e = moe::launch_dispatch(*p, u, o->topk_idx, C, o->expert_counts, o->kept_counts, o->offsets,
+                           o->row_of, o->token_of_row, o->x_perm,
+                           reinterpret_cast<int32_t*>(ws_at(ws, w.disp_count)),
+                           reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)), w.disp_blocks, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  void* ysh = p->n_shared > 0 ? o->y_shared : nullptr;
+  e = moe::launch_grouped_ffn(*p, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u,
+                              wt->ws_gate, wt->ws_up, wt->ws_down, o->y_perm, ysh,
+                              reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)), ws_at(ws, w.act),
+                              ws_at(ws, w.act_shared), s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(*p, u, o->y_perm, o->row_of, o->topk_gate, ysh, out, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

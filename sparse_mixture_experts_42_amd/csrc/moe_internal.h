@@ -1,0 +1,75 @@
+// Internal declarations shared by the libmoe translation units (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16
+// bf16 is the upper half of an IEEE binary32 pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((x >> 16) | 0x40u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return static_cast<uint16_t>(x >> 16);
+}
+
+// ------------------------------------------------------------- layout
+constexpr size_t kAlign = 256;
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Router launch shape: each block owns `tok` tokens (16, 32 or 64).
+int route_tokens_per_block(const moe_problem_t& p);
+constexpr int kDispatchTok = 256;   // tokens per dispatch block
+
+struct Workspace {
+  size_t route_part;   // fp32 [route_blocks][N]   per-block softmax sums
+  size_t disp_count;   // int32 [disp_blocks][N]  per-block expert counts
+  size_t disp_base;    // int32 [disp_blocks][N]  per-block rank base
+  size_t tiles;        // int32 [N+2]             grouped-GEMM tile prefix
+  size_t act;          // elem [T*K][d_ff]        gated activations
+  size_t act_shared;   // elem [T][n_shared*d_ff_shared]
+  size_t total;
+  int route_blocks;
+  int disp_blocks;
+};
+Workspace workspace_layout(const moe_problem_t& p);
+
+// ------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; arguments are pre-validated.
+hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_router,
+                        const float* b_router, const float* noise, float* scores,
+                        int32_t* topk_idx, float* topk_gate, float* mean_prob,
+                        float* lse_sq, float* part, int route_blocks, hipStream_t s);
+
+hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t* topk_idx,
+                           int32_t capacity, int32_t* expert_counts, int32_t* kept_counts,
+                           int32_t* offsets, int32_t* row_of, int32_t* token_of_row,
+                           void* x_perm, int32_t* blk_count, int32_t* blk_base,
+                           int disp_blocks, hipStream_t s);
+
+hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
+                              const int32_t* offsets, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* u, const void* ws_gate,
+                              const void* ws_up, const void* ws_down, void* y_perm,
+                              void* y_shared, int32_t* tiles, void* act, void* act_shared,
+                              hipStream_t s);
+
+hipError_t launch_combine(const moe_problem_t& p, const void* u, const void* y_perm,
+                          const int32_t* row_of, const float* topk_gate,
+                          const void* y_shared, void* out, hipStream_t s);
+
+}  // namespace moe

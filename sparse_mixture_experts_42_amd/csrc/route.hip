@@ -1,0 +1,396 @@
+// Stage 1 -- router: fp32 router GEMM on the matrix cores, then softmax
+// statistics, top-K and gates in registers, one 64-lane wave per group of
+// tokens.
+//
+// MoE-layer equation ("Mixture-of-Experts (MoE)" ML notes, quoting
+// DeepSeekMoE): s_{i,t} = Softmax_i(u_t^T e_i), g = s on the Top-K, else 0.
+// "MoE: Choosing Which MLPs to Use for Each Token", Router section
+// (Figure 2): top-K of the scores, then softmax over the selected scores.
+// "Noise Top-k Gating", key implementation details: W_noise * N(0,1) noise is
+// added to the logits before the selection.  "Switch Transformers explained",
+// "Making it work": the router runs at higher precision (fp32 here).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kDK = 64;          // k-chunk staged in LDS per iteration
+constexpr int kLd = kDK + 4;     // padded LDS row (floats): spreads rows over banks
+constexpr int kThreads = 256;    // 4 waves
+
+struct RouteArgs {
+  const void* u;
+  const float* w;      // [N][d]
+  const float* b;      // [N] or null
+  const float* noise;  // [T][N] or null
+  float w_noise;
+  float* scores;       // [T][N] or null
+  int32_t* topk_idx;   // [T][K]
+  float* topk_gate;    // [T][K]
+  float* lse_sq;       // [T]
+  float* part;         // [blocks][N]
+  int T, d, N, K, gating;
+};
+
+template <typename E> struct Elem;
+template <> struct Elem<float> {
+  // 4 consecutive values per 16-byte vector
+  static constexpr int kPerVec = 4;
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kPerVec = 8;
+};
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// +0 and -0 are made equal first.
+__device__ __forceinline__ uint32_t order_key(float h) {
+  if (h == 0.0f) h = 0.0f;
+  uint32_t b = __float_as_uint(h);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_inv(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+template <int G>
+__device__ __forceinline__ float seg_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// One block: TOK tokens (TOK = 16 * TG), 4 waves = TG token groups x KS
+// k-splits.  NT = experts padded to 16 * NT (NT a power of two, <= 16).
+// G = lanes per token in the softmax/top-K phase (power of two, 4..64);
+// each lane holds R = max(1, 16*NT/64) expert slots.
+template <typename E, int TG, int NT, int G>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+  constexpr int TOK = 16 * TG;
+  constexpr int KS = 4 / TG;            // waves sharing a token group
+  constexpr int NP = 16 * NT;           // padded experts
+  constexpr int KW = kDK / KS;          // k per wave per chunk
+  constexpr int R = (NP + G - 1) / G;   // expert slots per lane
+  extern __shared__ float smem[];
+  float* sU = smem;                     // [TOK][kLd]
+  float* sW = smem + TOK * kLd;         // [NP][kLd]; reused as logits [TOK][NP+1]
+  float* sL = sW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tg = wave / KS;             // token group of this wave
+  const int ks = wave % KS;             // k-split of this wave
+  const int t0 = blockIdx.x * TOK;
+  const int T = a.T, d = a.d, N = a.N;
+
+  // zero padded expert rows once (never overwritten below)
+  for (int i = tid; i < (NP - N) * kLd; i += kThreads) sW[N * kLd + i] = 0.0f;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int VPR = kDK / Elem<E>::kPerVec;      // 16-byte vectors per u row chunk
+  for (int k0 = 0; k0 < d; k0 += kDK) {
+    // stage u[t0 .. t0+TOK)[k0 .. k0+kDK) as fp32
+    for (int v = tid; v < TOK * VPR; v += kThreads) {
+      const int r = v / VPR, c = v % VPR;
+      const int t = t0 + r;
+      float* dst = sU + r * kLd + c * Elem<E>::kPerVec;
+      if (t < T) {
+        const uint4 q = *reinterpret_cast<const uint4*>(
+            static_cast<const E*>(a.u) + (size_t)t * d + k0 + c * Elem<E>::kPerVec);
+        if constexpr (sizeof(E) == 2) {
+          const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[2 * i] = __uint_as_float(w4[i] << 16);
+            dst[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+          }
+        } else {
+          dst[0] = __uint_as_float(q.x);
+          dst[1] = __uint_as_float(q.y);
+          dst[2] = __uint_as_float(q.z);
+          dst[3] = __uint_as_float(q.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < Elem<E>::kPerVec; ++i) dst[i] = 0.0f;
+      }
+    }
+    // stage w_router[0..N)[k0 .. k0+kDK)
+    for (int v = tid; v < N * (kDK / 4); v += kThreads) {
+      const int r = v / (kDK / 4), c = v % (kDK / 4);
+      const float4 q = *reinterpret_cast<const float4*>(a.w + (size_t)r * d + k0 + 4 * c);
+      *reinterpret_cast<float4*>(sW + r * kLd + 4 * c) = q;
+    }
+    __syncthreads();
+    // 16x16x4 fp32 MFMA: A row = token (lane%16), B col = expert (lane%16),
+    // k = lane/16 within each group of 4
+    const float* pa = sU + (tg * 16 + (lane & 15)) * kLd + ks * KW + (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < KW; kk += 4) {
+      const float av = pa[kk];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const float bv = sW[(j * 16 + (lane & 15)) * kLd + ks * KW + kk + (lane >> 4)];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- sum the k-split partial logits into sL[TOK][NP+1] (fixed order)
+  constexpr int LdL = NP + 1;
+  for (int s = 0; s < KS; ++s) {
+    if (ks == s) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float* dst = sL + (tg * 16 + 4 * (lane >> 4) + v) * LdL + j * 16 + (lane & 15);
+          *dst = (s == 0) ? acc[j][v] : *dst + acc[j][v];
+        }
+    }
+    __syncthreads();
+  }
+
+  // ---- softmax statistics, top-K and gates: each wave takes TOK/4 tokens
+  constexpr int TPW = TOK / 4;              // tokens per wave
+  constexpr int TPP = (64 / G) < TPW ? (64 / G) : TPW;  // tokens per pass
+  const int seg = lane / G, j = lane % G;
+  float pacc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) pacc[r] = 0.0f;
+
+  for (int pass = 0; pass < TPW / TPP; ++pass) {
+    const int lt = wave * TPW + pass * TPP + seg;   // token within block
+    const int t = t0 + lt;
+    const bool tok_ok = (seg < TPP) && (t < T);
+    float h[R];
+    bool ok[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = j + r * G;
+      ok[r] = tok_ok && (i < N);
+      float v = -INFINITY;
+      if (ok[r]) {
+        v = sL[lt * LdL + i];
+        if (a.b) v += a.b[i];
+        if (a.noise) v = fmaf(a.w_noise, a.noise[(size_t)t * N + i], v);
+        if (a.scores) a.scores[(size_t)t * N + i] = v;
+      }
+      h[r] = v;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < R; ++r) m = fmaxf(m, h[r]);
+    m = seg_max<G>(m);
+    float e[R], z = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      e[r] = ok[r] ? expf(h[r] - m) : 0.0f;
+      z += e[r];
+    }
+    z = seg_sum<G>(z);
+    const float inv_z = 1.0f / z;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (ok[r]) pacc[r] += e[r] / z;
+    if (tok_ok && j == 0) {
+      const float lse = m + logf(z);
+      a.lse_sq[t] = lse * lse;
+    }
+    (void)inv_z;
+    // top-K by K rounds of a segment-wide max of (score, -index) keys
+    uint64_t key[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t i = j + r * G;
+      key[r] = ok[r] ? ((uint64_t)order_key(h[r]) << 32) | (uint64_t)(0xffffffffu - i) : 0ull;
+    }
+    float hk0 = 0.0f, gsum = 0.0f;
+    int sel_idx[16];
+    float sel_h[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < a.K) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) best = key[r] > best ? key[r] : best;
+        best = seg_max_u64<G>(best);
+        const uint32_t idx = 0xffffffffu - (uint32_t)(best & 0xffffffffu);
+        const float hk = order_key_inv((uint32_t)(best >> 32));
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (key[r] == best) key[r] = 0ull;
+        sel_idx[k] = (int)idx;
+        sel_h[k] = hk;
+        if (k == 0) hk0 = hk;
+        gsum += expf(hk - hk0);
+      }
+    }
+    if (tok_ok && j == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k < a.K) {
+          float g;
+          if (a.gating == MOE_GATE_SOFTMAX_TOPK) g = expf(sel_h[k] - m) / z;
+          else g = expf(sel_h[k] - hk0) / gsum;
+          a.topk_idx[(size_t)t * a.K + k] = sel_idx[k];
+          a.topk_gate[(size_t)t * a.K + k] = g;
+        }
+      }
+    }
+  }
+
+  // ---- per-block sums of the softmax probabilities (fixed order)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float v = pacc[r];
+    for (int o = G; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    pacc[r] = v;
+  }
+  __syncthreads();                       // sL no longer read
+  float* sP = smem;                      // [4][NP]
+  if (lane < G) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = lane + r * G;
+      if (i < NP) sP[wave * NP + i] = pacc[r];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += kThreads)
+    a.part[(size_t)blockIdx.x * N + i] = ((sP[i] + sP[NP + i]) + sP[2 * NP + i]) + sP[3 * NP + i];
+}
+
+// mean_prob[i] = (sum over blocks of part[b][i], in block order) / T
+__global__ __launch_bounds__(256) void route_finalize_kernel(const float* part, int blocks, int N,
+                                                             int T, float* mean_prob) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  float s = 0.0f;
+  for (int b = 0; b < blocks; ++b) s += part[(size_t)b * N + i];
+  mean_prob[i] = s / (float)T;
+}
+
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+template <typename E, int TG, int NT, int G>
+hipError_t launch_g(const RouteArgs& a, int blocks, hipStream_t s) {
+  constexpr int TOK = 16 * TG, NP = 16 * NT;
+  constexpr size_t stage = (size_t)(TOK + NP) * kLd * sizeof(float);
+  constexpr size_t logits = (size_t)TOK * kLd * sizeof(float) + (size_t)TOK * (NP + 1) * sizeof(float);
+  constexpr size_t lds = stage > logits ? stage : logits;
+  static_assert(lds <= 160 * 1024, "router tile exceeds the LDS of a CU");
+  if constexpr (lds > 64 * 1024) {
+    static bool attr_set = false;   // once per instantiation (idempotent)
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&route_kernel<E, TG, NT, G>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL((route_kernel<E, TG, NT, G>), dim3(blocks), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+// Lanes per token G: the smallest power of two >= N (at least 4, at most
+// 64); that fixes G for every padded width above 16 experts.
+template <typename E, int TG, int NT>
+hipError_t launch_gsel(const moe_problem_t& p, const RouteArgs& a, int blocks, hipStream_t s) {
+  if constexpr (NT == 1) {
+    if (p.N <= 4) return launch_g<E, TG, 1, 4>(a, blocks, s);
+    if (p.N <= 8) return launch_g<E, TG, 1, 8>(a, blocks, s);
+    return launch_g<E, TG, 1, 16>(a, blocks, s);
+  } else {
+    return launch_g<E, TG, NT, (16 * NT < 64 ? 16 * NT : 64)>(a, blocks, s);
+  }
+}
+
+template <typename E, int TG>
+hipError_t launch_nt(const moe_problem_t& p, const RouteArgs& a, int blocks, hipStream_t s) {
+  const int nt = pow2_at_least((p.N + 15) / 16);
+  switch (nt) {
+    case 1: return launch_gsel<E, TG, 1>(p, a, blocks, s);
+    case 2: return launch_gsel<E, TG, 2>(p, a, blocks, s);
+    case 4: return launch_gsel<E, TG, 4>(p, a, blocks, s);
+    case 8: return launch_gsel<E, TG, 8>(p, a, blocks, s);
+    case 16: return launch_gsel<E, TG, 16>(p, a, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename E>
+hipError_t launch_tg(const moe_problem_t& p, const RouteArgs& a, int blocks, hipStream_t s) {
+  switch (route_tokens_per_block(p)) {
+    case 16: return launch_nt<E, 1>(p, a, blocks, s);
+    case 32: return launch_nt<E, 2>(p, a, blocks, s);
+    case 64: return launch_nt<E, 4>(p, a, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// Small expert counts keep the router HBM-bound: few tokens per block, many
+// blocks.  Wide routers reuse the staged router weights over more tokens.
+int route_tokens_per_block(const moe_problem_t& p) {
+  if (p.N <= 32) return 16;
+  if ((long long)p.T >= 64LL * 256) return 64;
+  if ((long long)p.T >= 32LL * 256) return 32;
+  return 16;
+}
+
+hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_router,
+                        const float* b_router, const float* noise, float* scores,
+                        int32_t* topk_idx, float* topk_gate, float* mean_prob,
+                        float* lse_sq, float* part, int route_blocks, hipStream_t s) {
+  RouteArgs a;
+  a.u = u;
+  a.w = w_router;
+  a.b = b_router;
+  a.noise = noise;
+  a.w_noise = p.noise_weight;
+  a.scores = scores;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.lse_sq = lse_sq;
+  a.part = part;
+  a.T = p.T;
+  a.d = p.d;
+  a.N = p.N;
+  a.K = p.K;
+  a.gating = p.gating;
+  hipError_t e = p.dtype == MOE_BF16 ? launch_tg<uint16_t>(p, a, route_blocks, s)
+                                     : launch_tg<float>(p, a, route_blocks, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_finalize_kernel, dim3((p.N + 255) / 256), dim3(256), 0, s,
+                     (const float*)part, route_blocks, p.N, p.T, mean_prob);
+  return hipGetLastError();
+}
+
+}  // namespace moe

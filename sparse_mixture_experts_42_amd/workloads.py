@@ -5,8 +5,10 @@ arithmetic, so both the HIP path and the CPU oracle can be fed from it.  All
 draws are fp32 from a torch CPU generator, then rounded to bf16 (round to
 nearest even, torch's conversion) where the workload stores bf16.
 
-Draw order (fixed): u, w_router, b_router, w_gate, w_up, w_down, shared
-(gate, up, down), noise.  Distributions: u ~ N(0, 1); weights ~ N(0, std)
+Every tensor has its own generator stream, seeded with seed*1000 + a fixed
+index (u 0, w_router 1, b_router 2, w_gate 3, w_up 4, w_down 5, ws_gate 6,
+ws_up 7, ws_down 8, noise 9), so any subset can be drawn alone and comes out
+the same.  Distributions: u ~ N(0, 1); weights ~ N(0, std)
 with std = 1/sqrt(fan_in) unless the workload fixes it (the second argument
 of N(.,.) is the standard deviation).
 """
@@ -97,43 +99,71 @@ def harmonic(n: int, s: float) -> float:
     return math.fsum(r ** -s for r in range(1, n + 1))
 
 
-def generate(w: Workload) -> Dict[str, Optional[torch.Tensor]]:
-    """All inputs of workload `w` as CPU tensors (weights row-major [out][in])."""
-    g = torch.Generator().manual_seed(w.seed)
+STREAMS = dict(u=0, w_router=1, b_router=2, w_gate=3, w_up=4, w_down=5, ws_gate=6, ws_up=7,
+               ws_down=8, noise=9)
+ROUTER = ("u", "w_router", "b_router", "noise")
+
+
+def _gen(w: Workload, name: str) -> torch.Generator:
+    return torch.Generator().manual_seed(w.seed * 1000 + STREAMS[name])
+
+
+def generate(w: Workload, only=None) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs of workload `w` as CPU tensors (weights row-major [out][in]).
+    `only`: names to draw (default all); the others are None."""
+    want = set(STREAMS) if only is None else set(only)
     et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     T, d, N, dff = w.T, w.d, w.N, w.d_ff
-    x: Dict[str, Optional[torch.Tensor]] = {}
-    x["u"] = _normal(g, (T, d), 1.0, et)
-    x["w_router"] = _normal(g, (N, d), w.router_std or 1.0 / math.sqrt(d), torch.float32)
-    if w.bias == "none":
-        x["b_router"] = None
-    elif w.bias == "hot2":
-        # two seeded experts get a positive bias so that they draw about twice
-        # the mean load
-        hot = torch.randperm(N, generator=g)[:2]
-        b = torch.zeros(N, dtype=torch.float32)
-        b[hot] = w.hot_bias
+    x: Dict[str, Optional[torch.Tensor]] = {k: None for k in STREAMS}
+    if "u" in want:
+        x["u"] = _normal(_gen(w, "u"), (T, d), 1.0, et)
+    if "w_router" in want:
+        x["w_router"] = _normal(_gen(w, "w_router"), (N, d), w.router_std or 1.0 / math.sqrt(d),
+                                torch.float32)
+    if "b_router" in want and w.bias != "none":
+        g = _gen(w, "b_router")
+        if w.bias == "hot2":
+            # two seeded experts get a positive bias so that they draw about
+            # twice the mean load
+            hot = torch.randperm(N, generator=g)[:2]
+            b = torch.zeros(N, dtype=torch.float32)
+            b[hot] = w.hot_bias
+        elif w.bias == "zipf":
+            # seeded ranking r_e (a permutation of 1..N); softmax(b) is the
+            # Zipf pmf r^-s / H_{N,s}
+            r = (torch.randperm(N, generator=g) + 1).to(torch.float64)
+            b = (-w.zipf_s * torch.log(r) - math.log(harmonic(N, w.zipf_s))).to(torch.float32)
+        else:
+            raise ValueError(w.bias)
         x["b_router"] = b
-    elif w.bias == "zipf":
-        # seeded ranking r_e (a permutation of 1..N); softmax(b) is the Zipf pmf
-        # r^-s / H_{N,s}
-        r = (torch.randperm(N, generator=g) + 1).to(torch.float64)
-        b = -w.zipf_s * torch.log(r) - math.log(harmonic(N, w.zipf_s))
-        x["b_router"] = b.to(torch.float32)
-    else:
-        raise ValueError(w.bias)
     sd_in = w.expert_std or 1.0 / math.sqrt(d)
     sd_ff = w.expert_std or 1.0 / math.sqrt(dff)
-    x["w_gate"] = _normal(g, (N, dff, d), sd_in, et)
-    x["w_up"] = _normal(g, (N, dff, d), sd_in, et) if w.act == "swiglu" else None
-    x["w_down"] = _normal(g, (N, d, dff), sd_ff, et)
+    if "w_gate" in want:
+        x["w_gate"] = _normal(_gen(w, "w_gate"), (N, dff, d), sd_in, et)
+    if "w_up" in want and w.act == "swiglu":
+        x["w_up"] = _normal(_gen(w, "w_up"), (N, dff, d), sd_in, et)
+    if "w_down" in want:
+        x["w_down"] = _normal(_gen(w, "w_down"), (N, d, dff), sd_ff, et)
     if w.n_shared > 0:
         ds = w.d_ff_shared
         sd_ffs = w.expert_std or 1.0 / math.sqrt(ds)
-        x["ws_gate"] = _normal(g, (w.n_shared, ds, d), sd_in, et)
-        x["ws_up"] = _normal(g, (w.n_shared, ds, d), sd_in, et) if w.act == "swiglu" else None
-        x["ws_down"] = _normal(g, (w.n_shared, d, ds), sd_ffs, et)
-    else:
-        x["ws_gate"] = x["ws_up"] = x["ws_down"] = None
-    x["noise"] = _normal(g, (T, N), 1.0, torch.float32) if w.noise else None
+        if "ws_gate" in want:
+            x["ws_gate"] = _normal(_gen(w, "ws_gate"), (w.n_shared, ds, d), sd_in, et)
+        if "ws_up" in want and w.act == "swiglu":
+            x["ws_up"] = _normal(_gen(w, "ws_up"), (w.n_shared, ds, d), sd_in, et)
+        if "ws_down" in want:
+            x["ws_down"] = _normal(_gen(w, "ws_down"), (w.n_shared, d, ds), sd_ffs, et)
+    if "noise" in want and w.noise:
+        x["noise"] = _normal(_gen(w, "noise"), (T, N), 1.0, torch.float32)
     return x
+
+
+def random_topk(T: int, N: int, K: int, seed: int, skew: float = 0.0) -> torch.Tensor:
+    """Seeded expert choices [T][K] int32: K distinct experts per token,
+    drawn without replacement with weights (rank)^-skew (0: uniform)."""
+    g = torch.Generator().manual_seed(seed)
+    wts = torch.arange(1, N + 1, dtype=torch.float64) ** (-skew)
+    wts = wts[torch.randperm(N, generator=g)]
+    if T == 0:
+        return torch.zeros((0, K), dtype=torch.int32)
+    return torch.multinomial(wts.expand(T, N), K, replacement=False, generator=g).to(torch.int32)

@@ -483,3 +483,35 @@ def test_layer_forward_is_the_staged_composition():
     for k in ("expert_counts", "kept_counts", "offsets", "row_of", "token_of_row"):
         assert np.array_equal(o[k], dsp[k])
     assert np.array_equal(o["out"], out)
+
+
+def test_combine_pins():
+    """Zero expert outputs give the residual; a single gate-1 expert gives
+    u + y exactly (both bf16, the double sum is exact); combining the oracle's
+    own FFN rows reproduces the layer rows."""
+    w = _tiny(n_shared=1, d_ff_shared=8, capacity_factor=0.8)
+    x = W.generate(w)
+    p = _io.problem(w)
+    xi = _io.inputs(p, x)
+    o = O.layer_forward(p, xi)
+    u = _io.to_np(x["u"])
+    zeros = np.zeros((w.T * w.K, w.d), np.uint16)
+    out0 = O.combine(p, u, zeros, o["row_of"], o["topk_gate"])
+    assert np.array_equal(out0, _io.elems_to_f64(u, p.dtype))
+    # expert rows exactly as the layer computes them, then combined
+    rows = np.zeros((w.T * w.K, w.d), np.uint16)
+    tor = o["token_of_row"]
+    R = int(o["offsets"][-1])
+    eor = np.repeat(np.arange(w.N, dtype=np.int32), np.diff(o["offsets"]))
+    y = O.ffn_rows(p, xi, u[tor[:R]], eor)
+    rows[:R] = bf16_bits(y)
+    ys = bf16_bits(O.ffn_rows(p, xi, u, np.full(w.T, -1, np.int32)))
+    out = O.combine(p, u, rows, o["row_of"], o["topk_gate"], ys)
+    assert np.array_equal(out, o["out"])
+    # one routed expert with gate one
+    p1 = O.Problem(T=3, d=w.d, N=2, K=1, d_ff=8, dtype=O.BF16)
+    u1 = bf16_bits(np.random.default_rng(3).standard_normal((3, w.d)))
+    y1 = bf16_bits(np.random.default_rng(4).standard_normal((3, w.d)))
+    out1 = O.combine(p1, u1, y1, np.array([[2], [0], [1]], np.int32), np.ones((3, 1)))
+    ref = _io.elems_to_f64(u1, O.BF16) + _io.elems_to_f64(y1, O.BF16)[[2, 0, 1]]
+    assert np.array_equal(out1, ref)
