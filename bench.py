@@ -60,7 +60,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--cpu-sample", type=int, default=96, help="tokens timed on the CPU oracle")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

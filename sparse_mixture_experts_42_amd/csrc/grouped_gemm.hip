@@ -73,152 +73,237 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int
   return rows > 0;
 }
 
-// Consecutive logical blocks are spread by the hardware over the 8 XCDs
-// round-robin; remap so that each XCD gets a contiguous run of logical
-// blocks (row blocks sharing one weight tile then meet in one L2).
-__device__ __forceinline__ void xcd_remap(int& bx, int& by) {
-  const int nx = gridDim.x, total = gridDim.x * gridDim.y;
-  int lin = blockIdx.x + blockIdx.y * nx;
-  const int full = total - total % 8;
-  if (lin < full) lin = (lin % 8) * (full / 8) + lin / 8;
-  bx = lin % nx;
-  by = lin / nx;
+constexpr int kPatchN = 4;   // n-tiles per patch: an XCD works on m-tiles x 4 n-tiles of one group
+
+// 1-D grid.  The hardware hands consecutive blocks to the 8 XCDs round-robin,
+// each XCD with its own L2; hardware block h < (row tiles x n-tiles) is
+// remapped so that each XCD owns a contiguous run of logical tiles, and
+// logical tiles walk each group in patches of (all its row tiles) x kPatchN
+// n-tiles, so the activation and weight panels of a patch are fetched into
+// one L2 once and shared by the blocks of the patch.  Blocks past the real
+// tile count (the grid is sized for the largest possible count) exit.
+__device__ __forceinline__ bool find_tile_2d(const GemmArgs& a, int BM, int ntiles, int& g,
+                                             int& row0, int& rows, int& nt) {
+  const int h = blockIdx.x;
+  int mtiles_total, mt_g, base;
+  if (a.offsets == nullptr) {
+    mtiles_total = (a.M + BM - 1) / BM;
+  } else {
+    mtiles_total = a.tiles[a.G];
+  }
+  const int real = mtiles_total * ntiles;
+  if (h >= real) return false;
+  const int full = real - real % 8;
+  const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
+  if (a.offsets == nullptr) {
+    g = 0;
+    mt_g = mtiles_total;
+    base = 0;
+  } else {
+    int lo = 0, hi = a.G;          // tiles[lo]*ntiles <= L < tiles[hi]*ntiles
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tiles[mid] * ntiles <= L) lo = mid;
+      else hi = mid;
+    }
+    g = lo;
+    mt_g = a.tiles[g + 1] - a.tiles[g];
+    base = a.tiles[g] * ntiles;
+  }
+  const int l = L - base;
+  const int nb = l / (mt_g * kPatchN);
+  const int rem = l - nb * mt_g * kPatchN;
+  const int nbe = ntiles - nb * kPatchN < kPatchN ? ntiles - nb * kPatchN : kPatchN;
+  const int mt = rem / nbe;
+  nt = nb * kPatchN + rem % nbe;
+  row0 = (a.offsets == nullptr ? 0 : a.offsets[g]) + mt * BM;
+  const int end = a.offsets == nullptr ? a.M : a.offsets[g + 1];
+  rows = end - row0;
+  if (rows > BM) rows = BM;
+  return rows > 0;
 }
 
 // ------------------------------------------------------------ bf16 MFMA
-constexpr int BM = 128, BN = 128, BK = 64;
+// Block tile BM x BN (BN counts weight rows: for SwiGLU the first half are
+// gate rows and the second half the up rows of the same BN/2 act columns),
+// 4 waves as WGM x WGN, each wave a (BM/WGM) x (BN/WGN) grid of 32x32
+// accumulators.  K advances 64 at a time through two LDS stages that are
+// filled straight from global memory (buffer loads to LDS, no register
+// staging) while the matrix cores work on the other stage.
+constexpr int BK = 64;               // k per stage: 128 bytes per tile row
 constexpr int kThreads = 256;
 
-// LDS tiles are [rows][64 bf16] = 8 chunks of 16 bytes per row; chunk c of
-// row r lives at slot c ^ (r & 7) so that the 32 rows read by one MFMA
-// operand load spread over all banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+typedef __attribute__((address_space(3))) void lds_t;
 
-template <int EPI>
+// LDS tiles are [rows][64 bf16] = 8 chunks of 16 bytes per row.  The LDS
+// has 64 banks (256 bytes) and serves a 16-byte read for 16 lanes at once,
+// i.e. 16 consecutive tile rows at one logical chunk; chunk c of row r is
+// stored at slot c ^ ((r >> 1) & 7), which puts those 16 rows on 16
+// different 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float silu_fast(float g) {
+  // g * sigmoid(g) with the hardware exp2 and reciprocal
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+template <int EPI, int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs a) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;     // 32x32 accumulators per wave
+  constexpr int AI = BM / 32, BI = BN / 32;       // 1-KB direct loads per wave per stage
+  static_assert(WGM * WGN == 4, "four waves");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
   __shared__ u32x4 sA[2][BM * 8];
   __shared__ u32x4 sB[2][BN * 8];
-  int bx, by;
-  xcd_remap(bx, by);
-  int g, row0, rows;
-  if (!find_tile(a, bx, BM, g, row0, rows)) return;
+
+  constexpr int BNH = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per tile
+  int g, row0, rows, by;
+  if (!find_tile_2d(a, BM, (a.Ndim + BNH - 1) / BNH, g, row0, rows, by)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const uint16_t* A = static_cast<const uint16_t*>(a.A);
-  const uint16_t* Bg = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
-  const uint16_t* Bu = EPI == EPI_SWIGLU
-                           ? static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride
-                           : Bg;
-  // SwiGLU tiles hold 64 act columns: B rows 0..63 gate, 64..127 up
-  const int n0 = EPI == EPI_SWIGLU ? by * (BN / 2) : by * BN;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int n0 = by * BNH;
 
-  // global -> LDS: thread loads chunk lc of rows lr + 32 j (row offsets in
-  // elements; B rows of SwiGLU tiles alternate gate (0..63) and up (64..127))
-  const int lc = tid & 7, lr = tid >> 3;
-  size_t oa[4], ob[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int r = row0 + lr + 32 * j;
-    r = r < a.rows_alloc ? r : a.rows_alloc - 1;
-    oa[j] = (size_t)r * a.lda + lc * 8;
-    const int tr = lr + 32 * j;
-    int n = EPI == EPI_SWIGLU ? n0 + (tr & 63) : n0 + tr;
-    n = n < a.Ndim ? n : a.Ndim - 1;
-    ob[j] = (size_t)n * a.ldb + lc * 8;
+  // Direct loads: load i of this wave fills tile rows R0 .. R0+8 with
+  // R0 = 8q, q = wave*AI + i (1 KB of LDS); lane l writes slot l%8 of row
+  // R0 + l/8, which holds logical chunk (l%8) ^ ((R0 + l/8) >> 1 & 7)
+  // = (l%8) ^ (4*(q&1) + l/16): one lane mapping for even q, one for odd.
+  const int lrow = lane >> 3;
+  const int lchunk_even = (lane & 7) ^ (lrow >> 1);
+  const int lchunk_odd = (lane & 7) ^ (4 + (lrow >> 1));
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda, (uint32_t)rows * a.lda * 2);
+  // instruction i of this wave covers q = wave*AI + i
+  const uint32_t a_voff_e = (uint32_t)((wave * AI * 8 + lrow) * a.lda + lchunk_even * 8) * 2;
+  const uint32_t a_voff_o = (uint32_t)((wave * AI * 8 + lrow) * a.lda + lchunk_odd * 8) * 2;
+  const uint32_t a_step = 8u * a.lda * 2;
+
+  // B rows of this wave: [wave*BN/4, +BN/4) of the tile.  SwiGLU: waves 0-1
+  // load gate rows, waves 2-3 the up rows of the same columns.
+  const uint16_t* Bsrc = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
+  int b_local0 = wave * (BN / 4);
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (wave >= 2) {
+      Bsrc = static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride;
+      b_local0 -= BN / 2;
+    }
   }
-  const uint16_t* pb_lo = Bg;                                  // B rows 0..63 of the tile
-  const uint16_t* pb_hi = EPI == EPI_SWIGLU ? Bu : Bg;         // B rows 64..127
-  u32x4 ra[4], rb[4];
-  // (explicitly unrolled: the staging registers must never be indexed
-  // dynamically, or they would be demoted to scratch)
-#define MOE_GLOAD1(j_, kb_, boff_)                                                  \
-  ra[j_] = *reinterpret_cast<const u32x4*>(A + oa[j_] + (kb_));                     \
-  rb[j_] = *reinterpret_cast<const u32x4*>(((j_) < 2 ? pb_lo : pb_hi) + ob[j_] + (boff_));
-#define MOE_GLOAD(kt_)                                                              \
-  do {                                                                              \
-    const int kb_ = (kt_) * BK;                                                     \
-    const int seg_ = kb_ / a.kseg;                                                  \
-    const size_t boff_ = (size_t)seg_ * a.kseg_stride + (kb_ - seg_ * a.kseg);      \
-    MOE_GLOAD1(0, kb_, boff_) MOE_GLOAD1(1, kb_, boff_)                             \
-    MOE_GLOAD1(2, kb_, boff_) MOE_GLOAD1(3, kb_, boff_)                             \
-  } while (0)
-#define MOE_SSTORE1(j_, buf_)                                                       \
-  sA[(buf_)][swz(lr + 32 * (j_), lc)] = ra[j_];                                     \
-  sB[(buf_)][swz(lr + 32 * (j_), lc)] = rb[j_];
-#define MOE_SSTORE(buf_)                                                            \
-  do {                                                                              \
-    MOE_SSTORE1(0, buf_) MOE_SSTORE1(1, buf_) MOE_SSTORE1(2, buf_) MOE_SSTORE1(3, buf_) \
-  } while (0)
+  Bsrc += (size_t)n0 * a.ldb;
+  const int b_valid = a.Ndim - n0 < BNH ? a.Ndim - n0 : BNH;
+  const uint32_t b_bytes = (uint32_t)b_valid * a.ldb * 2;
+  const uint32_t b_voff_e = (uint32_t)((b_local0 + lrow) * a.ldb + lchunk_even * 8) * 2;
+  const uint32_t b_voff_o = (uint32_t)((b_local0 + lrow) * a.ldb + lchunk_odd * 8) * 2;
+  const uint32_t b_step = 8u * a.ldb * 2;
 
-  f32x16 acc[2][2];
+  lds_t* ldsA[2] = {(lds_t*)&sA[0][wave * AI * 64], (lds_t*)&sA[1][wave * AI * 64]};
+  lds_t* ldsB[2] = {(lds_t*)&sB[0][wave * BI * 64], (lds_t*)&sB[1][wave * BI * 64]};
+
+  auto issue = [&](int kt, int buf) {
+    const int kb = kt * BK;
+    const int seg = kb / a.kseg;
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bsrc + (size_t)seg * a.kseg_stride, b_bytes);
+    const uint32_t ka = (uint32_t)kb * 2, kbb = (uint32_t)(kb - seg * a.kseg) * 2;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < AI; ++i) {
+      const bool odd = ((wave * AI + i) & 1) != 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
+                                               (odd ? a_voff_o : a_voff_e) + i * a_step + ka, 0, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < BI; ++i) {
+      const bool odd = ((wave * BI + i) & 1) != 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
+                                               (odd ? b_voff_o : b_voff_e) + i * b_step + kbb, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // B rows used by this wave for its two n-tiles
-  int brow[2];
-  if (EPI == EPI_SWIGLU) {
-    brow[0] = wn * 32;          // gate rows
-    brow[1] = 64 + wn * 32;     // up rows, same act columns
-  } else {
-    brow[0] = wn * 64;
-    brow[1] = wn * 64 + 32;
-  }
+  // first row of each n-tile of this wave inside the B tile
+  auto brow = [&](int j) {
+    if constexpr (EPI == EPI_SWIGLU)
+      return j < TN / 2 ? wn * (WTN / 2) + 32 * j : BN / 2 + wn * (WTN / 2) + 32 * (j - TN / 2);
+    else
+      return wn * WTN + 32 * j;
+  };
 
   const int nk = a.Kdim / BK;
-  MOE_GLOAD(0);
-  MOE_SSTORE(0);
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) MOE_GLOAD(kt + 1);
+    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+    // operand fragments of k-step kk+1 are read while k-step kk multiplies
+    bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[0][i] = __builtin_bit_cast(bf16x8, sA[buf][swz(wm * WTM + i * 32 + (lane & 31), (lane >> 5))]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[0][j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), (lane >> 5))]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8 fa[2], fb[2];
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {
+        const int c = (kk + 1) * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const u32x4 q = sA[buf][swz(wm * 64 + i * 32 + (lane & 31), c)];
-        fa[i] = __builtin_bit_cast(bf16x8, q);
-        const u32x4 w = sB[buf][swz(brow[i] + (lane & 31), c)];
-        fb[i] = __builtin_bit_cast(bf16x8, w);
+        for (int i = 0; i < TM; ++i)
+          fa[cur ^ 1][i] = __builtin_bit_cast(bf16x8, sA[buf][swz(wm * WTM + i * 32 + (lane & 31), c)]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb[cur ^ 1][j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), c)]);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) MOE_SSTORE(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-#undef MOE_GLOAD1
-#undef MOE_GLOAD
-#undef MOE_SSTORE1
-#undef MOE_SSTORE
   // epilogue: lane holds column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4
   uint16_t* C = static_cast<uint16_t*>(a.C);
+  constexpr int OUT_TN = EPI == EPI_SWIGLU ? TN / 2 : TN;
+  const int col_base = n0 + (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= rows) continue;
-      if (EPI == EPI_SWIGLU) {
-        const int col = n0 + wn * 32 + (lane & 31);
-        if (col < a.Ndim)
-          C[(size_t)(row0 + r) * a.ldc + col] = f32_to_bf16(epilogue<EPI>(acc[i][0][v], acc[i][1][v]));
-      } else {
+    for (int j = 0; j < OUT_TN; ++j) {
+      const int col = col_base + 32 * j;
+      if (col >= a.Ndim) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + brow[j] + (lane & 31);
-          if (col < a.Ndim)
-            C[(size_t)(row0 + r) * a.ldc + col] = f32_to_bf16(epilogue<EPI>(acc[i][j][v], 0.0f));
+      for (int v = 0; v < 16; v += 2) {
+        f32x2 pr;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float x = acc[i][j][v + q];
+          if constexpr (EPI == EPI_SWIGLU) pr[q] = silu_fast(x) * acc[i][j + TN / 2][v + q];
+          else if constexpr (EPI == EPI_RELU) pr[q] = x > 0.0f ? x : 0.0f;
+          else pr[q] = x;
+        }
+        const uint32_t packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r = wm * WTM + i * 32 + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
+          if (r < rows)
+            C[(size_t)(row0 + r) * a.ldc + col] = (uint16_t)(q ? packed >> 16 : packed & 0xffffu);
         }
       }
     }
@@ -268,34 +353,43 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, 
   if (g == 0) tiles[0] = 0;
 }
 
-hipError_t run_gemm(const GemmArgs& a, int epi, bool bf16, int mtiles_max, hipStream_t s) {
+// Tile shape per problem: large groups use 256x256 tiles (128x128 per
+// wave); groups of a few rows (decode-sized batches) use 32-row tiles so the
+// matrix cores do not multiply mostly-empty rows.
+struct TileShape { int bm; };
+
+TileShape pick_tiles(int rows_per_group) { return TileShape{rows_per_group >= 128 ? 256 : 32}; }
+
+template <int EPI>
+hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
+  constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
+  dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
+  if (bm == 256)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 256, 256, 2, 2>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 256, 1, 4>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t run_gemm(const GemmArgs& a, int epi, bool bf16, int bm, int mtiles, hipStream_t s) {
   if (bf16) {
-    const int bn = epi == EPI_SWIGLU ? BN / 2 : BN;
-    dim3 grid(mtiles_max, (a.Ndim + bn - 1) / bn);
     switch (epi) {
-      case EPI_SWIGLU:
-        hipLaunchKernelGGL(grouped_gemm_bf16_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s, a);
-        break;
-      case EPI_RELU:
-        hipLaunchKernelGGL(grouped_gemm_bf16_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s, a);
-        break;
-      default:
-        hipLaunchKernelGGL(grouped_gemm_bf16_kernel<EPI_NONE>, grid, dim3(kThreads), 0, s, a);
-        break;
+      case EPI_SWIGLU: return launch_bf16<EPI_SWIGLU>(a, bm, mtiles, s);
+      case EPI_RELU: return launch_bf16<EPI_RELU>(a, bm, mtiles, s);
+      default: return launch_bf16<EPI_NONE>(a, bm, mtiles, s);
     }
-  } else {
-    dim3 grid(mtiles_max, (a.Ndim + 255) / 256);
-    switch (epi) {
-      case EPI_SWIGLU:
-        hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, a, BM);
-        break;
-      case EPI_RELU:
-        hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_RELU>, grid, dim3(256), 0, s, a, BM);
-        break;
-      default:
-        hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_NONE>, grid, dim3(256), 0, s, a, BM);
-        break;
-    }
+  }
+  dim3 grid(mtiles, (a.Ndim + 255) / 256);
+  switch (epi) {
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, a, bm);
+      break;
+    case EPI_RELU:
+      hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_RELU>, grid, dim3(256), 0, s, a, bm);
+      break;
+    default:
+      hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_NONE>, grid, dim3(256), 0, s, a, bm);
+      break;
   }
   return hipGetLastError();
 }
@@ -311,9 +405,12 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
   const bool bf16 = p.dtype == MOE_BF16;
   const int epi1 = p.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
   const int rows_alloc = p.T * p.K;
-  const int mtiles_max = (rows_alloc + BM - 1) / BM + p.N;
+  // fp32 problems: one block per 128 rows; bf16: tiles sized to the mean
+  // group (all groups share one tile height so the plan is one prefix sum)
+  const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : 128;
+  const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N;
 
-  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, offsets, p.N, BM, tiles);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, offsets, p.N, bm, tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -335,7 +432,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
   g1.kseg = p.d;
   g1.kseg_stride = 0;
   g1.b_group_stride = (size_t)p.d_ff * p.d;
-  if ((e = run_gemm(g1, epi1, bf16, mtiles_max, s)) != hipSuccess) return e;
+  if ((e = run_gemm(g1, epi1, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
   GemmArgs g2 = g1;
   g2.A = act;
@@ -349,14 +446,15 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
   g2.ldc = p.d;
   g2.kseg = p.d_ff;
   g2.b_group_stride = (size_t)p.d * p.d_ff;
-  if ((e = run_gemm(g2, EPI_NONE, bf16, mtiles_max, s)) != hipSuccess) return e;
+  if ((e = run_gemm(g2, EPI_NONE, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
   if (p.n_shared > 0) {
     // all shared experts as one expert of width n_shared*d_ff_shared: the
     // gate/up rows of consecutive experts are contiguous; the down
     // projection is K-segmented, one segment per shared expert
     const int ws_w = p.n_shared * p.d_ff_shared;
-    const int mt = (p.T + BM - 1) / BM;
+    const int sbm = bf16 ? pick_tiles(p.T).bm : 128;
+    const int mt = (p.T + sbm - 1) / sbm;
     GemmArgs s1{};
     s1.A = u;
     s1.B0 = ws_gate;
@@ -375,7 +473,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
     s1.kseg = p.d;
     s1.kseg_stride = 0;
     s1.b_group_stride = 0;
-    if ((e = run_gemm(s1, epi1, bf16, mt, s)) != hipSuccess) return e;
+    if ((e = run_gemm(s1, epi1, bf16, sbm, mt, s)) != hipSuccess) return e;
     GemmArgs s2 = s1;
     s2.A = act_shared;
     s2.B0 = ws_down;
@@ -388,7 +486,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
     s2.ldc = p.d;
     s2.kseg = p.d_ff_shared;
     s2.kseg_stride = (size_t)p.d * p.d_ff_shared;
-    if ((e = run_gemm(s2, EPI_NONE, bf16, mt, s)) != hipSuccess) return e;
+    if ((e = run_gemm(s2, EPI_NONE, bf16, sbm, mt, s)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

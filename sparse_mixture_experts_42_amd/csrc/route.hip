@@ -14,9 +14,19 @@
 namespace moe {
 namespace {
 
-constexpr int kDK = 64;          // k-chunk staged in LDS per iteration
-constexpr int kLd = kDK + 4;     // padded LDS row (floats): spreads rows over banks
 constexpr int kThreads = 256;    // 4 waves
+
+// k-chunk staged in LDS per iteration: wide for narrow routers (few, large
+// iterations keep enough bytes in flight for an HBM-bound stream), narrower
+// as the padded expert count grows so that the staged weights fit the LDS.
+// (at most 512 / NT, and staged u and weights of one chunk within ~80 KB)
+template <int TG, int NT>
+constexpr int chunk_k() {
+  int k = 512 / NT;
+  const int fit = 20480 / (16 * TG + 16 * NT) - 4;
+  while (k > fit) k /= 2;
+  return k < 32 ? 32 : k;
+}
 
 struct RouteArgs {
   const void* u;
@@ -84,6 +94,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   constexpr int TOK = 16 * TG;
   constexpr int KS = 4 / TG;            // waves sharing a token group
   constexpr int NP = 16 * NT;           // padded experts
+  constexpr int kDK = chunk_k<TG, NT>();
+  constexpr int kLd = kDK + 4;          // padded LDS row (floats): spreads rows over banks
   constexpr int KW = kDK / KS;          // k per wave per chunk
   constexpr int R = (NP + G - 1) / G;   // expert slots per lane
   extern __shared__ float smem[];
@@ -108,37 +120,53 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 
   constexpr int VPR = kDK / Elem<E>::kPerVec;      // 16-byte vectors per u row chunk
   for (int k0 = 0; k0 < d; k0 += kDK) {
-    // stage u[t0 .. t0+TOK)[k0 .. k0+kDK) as fp32
-    for (int v = tid; v < TOK * VPR; v += kThreads) {
+    // stage u[t0 .. t0+TOK)[k0 .. k0+kDK) as fp32 and w_router[0..N)[k0 ..
+    // k0+kDK): every load of the chunk is issued before any is consumed
+    constexpr int UV = (TOK * VPR + kThreads - 1) / kThreads;
+    constexpr int WV = (NP * (kDK / 4) + kThreads - 1) / kThreads;
+    u32x4 qu[UV];
+    float4 qw[WV];
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      const int v = tid + i * kThreads;
       const int r = v / VPR, c = v % VPR;
       const int t = t0 + r;
-      float* dst = sU + r * kLd + c * Elem<E>::kPerVec;
-      if (t < T) {
-        const uint4 q = *reinterpret_cast<const uint4*>(
-            static_cast<const E*>(a.u) + (size_t)t * d + k0 + c * Elem<E>::kPerVec);
-        if constexpr (sizeof(E) == 2) {
-          const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+      qu[i] = u32x4{0u, 0u, 0u, 0u};
+      if (v < TOK * VPR && t < T && k0 + c * Elem<E>::kPerVec < d)
+        qu[i] = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.u) + (size_t)t * d + k0 +
+                                                c * Elem<E>::kPerVec);
+    }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dst[2 * i] = __uint_as_float(w4[i] << 16);
-            dst[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
-          }
-        } else {
-          dst[0] = __uint_as_float(q.x);
-          dst[1] = __uint_as_float(q.y);
-          dst[2] = __uint_as_float(q.z);
-          dst[3] = __uint_as_float(q.w);
+    for (int i = 0; i < WV; ++i) {
+      const int v = tid + i * kThreads;
+      const int r = v / (kDK / 4), c = v % (kDK / 4);
+      qw[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < N && k0 + 4 * c < d)
+        qw[i] = *reinterpret_cast<const float4*>(a.w + (size_t)r * d + k0 + 4 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      const int v = tid + i * kThreads;
+      if (v >= TOK * VPR) continue;
+      const int r = v / VPR, c = v % VPR;
+      float* dst = sU + r * kLd + c * Elem<E>::kPerVec;
+      const u32x4 q = qu[i];
+      if constexpr (sizeof(E) == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dst[2 * j] = __uint_as_float(q[j] << 16);
+          dst[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < Elem<E>::kPerVec; ++i) dst[i] = 0.0f;
+        for (int j = 0; j < 4; ++j) dst[j] = __uint_as_float(q[j]);
       }
     }
-    // stage w_router[0..N)[k0 .. k0+kDK)
-    for (int v = tid; v < N * (kDK / 4); v += kThreads) {
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int v = tid + i * kThreads;
       const int r = v / (kDK / 4), c = v % (kDK / 4);
-      const float4 q = *reinterpret_cast<const float4*>(a.w + (size_t)r * d + k0 + 4 * c);
-      *reinterpret_cast<float4*>(sW + r * kLd + 4 * c) = q;
+      if (r < N) *reinterpret_cast<float4*>(sW + r * kLd + 4 * c) = qw[i];
     }
     __syncthreads();
     // 16x16x4 fp32 MFMA: A row = token (lane%16), B col = expert (lane%16),
@@ -278,17 +306,25 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
   for (int i = tid; i < N; i += kThreads)
-    a.part[(size_t)blockIdx.x * N + i] = ((sP[i] + sP[NP + i]) + sP[2 * NP + i]) + sP[3 * NP + i];
+    a.part[(size_t)i * gridDim.x + blockIdx.x] = ((sP[i] + sP[NP + i]) + sP[2 * NP + i]) + sP[3 * NP + i];
 }
 
-// mean_prob[i] = (sum over blocks of part[b][i], in block order) / T
+// mean_prob[i] = (sum of the per-block sums part[i][*]) / T: one block per
+// expert; thread t sums blocks t, t+256, ... in order, then a fixed tree.
 __global__ __launch_bounds__(256) void route_finalize_kernel(const float* part, int blocks, int N,
                                                              int T, float* mean_prob) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= N) return;
-  float s = 0.0f;
-  for (int b = 0; b < blocks; ++b) s += part[(size_t)b * N + i];
-  mean_prob[i] = s / (float)T;
+  __shared__ float s[256];
+  const int i = blockIdx.x;
+  const float* p = part + (size_t)i * blocks;
+  float acc = 0.0f;
+  for (int b = threadIdx.x; b < blocks; b += 256) acc += p[b];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mean_prob[i] = s[0] / (float)T;
 }
 
 int pow2_at_least(int x) {
@@ -300,6 +336,7 @@ int pow2_at_least(int x) {
 template <typename E, int TG, int NT, int G>
 hipError_t launch_g(const RouteArgs& a, int blocks, hipStream_t s) {
   constexpr int TOK = 16 * TG, NP = 16 * NT;
+  constexpr int kLd = chunk_k<TG, NT>() + 4;
   constexpr size_t stage = (size_t)(TOK + NP) * kLd * sizeof(float);
   constexpr size_t logits = (size_t)TOK * kLd * sizeof(float) + (size_t)TOK * (NP + 1) * sizeof(float);
   constexpr size_t lds = stage > logits ? stage : logits;
@@ -388,8 +425,8 @@ hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_ro
   hipError_t e = p.dtype == MOE_BF16 ? launch_tg<uint16_t>(p, a, route_blocks, s)
                                      : launch_tg<float>(p, a, route_blocks, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_finalize_kernel, dim3((p.N + 255) / 256), dim3(256), 0, s,
-                     (const float*)part, route_blocks, p.N, p.T, mean_prob);
+  hipLaunchKernelGGL(route_finalize_kernel, dim3(p.N), dim3(256), 0, s, (const float*)part,
+                     route_blocks, p.N, p.T, mean_prob);
   return hipGetLastError();
 }
 
