@@ -62,6 +62,9 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device-to-device three times (a transfer of "
+                         "known size, to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -200,6 +203,17 @@ def main():
                "sample": f"first {n} tokens of the {w.name} batch (same weights), whole oracle pass "
                          f"(router, top-K, dispatch, expert FFNs, combine) in {cs:.1f} s"}
         log(f"cpu oracle: {cs:.1f} s")
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copies: 3 x {args.calibrate_copy} MiB read + written")
+        del src, dst
 
     value = w.T * args.steps / wall
     line = {
