@@ -126,12 +126,13 @@ __device__ __forceinline__ bool find_tile_2d(const GemmArgs& a, int BM, int ntil
 // ------------------------------------------------------------ bf16 MFMA
 // Block tile BM x BN (BN counts weight rows: for SwiGLU the first half are
 // gate rows and the second half the up rows of the same BN/2 act columns),
-// 4 waves as WGM x WGN, each wave a (BM/WGM) x (BN/WGN) grid of 32x32
+// WGM x WGN waves (4 or 8), each wave a (BM/WGM) x (BN/WGN) grid of 32x32
 // accumulators.  K advances 64 at a time through two LDS stages that are
 // filled straight from global memory (buffer loads to LDS, no register
-// staging) while the matrix cores work on the other stage.
+// staging) while the matrix cores work on the other stage.  Eight waves put
+// two on every SIMD, so one wave's matrix instructions run while the other
+// waits on LDS reads or on the stage barrier.
 constexpr int BK = 64;               // k per stage: 128 bytes per tile row
-constexpr int kThreads = 256;
 
 typedef __attribute__((address_space(3))) void lds_t;
 
@@ -154,11 +155,13 @@ __device__ __forceinline__ float silu_fast(float g) {
 }
 
 template <int EPI, int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NW = WGM * WGN;                   // waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;     // 32x32 accumulators per wave
-  constexpr int AI = BM / 32, BI = BN / 32;       // 1-KB direct loads per wave per stage
-  static_assert(WGM * WGN == 4, "four waves");
+  constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW;   // 1-KB direct loads per wave per stage
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(AI >= 1 && BI >= 1, "every wave loads A and B rows");
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
   __shared__ u32x4 sA[2][BM * 8];
   __shared__ u32x4 sB[2][BN * 8];
@@ -185,12 +188,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_kernel(GemmArgs a)
   const uint32_t a_voff_o = (uint32_t)((wave * AI * 8 + lrow) * a.lda + lchunk_odd * 8) * 2;
   const uint32_t a_step = 8u * a.lda * 2;
 
-  // B rows of this wave: [wave*BN/4, +BN/4) of the tile.  SwiGLU: waves 0-1
-  // load gate rows, waves 2-3 the up rows of the same columns.
+  // B rows of this wave: [wave*BN/NW, +BN/NW) of the tile.  SwiGLU: the
+  // first half of the waves load gate rows, the second half the up rows of
+  // the same columns.
   const uint16_t* Bsrc = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
-  int b_local0 = wave * (BN / 4);
+  int b_local0 = wave * (BN / NW);
   if constexpr (EPI == EPI_SWIGLU) {
-    if (wave >= 2) {
+    if (wave >= NW / 2) {
       Bsrc = static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride;
       b_local0 -= BN / 2;
     }
@@ -353,8 +357,8 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, 
   if (g == 0) tiles[0] = 0;
 }
 
-// Tile shape per problem: large groups use 256x256 tiles (128x128 per
-// wave); groups of a few rows (decode-sized batches) use 32-row tiles so the
+// Tile shape per problem: large groups use 256x256 tiles (8 waves of
+// 128x64); groups of a few rows (decode-sized batches) use 32-row tiles so the
 // matrix cores do not multiply mostly-empty rows.
 struct TileShape { int bm; };
 
@@ -365,9 +369,9 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
   constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
   dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
   if (bm == 256)
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 256, 256, 2, 2>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 256, 256, 2, 4>), grid, dim3(64 * 8), 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 256, 1, 4>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 256, 1, 4>), grid, dim3(64 * 4), 0, s, a);
   return hipGetLastError();
 }
 
