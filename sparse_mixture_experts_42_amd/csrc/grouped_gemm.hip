@@ -27,7 +27,9 @@ struct GemmArgs {
   const void* B1;           // up-projection weights (SwiGLU), same layout
   void* C;                  // [rows][ldc]
   const int32_t* offsets;   // [G+1] group row offsets, or null: one group [0, M)
-  const int32_t* tiles;     // [G+1] prefix of row tiles per group (with offsets)
+  const int32_t* tiles;     // [G+1] prefix of full-height row tiles per group
+  const int32_t* tails;     // [G+1] prefix of short tail tiles per group
+  int tail_rows;            // tallest tail tile (0: no tail tiles)
   int G;
   int M;                    // rows of the single group when offsets == null
   int rows_alloc;           // rows addressable through A (loads are clamped)
@@ -46,6 +48,17 @@ __device__ __forceinline__ float epilogue(float g, float up) {
   if constexpr (EPI == EPI_SWIGLU) return silu(g) * up;
   else if constexpr (EPI == EPI_RELU) return g > 0.0f ? g : 0.0f;
   else return g;
+}
+
+// Row tiles of a group of n rows: full-height tiles (the last may be partly
+// filled), plus one short tail tile when the remainder is at most tail_rows
+// rows, so that a group a few rows past a multiple of the tile height does
+// not cost a whole extra full-height tile.
+__host__ __device__ inline void split_rows(int n, int BM, int tail_rows, int& full, int& tail) {
+  const int rem = n % BM;
+  const bool t = tail_rows > 0 && rem > 0 && rem <= tail_rows;
+  full = n / BM + (rem > 0 && !t ? 1 : 0);
+  tail = t ? 1 : 0;
 }
 
 // Locate the row block: returns false when the block has no work.
@@ -75,29 +88,29 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int
 
 constexpr int kPatchN = 4;   // n-tiles per patch: an XCD works on m-tiles x 4 n-tiles of one group
 
-// 1-D grid.  The hardware hands consecutive blocks to the 8 XCDs round-robin,
-// each XCD with its own L2; hardware block h < (row tiles x n-tiles) is
+// Full-height tiles of all groups (single-group form: from M).
+__device__ __forceinline__ int full_tiles_total(const GemmArgs& a, int BM) {
+  if (a.offsets != nullptr) return a.tiles[a.G];
+  int f, t;
+  split_rows(a.M, BM, a.tail_rows, f, t);
+  return f;
+}
+
+// 1-D grid: blocks [0, full tiles x n-tiles) are the full-height tiles, the
+// blocks after them the tail tiles.  The hardware hands consecutive blocks
+// to the 8 XCDs round-robin, each XCD with its own L2; full-tile block h is
 // remapped so that each XCD owns a contiguous run of logical tiles, and
 // logical tiles walk each group in patches of (all its row tiles) x kPatchN
 // n-tiles, so the activation and weight panels of a patch are fetched into
-// one L2 once and shared by the blocks of the patch.  Blocks past the real
-// tile count (the grid is sized for the largest possible count) exit.
-__device__ __forceinline__ bool find_tile_2d(const GemmArgs& a, int BM, int ntiles, int& g,
-                                             int& row0, int& rows, int& nt) {
-  const int h = blockIdx.x;
-  int mtiles_total, mt_g, base;
-  if (a.offsets == nullptr) {
-    mtiles_total = (a.M + BM - 1) / BM;
-  } else {
-    mtiles_total = a.tiles[a.G];
-  }
-  const int real = mtiles_total * ntiles;
-  if (h >= real) return false;
+// one L2 once and shared by the blocks of the patch.
+__device__ __forceinline__ void find_tile_2d(const GemmArgs& a, int BM, int ntiles, int h, int real,
+                                             int& g, int& row0, int& rows, int& nt) {
+  int mt_g, base;
   const int full = real - real % 8;
   const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
   if (a.offsets == nullptr) {
     g = 0;
-    mt_g = mtiles_total;
+    mt_g = real / ntiles;
     base = 0;
   } else {
     int lo = 0, hi = a.G;          // tiles[lo]*ntiles <= L < tiles[hi]*ntiles
@@ -120,6 +133,36 @@ __device__ __forceinline__ bool find_tile_2d(const GemmArgs& a, int BM, int ntil
   const int end = a.offsets == nullptr ? a.M : a.offsets[g + 1];
   rows = end - row0;
   if (rows > BM) rows = BM;
+}
+
+// Tail tile h (counted from the first tail block): n-tile fastest.  Returns
+// false past the last tail tile.
+__device__ __forceinline__ bool find_tail(const GemmArgs& a, int BM, int ntiles, int h, int& g,
+                                          int& row0, int& rows, int& nt) {
+  if (a.tail_rows == 0) return false;
+  const int ti = h / ntiles;
+  nt = h - ti * ntiles;
+  int full, end;
+  if (a.offsets == nullptr) {
+    int t;
+    split_rows(a.M, BM, a.tail_rows, full, t);
+    if (ti >= t) return false;
+    g = 0;
+    row0 = full * BM;
+    end = a.M;
+  } else {
+    if (ti >= a.tails[a.G]) return false;
+    int lo = 0, hi = a.G;          // tails[lo] <= ti < tails[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tails[mid] <= ti) lo = mid;
+      else hi = mid;
+    }
+    g = lo;
+    row0 = a.offsets[g] + (a.tiles[g + 1] - a.tiles[g]) * BM;
+    end = a.offsets[g + 1];
+  }
+  rows = end - row0;
   return rows > 0;
 }
 
@@ -154,8 +197,11 @@ __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-template <int EPI, int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_bf16_kernel(GemmArgs a) {
+// One BM x BN output tile of group g (rows [row0, row0+rows), n-tile by),
+// staged through the caller's LDS arrays (at least BM and BN rows a stage).
+template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, int rows, int by,
+                                          u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN]) {
   constexpr int NW = WGM * WGN;                   // waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;     // 32x32 accumulators per wave
@@ -163,14 +209,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_bf16_kernel(GemmA
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(AI >= 1 && BI >= 1, "every wave loads A and B rows");
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
-  __shared__ u32x4 sA[2][BM * 8];
-  __shared__ u32x4 sB[2][BN * 8];
-
+  static_assert(SAN >= BM * 8 && SBN >= BN * 8, "LDS stages hold the tile");
   constexpr int BNH = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per tile
-  int g, row0, rows, by;
-  if (!find_tile_2d(a, BM, (a.Ndim + BNH - 1) / BNH, g, row0, rows, by)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int wm = wave / WGN, wn = wave % WGN;
   const int n0 = by * BNH;
 
@@ -314,6 +357,42 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_bf16_kernel(GemmA
   }
 }
 
+// Groups of many rows: 256x256 tiles on 8 waves (128x64 each), and 64-row
+// tail tiles (32x64 per wave) for groups a few rows past a multiple of 256.
+constexpr int kTailRows = 64;
+
+template <int EPI>
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
+  __shared__ u32x4 sA[2][256 * 8];
+  __shared__ u32x4 sB[2][256 * 8];
+  constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
+  const int ntiles = (a.Ndim + BNH - 1) / BNH;
+  const int real = full_tiles_total(a, 256) * ntiles;
+  const int h = blockIdx.x;
+  int g, row0, rows, by;
+  if (h < real) {
+    find_tile_2d(a, 256, ntiles, h, real, g, row0, rows, by);
+    gemm_tile<EPI, 256, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
+  } else if (find_tail(a, 256, ntiles, h - real, g, row0, rows, by)) {
+    gemm_tile<EPI, kTailRows, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
+  }
+}
+
+// Groups of a few rows (decode-sized batches): 32x256 tiles on 4 waves.
+template <int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_small_kernel(GemmArgs a) {
+  __shared__ u32x4 sA[2][32 * 8];
+  __shared__ u32x4 sB[2][256 * 8];
+  constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
+  const int ntiles = (a.Ndim + BNH - 1) / BNH;
+  const int real = full_tiles_total(a, 32) * ntiles;
+  const int h = blockIdx.x;
+  if (h >= real) return;
+  int g, row0, rows, by;
+  find_tile_2d(a, 32, ntiles, h, real, g, row0, rows, by);
+  gemm_tile<EPI, 32, 256, 1, 4>(a, g, row0, rows, by, sA, sB);
+}
+
 // --------------------------------------------------------------- fp32
 // Plain fp32 path (one thread per output element), for fp32 problems.
 template <int EPI>
@@ -340,21 +419,34 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs a, int B
   }
 }
 
-// tiles[g+1] = tiles[g] + ceil((offsets[g+1]-offsets[g]) / BM), one block
+// Prefix sums over the groups of their full-height and tail row tiles
+// (split_rows), one block: tiles[g], tails[g] for g = 0..G.
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, int G, int BMr,
-                                                        int32_t* tiles) {
-  __shared__ int32_t s[256];
+                                                        int tail_rows, int32_t* tiles,
+                                                        int32_t* tails) {
+  __shared__ int32_t s[256], t[256];
   const int g = threadIdx.x;
-  s[g] = g < G ? (offsets[g + 1] - offsets[g] + BMr - 1) / BMr : 0;
+  int f = 0, tl = 0;
+  if (g < G) split_rows(offsets[g + 1] - offsets[g], BMr, tail_rows, f, tl);
+  s[g] = f;
+  t[g] = tl;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
     const int v = g >= o ? s[g - o] : 0;
+    const int w = g >= o ? t[g - o] : 0;
     __syncthreads();
     s[g] += v;
+    t[g] += w;
     __syncthreads();
   }
-  if (g < G) tiles[g + 1] = s[g];
-  if (g == 0) tiles[0] = 0;
+  if (g < G) {
+    tiles[g + 1] = s[g];
+    tails[g + 1] = t[g];
+  }
+  if (g == 0) {
+    tiles[0] = 0;
+    tails[0] = 0;
+  }
 }
 
 // Tile shape per problem: large groups use 256x256 tiles (8 waves of
@@ -369,9 +461,9 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
   constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
   dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
   if (bm == 256)
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 256, 256, 2, 4>), grid, dim3(64 * 8), 0, s, a);
+    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<EPI>, grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 256, 1, 4>), grid, dim3(64 * 4), 0, s, a);
+    hipLaunchKernelGGL(grouped_gemm_bf16_small_kernel<EPI>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -412,9 +504,13 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
   // fp32 problems: one block per 128 rows; bf16: tiles sized to the mean
   // group (all groups share one tile height so the plan is one prefix sum)
   const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : 128;
-  const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N;
+  const int tail_rows = bf16 && bm == 256 ? kTailRows : 0;
+  // grid bound: at most rows/bm + 1 full tiles and one tail tile per group
+  const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N + (tail_rows > 0 ? p.N : 0);
+  int32_t* tails = tiles + (p.N + 2);
 
-  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, offsets, p.N, bm, tiles);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, offsets, p.N, bm, tail_rows,
+                     tiles, tails);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -426,6 +522,8 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
   g1.C = act;
   g1.offsets = offsets;
   g1.tiles = tiles;
+  g1.tails = tails;
+  g1.tail_rows = tail_rows;
   g1.G = p.N;
   g1.rows_alloc = rows_alloc;
   g1.Ndim = p.d_ff;
@@ -458,7 +556,13 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
     // projection is K-segmented, one segment per shared expert
     const int ws_w = p.n_shared * p.d_ff_shared;
     const int sbm = bf16 ? pick_tiles(p.T).bm : 128;
-    const int mt = (p.T + sbm - 1) / sbm;
+    const int s_tail = bf16 && sbm == 256 ? kTailRows : 0;
+    int mt = (p.T + sbm - 1) / sbm;
+    if (s_tail > 0) {
+      int f, t;
+      split_rows(p.T, sbm, s_tail, f, t);
+      mt = f + t;
+    }
     GemmArgs s1{};
     s1.A = u;
     s1.B0 = ws_gate;
@@ -466,6 +570,8 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
     s1.C = act_shared;
     s1.offsets = nullptr;
     s1.tiles = nullptr;
+    s1.tails = nullptr;
+    s1.tail_rows = s_tail;
     s1.G = 1;
     s1.M = p.T;
     s1.rows_alloc = p.T;

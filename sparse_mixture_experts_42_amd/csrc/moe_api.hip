@@ -22,7 +22,7 @@ Workspace workspace_layout(const moe_problem_t& p) {
   w.disp_base = off;
   off = align_up(off + (size_t)w.disp_blocks * N * 4, kAlign);
   w.tiles = off;
-  off = align_up(off + (N + 2) * 4, kAlign);
+  off = align_up(off + 2 * (N + 2) * 4, kAlign);
   w.act = off;
   off = align_up(off + T * K * (size_t)p.d_ff * es, kAlign);
   w.act_shared = off;

@@ -41,7 +41,7 @@ struct Workspace {
   size_t route_part;   // fp32 [route_blocks][N]   per-block softmax sums
   size_t disp_count;   // int32 [disp_blocks][N]  per-block expert counts
   size_t disp_base;    // int32 [disp_blocks][N]  per-block rank base
-  size_t tiles;        // int32 [N+2]             grouped-GEMM tile prefix
+  size_t tiles;        // int32 [2][N+2]          grouped-GEMM full and tail tile prefixes
   size_t act;          // elem [T*K][d_ff]        gated activations
   size_t act_shared;   // elem [T][n_shared*d_ff_shared]
   size_t total;
