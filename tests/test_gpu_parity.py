@@ -221,6 +221,37 @@ def test_grouped_ffn_ragged(T, N, K, d, dff, act, shared):
     _ffn_case(w, W.generate(w))
 
 
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_grouped_ffn_group_sizes_around_tile_multiples(act):
+    """Groups of 0, 1, 255, 257, 300, 320, 321 and 600 rows (256-row tiles
+    with short tails for remainders of at most 64 rows) and a shared expert
+    over 1050 tokens (4 full tiles and a 26-row tail): every row checked."""
+    sizes = [257, 320, 321, 300, 0, 255, 1, 600]
+    T, K, d, dff = 1050, 2, 128, 192
+    w = W.Workload("tails", T=T, d=d, N=len(sizes), K=K, d_ff=dff, act=act, n_shared=1,
+                   d_ff_shared=128, seed=77, dtype="bf16")
+    x = W.generate(w)
+    p = M.problem_of(w)
+    po = _io.problem(w)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offsets[-1])
+    assert R <= T * K
+    g = torch.Generator().manual_seed(5)
+    x_perm = torch.randn(T * K, d, generator=g).to(torch.bfloat16)
+    say(f"ffn tails {act}: groups {sizes}, shared over {T} tokens")
+    xg = gpu(x)
+    o = M.moe_grouped_ffn(p, x_perm.to(DEV), torch.from_numpy(offsets).to(DEV), xg["w_gate"],
+                          xg["w_up"], xg["w_down"], xg["u"], xg["ws_gate"], xg["ws_up"],
+                          xg["ws_down"])
+    torch.cuda.synchronize()
+    eor = np.repeat(np.arange(len(sizes), dtype=np.int32), sizes)
+    xi = _io.inputs(po, x)
+    y_ref = O.ffn_rows(po, xi, elems(x_perm[:R]), eor)
+    assert_close(host(o["y_perm"][:R]), y_ref, "bf16", f"tails {act} y_perm")
+    ys_ref = O.ffn_rows(po, xi, elems(x["u"]), np.full(T, -1, np.int32))
+    assert_close(host(o["y_shared"]), ys_ref, "bf16", f"tails {act} y_shared")
+
+
 def test_grouped_ffn_integer_data_exact():
     """Small non-negative integers: every product and sum is exact, so the
     ReLU FFN on the matrix cores must equal the integer result bit for bit."""
