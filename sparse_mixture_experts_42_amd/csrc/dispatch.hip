@@ -62,10 +62,19 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* blk_c
   const int e = threadIdx.x;
   int kept = 0;
   if (e < N) {
+    // 16 block counts in flight at a time, then their running sums
+    constexpr int kChunk = 16;
     int run = 0;
-    for (int b = 0; b < blocks; ++b) {
-      blk_base[(size_t)b * N + e] = run;
-      run += blk_count[(size_t)b * N + e];
+    for (int b0 = 0; b0 < blocks; b0 += kChunk) {
+      int c[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        c[i] = b0 + i < blocks ? blk_count[(size_t)(b0 + i) * N + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (b0 + i < blocks) blk_base[(size_t)(b0 + i) * N + e] = run;
+        run += c[i];
+      }
     }
     expert_counts[e] = run;
     kept = (capacity >= 0 && run > capacity) ? capacity : run;
@@ -84,48 +93,60 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* blk_c
   if (e == 0) offsets[0] = 0;
 }
 
-__global__ __launch_bounds__(kTok) void dispatch_rank_kernel(
+// Ranks, maps and the row copy in one pass.  Block b owns kRowTok tokens
+// inside one 256-token mask chunk; it rebuilds that chunk's masks (the same
+// bits as dispatch_count_kernel's), computes the rows of its tokens, writes
+// row_of and token_of_row, then copies each token row (read once, 16-byte
+// vectors) to every kept row.
+constexpr int kRowTok = 16;                 // tokens per block
+constexpr int kVecPerLane = 8;              // 16-byte vectors in flight per lane
+static_assert(kTok % kRowTok == 0, "blocks tile the mask chunks");
+
+__global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T, int N, int K,
-    int32_t capacity, int32_t* row_of, int32_t* token_of_row) {
+    int32_t capacity, int32_t* row_of, int32_t* token_of_row, const u32x4* u, u32x4* x_perm,
+    int vec_per_row) {
   __shared__ uint32_t mask[256 * kWords];
-  const int tl = threadIdx.x;
-  const int t = blockIdx.x * kTok + tl;
-  build_masks(mask, topk_idx, T, N, K, tl, t);
-  if (t < T) {
-    const int w0 = tl >> 5;
-    const uint32_t below = (1u << (tl & 31)) - 1u;
-    for (int k = 0; k < K; ++k) {
-      const int e = topk_idx[(size_t)t * K + k];
-      int32_t row = -1;
-      if (e >= 0 && e < N) {
-        int r = __popc(mask[e * kWords + w0] & below);
-        for (int w = 0; w < w0; ++w) r += __popc(mask[e * kWords + w]);
-        const int rank = blk_base[(size_t)blockIdx.x * N + e] + r;
-        if (capacity < 0 || rank < capacity) {
-          row = offsets[e] + rank;
-          token_of_row[row] = t;
+  __shared__ int32_t srow[kRowTok * 16];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRowTok;           // first token of this block
+  const int chunk = t0 / kTok;
+  build_masks(mask, topk_idx, T, N, K, tid, chunk * kTok + tid);
+  if (tid < kRowTok) {
+    const int t = t0 + tid;
+    if (t < T) {
+      const int tl = t - chunk * kTok;
+      const int w0 = tl >> 5;
+      const uint32_t below = (1u << (tl & 31)) - 1u;
+      for (int k = 0; k < K; ++k) {
+        const int e = topk_idx[(size_t)t * K + k];
+        int32_t row = -1;
+        if (e >= 0 && e < N) {
+          int r = __popc(mask[e * kWords + w0] & below);
+          for (int w = 0; w < w0; ++w) r += __popc(mask[e * kWords + w]);
+          const int rank = blk_base[(size_t)chunk * N + e] + r;
+          if (capacity < 0 || rank < capacity) {
+            row = offsets[e] + rank;
+            token_of_row[row] = t;
+          }
         }
+        row_of[(size_t)t * K + k] = row;
+        srow[tid * 16 + k] = row;
       }
-      row_of[(size_t)t * K + k] = row;
     }
   }
   // rows past the kept total hold no token
   const int64_t total = (int64_t)T * K;
-  const int64_t stride = (int64_t)gridDim.x * kTok;
-  for (int64_t r = offsets[N] + (int64_t)blockIdx.x * kTok + tl; r < total; r += stride)
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t r = offsets[N] + (int64_t)blockIdx.x * 256 + tid; r < total; r += stride)
     token_of_row[r] = -1;
-}
+  __syncthreads();
 
-// x_perm[row_of[t][k]] = u[t]: each wave copies one token row at a time,
-// reading it once (16-byte vectors) and writing it to each kept row.
-constexpr int kVecPerLane = 8;
-__global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* u, const int32_t* row_of,
-                                                           u32x4* x_perm, int T, int K,
-                                                           int vec_per_row) {
-  const int lane = threadIdx.x & 63;
-  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
-  for (int t = wave_id; t < T; t += nwaves) {
+  // copy: wave w takes tokens w, w+4, ... of the block
+  const int lane = tid & 63;
+  for (int j = tid >> 6; j < kRowTok; j += 4) {
+    const int t = t0 + j;
+    if (t >= T) break;
     const u32x4* src = u + (size_t)t * vec_per_row;
     for (int v0 = 0; v0 < vec_per_row; v0 += 64 * kVecPerLane) {
       u32x4 q[kVecPerLane];
@@ -135,7 +156,7 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* u, const
         if (v < vec_per_row) q[i] = src[v];
       }
       for (int k = 0; k < K; ++k) {
-        const int row = row_of[(size_t)t * K + k];
+        const int row = srow[j * 16 + k];
         if (row < 0) continue;
         u32x4* dst = x_perm + (size_t)row * vec_per_row;
 #pragma unroll
@@ -163,19 +184,13 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                      blk_base, disp_blocks, p.N, capacity, expert_counts, kept_counts, offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(disp_blocks), dim3(kTok), 0, s, topk_idx,
-                     (const int32_t*)blk_base, (const int32_t*)offsets, p.T, p.N, p.K, capacity,
-                     row_of, token_of_row);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
   const int vec_per_row = (int)((size_t)p.d * es / 16);
-  long long waves = p.T;
-  long long blocks = (waves + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<const u32x4*>(u), (const int32_t*)row_of,
-                     static_cast<u32x4*>(x_perm), p.T, p.K, vec_per_row);
+  const unsigned blocks = (unsigned)((p.T + kRowTok - 1) / kRowTok);
+  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(blocks), dim3(256), 0, s, topk_idx,
+                     (const int32_t*)blk_base, (const int32_t*)offsets, p.T, p.N, p.K, capacity,
+                     row_of, token_of_row, static_cast<const u32x4*>(u),
+                     static_cast<u32x4*>(x_perm), vec_per_row);
   return hipGetLastError();
 }
 

@@ -89,10 +89,16 @@ __device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
 // k-splits.  NT = experts padded to 16 * NT (NT a power of two, <= 16).
 // G = lanes per token in the softmax/top-K phase (power of two, 4..64);
 // each lane holds R = max(1, 16*NT/64) expert slots.
-template <typename E, int TG, int NT, int G>
+// Narrow routers (at most 32 experts) are HBM-bound: DIRECT kernels skip
+// the LDS staging and load u and the router weights straight into the
+// operand registers of the 16x16x4 MFMA, two 32-wide k-steps ahead.
+// The k index of MFMA step m of k-step J on lane group q is 32J + 8q + m for
+// both operands, a permutation of k, so the dot products are unchanged.
+template <typename E, int TG, int NT, int G, bool DIRECT>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+  constexpr int NWV = 4;               // waves per block
   constexpr int TOK = 16 * TG;
-  constexpr int KS = 4 / TG;            // waves sharing a token group
+  constexpr int KS = NWV / TG;         // waves sharing a token group
   constexpr int NP = 16 * NT;           // padded experts
   constexpr int kDK = chunk_k<TG, NT>();
   constexpr int kLd = kDK + 4;          // padded LDS row (floats): spreads rows over banks
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   float* sU = smem;                     // [TOK][kLd]
   float* sW = smem + TOK * kLd;         // [NP][kLd]; reused as logits [TOK][NP+1]
-  float* sL = sW;
+  float* sL = DIRECT ? smem : sW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,12 +117,83 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int t0 = blockIdx.x * TOK;
   const int T = a.T, d = a.d, N = a.N;
 
-  // zero padded expert rows once (never overwritten below)
-  for (int i = tid; i < (NP - N) * kLd; i += kThreads) sW[N * kLd + i] = 0.0f;
-
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (DIRECT) {
+    static_assert(TG == 1 && KS == NWV, "one token group, a k-split per wave");
+    constexpr int PD = 2;                 // k-steps in flight per wave
+    // lane: token t0 + lane%16, k lanes group q = lane/16; wave ks takes the
+    // k-steps J = ks, ks+KS, ... of 32 k each
+    const int q = lane >> 4;
+    const int t = t0 + (lane & 15);
+    const bool t_ok = t < T;
+    const E* urow = static_cast<const E*>(a.u) + (size_t)(t_ok ? t : 0) * d + 8 * q;
+    const float* wrow[NT];
+    bool w_ok[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int e = 16 * j + (lane & 15);
+      w_ok[j] = e < N;
+      wrow[j] = a.w + (size_t)(w_ok[j] ? e : 0) * d + 8 * q;
+    }
+    const int nJ = d / 32;
+    // one k-step of one lane: 8 u values and 8 weights per expert tile
+    struct Step {
+      u32x4 u[sizeof(E) == 2 ? 1 : 2];
+      float4 w[NT][2];
+    };
+    auto load = [&](int J, Step& st) {
+      const bool ok = J < nJ;
+#pragma unroll
+      for (int i = 0; i < (sizeof(E) == 2 ? 1 : 2); ++i)
+        st.u[i] = (ok && t_ok) ? *reinterpret_cast<const u32x4*>(urow + 32 * J + i * 4)
+                               : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          st.w[j][i] = (ok && w_ok[j]) ? *reinterpret_cast<const float4*>(wrow[j] + 32 * J + 4 * i)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto uval = [&](const Step& st, int m) -> float {
+      if constexpr (sizeof(E) == 2) {
+        const uint32_t w = st.u[0][m >> 1];
+        return __uint_as_float((m & 1) ? (w & 0xffff0000u) : (w << 16));
+      } else {
+        return __uint_as_float(st.u[m >> 2][m & 3]);
+      }
+    };
+    auto wval = [&](const Step& st, int j, int m) -> float {
+      const float4 v = st.w[j][m >> 2];
+      return (m & 3) == 0 ? v.x : (m & 3) == 1 ? v.y : (m & 3) == 2 ? v.z : v.w;
+    };
+    auto mul = [&](const Step& st) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float av = uval(st, m);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wval(st, j, m), acc[j], 0, 0, 0);
+      }
+    };
+    // batches of PD k-steps; the next batch is requested before this one
+    // is multiplied
+    Step cur[PD], nxt[PD];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load(ks + KS * i, cur[i]);
+    for (int J0 = ks; J0 < nJ; J0 += KS * PD) {
+#pragma unroll
+      for (int i = 0; i < PD; ++i) load(J0 + KS * PD + KS * i, nxt[i]);
+#pragma unroll
+      for (int i = 0; i < PD; ++i) mul(cur[i]);
+#pragma unroll
+      for (int i = 0; i < PD; ++i) cur[i] = nxt[i];
+    }
+  } else {
+  // zero padded expert rows once (never overwritten below)
+  for (int i = tid; i < (NP - N) * kLd; i += kThreads) sW[N * kLd + i] = 0.0f;
 
   constexpr int VPR = kDK / Elem<E>::kPerVec;      // 16-byte vectors per u row chunk
   for (int k0 = 0; k0 < d; k0 += kDK) {
@@ -183,6 +260,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     }
     __syncthreads();
   }
+  }
 
   // ---- sum the k-split partial logits into sL[TOK][NP+1] (fixed order)
   constexpr int LdL = NP + 1;
@@ -200,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
 
   // ---- softmax statistics, top-K and gates: each wave takes TOK/4 tokens
-  constexpr int TPW = TOK / 4;              // tokens per wave
+  constexpr int TPW = TOK / NWV;            // tokens per wave
   constexpr int TPP = (64 / G) < TPW ? (64 / G) : TPW;  // tokens per pass
   const int seg = lane / G, j = lane % G;
   float pacc[R];
@@ -296,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     pacc[r] = v;
   }
   __syncthreads();                       // sL no longer read
-  float* sP = smem;                      // [4][NP]
+  float* sP = smem;                      // [NWV][NP]
   if (lane < G) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -305,8 +383,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < N; i += kThreads)
-    a.part[(size_t)i * gridDim.x + blockIdx.x] = ((sP[i] + sP[NP + i]) + sP[2 * NP + i]) + sP[3 * NP + i];
+  for (int i = tid; i < N; i += NWV * 64) {
+    float v = sP[i];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) v += sP[w * NP + i];
+    a.part[(size_t)i * gridDim.x + blockIdx.x] = v;
+  }
 }
 
 // mean_prob[i] = (sum of the per-block sums part[i][*]) / T: one block per
@@ -335,23 +417,25 @@ int pow2_at_least(int x) {
 
 template <typename E, int TG, int NT, int G>
 hipError_t launch_g(const RouteArgs& a, int blocks, hipStream_t s) {
+  constexpr bool DIRECT = TG == 1 && NT <= 2;
   constexpr int TOK = 16 * TG, NP = 16 * NT;
   constexpr int kLd = chunk_k<TG, NT>() + 4;
   constexpr size_t stage = (size_t)(TOK + NP) * kLd * sizeof(float);
   constexpr size_t logits = (size_t)TOK * kLd * sizeof(float) + (size_t)TOK * (NP + 1) * sizeof(float);
-  constexpr size_t lds = stage > logits ? stage : logits;
+  constexpr size_t direct = (size_t)(TOK * (NP + 1) > 4 * NP ? TOK * (NP + 1) : 4 * NP) * sizeof(float);
+  constexpr size_t lds = DIRECT ? direct : (stage > logits ? stage : logits);
   static_assert(lds <= 160 * 1024, "router tile exceeds the LDS of a CU");
   if constexpr (lds > 64 * 1024) {
     static bool attr_set = false;   // once per instantiation (idempotent)
     if (!attr_set) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&route_kernel<E, TG, NT, G>),
+          reinterpret_cast<const void*>(&route_kernel<E, TG, NT, G, DIRECT>),
           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL((route_kernel<E, TG, NT, G>), dim3(blocks), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((route_kernel<E, TG, NT, G, DIRECT>), dim3(blocks), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
