@@ -214,6 +214,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  // the tile coordinates are block-uniform; saying so keeps the buffer
+  // descriptors built from them in scalar registers
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  by = __builtin_amdgcn_readfirstlane(by);
   const int wm = wave / WGN, wn = wave % WGN;
   const int n0 = by * BNH;
 
