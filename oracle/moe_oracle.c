@@ -443,3 +443,41 @@ void oracle_layer_forward(const oracle_problem* p, const oracle_inputs* in,
   if (!row_of) free(rof);
   if (!token_of_row) free(tor);
 }
+
+/* ------------------------------------------------------------------ */
+/* router statistics                                                   */
+/* "Mixture of Experts (MoE)" glossary, auxiliary-loss and z-loss       */
+/* entries; "Noise Top-k Gating", load-balancing entry: the pages name  */
+/* the variance of the expert assignment distribution, the entropy of  */
+/* the routing probabilities and a penalty on large router logits.     */
+/* ------------------------------------------------------------------ */
+void oracle_router_stats(const oracle_problem* p, const int32_t* expert_counts,
+                         const double* mean_prob, const double* lse_sq, double* stats) {
+  const int N = p->N;
+  const double n = (double)N;
+  const double tk = (double)p->T * (double)p->K;
+  /* variance (population, over the N experts) of the assignment fractions */
+  double fv = 0.0;
+  for (int i = 0; i < N; ++i) {
+    const double f = tk > 0.0 ? (double)expert_counts[i] / tk : 0.0;
+    const double dlt = f - 1.0 / n;
+    fv += dlt * dlt;
+  }
+  stats[0] = fv / n;
+  /* variance of the mean routing probabilities */
+  double pv = 0.0;
+  for (int i = 0; i < N; ++i) {
+    const double dlt = mean_prob[i] - 1.0 / n;
+    pv += dlt * dlt;
+  }
+  stats[1] = pv / n;
+  /* entropy of the mean routing probabilities (natural log; 0 log 0 = 0) */
+  double ent = 0.0;
+  for (int i = 0; i < N; ++i)
+    if (mean_prob[i] > 0.0) ent -= mean_prob[i] * log(mean_prob[i]);
+  stats[2] = ent;
+  /* z-loss: mean over tokens of the squared log-partition of the logits */
+  double z = 0.0;
+  for (int t = 0; t < p->T; ++t) z += lse_sq[t];
+  stats[3] = p->T > 0 ? z / (double)p->T : 0.0;
+}

@@ -136,6 +136,18 @@ void oracle_layer_forward(const oracle_problem* p, const oracle_inputs* in,
                           int32_t* offsets, int32_t* row_of,
                           int32_t* token_of_row, double* out, int nthreads);
 
+/* Router statistics from the side outputs of a forward pass:
+ *   stats[0] = (1/N) sum_i (f_i - 1/N)^2,  f_i = expert_counts[i] / (T*K)
+ *   stats[1] = (1/N) sum_i (P_i - 1/N)^2,  P_i = mean_prob[i]
+ *   stats[2] = -sum_i P_i ln P_i
+ *   stats[3] = (1/T) sum_t lse_sq[t]
+ * The pages name these quantities (variance of the expert assignment
+ * distribution, entropy of the routing probabilities, a penalty on large
+ * router logits) without fixing a loss formula; combining them into a loss
+ * is the caller's choice. */
+void oracle_router_stats(const oracle_problem* p, const int32_t* expert_counts,
+                         const double* mean_prob, const double* lse_sq, double* stats);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,6 +84,7 @@ def lib():
         L.oracle_layer_rows.argtypes = [P, I, vp, vp, vp, i32, vp, vp, ctypes.c_int]
         L.oracle_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.oracle_layer_forward.argtypes = [P, I] + [vp] * 11 + [ctypes.c_int]
+        L.oracle_router_stats.argtypes = [P, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -229,3 +230,18 @@ def layer_forward(p: Problem, x: Inputs, nthreads: Optional[int] = None) -> Dict
     lib().oracle_layer_forward(ctypes.byref(p.c()), ctypes.byref(x.c),
                                *[_ptr(o[n]) for n in names], nthreads or nthreads_default())
     return o
+
+
+STAT_NAMES = ("f_var", "p_var", "p_entropy", "z_loss")
+
+
+def router_stats(p: Problem, expert_counts, mean_prob, lse_sq) -> Dict[str, float]:
+    """Variance of the assignment fractions, variance and entropy of the mean
+    probabilities, and the mean of lse^2 (see oracle_router_stats)."""
+    cnt = np.ascontiguousarray(expert_counts, dtype=np.int32)
+    mp = np.ascontiguousarray(mean_prob, dtype=np.float64)
+    ls = np.ascontiguousarray(lse_sq, dtype=np.float64)
+    assert cnt.shape == (p.N,) and mp.shape == (p.N,) and ls.shape == (p.T,)
+    st = np.zeros(4, np.float64)
+    lib().oracle_router_stats(ctypes.byref(p.c()), _ptr(cnt), _ptr(mp), _ptr(ls), _ptr(st))
+    return dict(zip(STAT_NAMES, st.tolist()))

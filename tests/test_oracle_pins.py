@@ -515,3 +515,62 @@ def test_combine_pins():
     out1 = O.combine(p1, u1, y1, np.array([[2], [0], [1]], np.int32), np.ones((3, 1)))
     ref = _io.elems_to_f64(u1, O.BF16) + _io.elems_to_f64(y1, O.BF16)[[2, 0, 1]]
     assert np.array_equal(out1, ref)
+
+
+# ------------------------------------------------------- router statistics
+
+def test_router_stats_uniform_and_one_hot_closed_forms():
+    """Uniform assignment and probabilities: both variances 0 and entropy
+    ln N.  Every assignment on one expert: f = (1, 0, ..., 0), whose
+    population variance is (N-1)/N^2, and P = e_0 has entropy 0."""
+    for N in (1, 2, 8, 64):
+        T, K = 4 * N, 2
+        p = O.Problem(T=T, d=64, N=N, K=K, d_ff=64)
+        lse = np.linspace(0.5, 3.0, T)
+        st = O.router_stats(p, np.full(N, T * K // N), np.full(N, 1.0 / N), lse)
+        assert st["f_var"] == pytest.approx(0.0, abs=1e-15)
+        assert st["p_var"] == pytest.approx(0.0, abs=1e-15)
+        assert st["p_entropy"] == pytest.approx(math.log(N), abs=1e-12)
+        assert st["z_loss"] == pytest.approx(float(np.mean(lse)), rel=1e-12)
+        cnt = np.zeros(N, np.int32)
+        cnt[0] = T * K
+        onehot = np.zeros(N)
+        onehot[0] = 1.0
+        st = O.router_stats(p, cnt, onehot, lse)
+        assert st["f_var"] == pytest.approx((N - 1) / N ** 2, rel=1e-12, abs=1e-15)
+        assert st["p_var"] == pytest.approx((N - 1) / N ** 2, rel=1e-12, abs=1e-15)
+        assert st["p_entropy"] == pytest.approx(0.0, abs=1e-15)
+
+
+def test_router_stats_worked_example_z_loss():
+    """Scores [1, 0, 2, -1] of the router worked example ("MoE: Choosing
+    Which MLPs to Use for Each Token", Figure 2) on one token: z-loss is
+    (ln(e + 1 + e^2 + e^-1))^2."""
+    g = golden("worked_example.json")
+    scores = np.array(g["scores"], np.float32)[None, :]
+    p = O.Problem(T=1, d=64, N=4, K=2, d_ff=64, gating=O.GATE_TOPK_SOFTMAX)
+    r = O.route(p, scores)
+    d = O.dispatch(p, r["topk_idx"])
+    st = O.router_stats(p, d["expert_counts"], r["mean_prob"], r["lse_sq"])
+    lse = math.log(math.e + 1.0 + math.e ** 2 + math.exp(-1.0))
+    assert st["z_loss"] == pytest.approx(lse * lse, rel=1e-7)
+    # the two selected experts (E3, E1) each hold half of the assignments
+    assert st["f_var"] == pytest.approx(((0.5 - 0.25) ** 2 * 2 + 0.25 ** 2 * 2) / 4, rel=1e-12)
+
+
+def test_router_stats_zipf_entropy():
+    """Zero router matrix, Zipf-ranked bias: P is the Zipf pmf, so the
+    entropy is -sum r^-s/H log(r^-s/H) over the ranks r = 1..N."""
+    w = W.WORKLOADS["decode_noisy"].replace(T=8, noise=False, noise_weight=0.0, d=64, d_ff=64)
+    x = W.generate(w)
+    N, s = w.N, w.zipf_s
+    Hn = W.harmonic(N, s)
+    ent = -math.fsum((r ** -s / Hn) * math.log(r ** -s / Hn) for r in range(1, N + 1))
+    p = _io.problem(w)
+    xi = O.Inputs(p, _io.to_np(x["u"]), np.zeros((N, 64), np.float32), x["b_router"].numpy())
+    r = O.route(p, O.router_logits(p, xi))
+    d = O.dispatch(p, r["topk_idx"])
+    st = O.router_stats(p, d["expert_counts"], r["mean_prob"], r["lse_sq"])
+    assert st["p_entropy"] == pytest.approx(ent, abs=1e-6)
+    # every token selects the same K experts: the K largest-bias ones
+    assert st["f_var"] == pytest.approx(((1.0 / w.K - 1.0 / N) ** 2 * w.K + (1.0 / N) ** 2 * (N - w.K)) / N, rel=1e-12)
