@@ -14,6 +14,7 @@
  *     moe_grouped_ffn  every expert's FFN over its ragged group of rows
  *     moe_combine      gate-weighted un-permute and sum, plus the residual
  *     moe_layer_forward  the four stages in order on one stream
+ *     moe_router_stats   load-balance and z statistics from the side outputs
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is DEVICE memory owned by the caller (for example
@@ -176,6 +177,27 @@ int moe_combine(const moe_problem_t* p, const void* u, const void* y_perm,
                 const int32_t* row_of, const float* topk_gate,
                 const void* y_shared, void* out, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* Router statistics of one forward pass, from its side outputs, into
+ * stats[4] fp32 (device memory):
+ *   stats[0]  variance over the N experts of the assignment fractions
+ *             f_i = expert_counts[i] / (T*K)  (counts before capacity)
+ *   stats[1]  variance over the experts of the mean probabilities mean_prob
+ *   stats[2]  entropy -sum_i P_i ln P_i of the mean probabilities
+ *   stats[3]  mean over the tokens of lse_sq (the squared log-partition of
+ *             the router logits)
+ * The "Mixture of Experts (MoE)" glossary (auxiliary-loss entry) names the
+ * variance of the expert assignment distribution and the entropy of the
+ * routing probabilities as what a load-balancing loss acts on, "Noise Top-k
+ * Gating" the variance of routing probability across experts, and the
+ * glossary's z-loss entry a penalty on large router logits; the pages fix no
+ * loss formula, so forming a loss from these is the caller's.  Variances are
+ * population variances (divided by N).  Sums run in double, in a fixed
+ * order.  No workspace.
+ * In:  expert_counts [N] int32, mean_prob [N] fp32, lse_sq [T] fp32, as
+ *      from moe_dispatch and moe_route. */
+int moe_router_stats(const moe_problem_t* p, const int32_t* expert_counts,
+                     const float* mean_prob, const float* lse_sq, float* stats, void* stream);
 
 /* The weights of one layer (all device pointers, layouts as above). */
 typedef struct moe_weights {

@@ -241,6 +241,18 @@ int moe_combine(const moe_problem_t* p, const void* u, const void* y_perm, const
                                         static_cast<hipStream_t>(stream)));
 }
 
+int moe_router_stats(const moe_problem_t* p, const int32_t* expert_counts,
+                     const float* mean_prob, const float* lse_sq, float* stats, void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(need(expert_counts, 4));
+  MOE_TRY(need(mean_prob, 4));
+  MOE_TRY(need(lse_sq, 4));
+  MOE_TRY(need(stats, 4));
+  return hip_status(moe::launch_router_stats(*p, expert_counts, mean_prob, lse_sq, stats,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
                       const moe_weights_t* wt, moe_layer_outputs_t* o, void* out, void* ws,
                       size_t ws_bytes, void* stream) {

@@ -57,6 +57,10 @@ hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_ro
                         int32_t* topk_idx, float* topk_gate, float* mean_prob,
                         float* lse_sq, float* part, int route_blocks, hipStream_t s);
 
+hipError_t launch_router_stats(const moe_problem_t& p, const int32_t* expert_counts,
+                               const float* mean_prob, const float* lse_sq, float* stats,
+                               hipStream_t s);
+
 hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t* topk_idx,
                            int32_t capacity, int32_t* expert_counts, int32_t* kept_counts,
                            int32_t* offsets, int32_t* row_of, int32_t* token_of_row,

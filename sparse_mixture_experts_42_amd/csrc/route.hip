@@ -409,6 +409,51 @@ __global__ __launch_bounds__(256) void route_finalize_kernel(const float* part, 
   if (threadIdx.x == 0) mean_prob[i] = s[0] / (float)T;
 }
 
+// Router statistics, one block: the variance of the assignment fractions
+// f_i = counts_i / (T K), the variance and entropy of the mean probabilities
+// and the mean of lse^2.  Double accumulators in a fixed order (strided
+// per-thread sums, then a fixed tree), so the result is run-to-run exact.
+__device__ __forceinline__ double block_sum(double v, double* s) {
+  s[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double r = s[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void router_stats_kernel(const int32_t* counts,
+                                                           const float* mean_prob,
+                                                           const float* lse_sq, int T, int N,
+                                                           int K, float* stats) {
+  __shared__ double s[256];
+  const int i = threadIdx.x;
+  double z = 0.0;
+  for (int t = i; t < T; t += 256) z += (double)lse_sq[t];
+  z = block_sum(z, s);
+  const double n = (double)N, tk = (double)T * (double)K;
+  double fv = 0.0, pv = 0.0, en = 0.0;
+  if (i < N) {
+    const double f = (double)counts[i] / tk - 1.0 / n;
+    const double pi = (double)mean_prob[i];
+    fv = f * f;
+    pv = (pi - 1.0 / n) * (pi - 1.0 / n);
+    en = pi > 0.0 ? -pi * log(pi) : 0.0;
+  }
+  fv = block_sum(fv, s);
+  pv = block_sum(pv, s);
+  en = block_sum(en, s);
+  if (i == 0) {
+    stats[0] = (float)(fv / n);
+    stats[1] = (float)(pv / n);
+    stats[2] = (float)en;
+    stats[3] = (float)(z / (double)T);
+  }
+}
+
 int pow2_at_least(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -511,6 +556,14 @@ hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_ro
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_finalize_kernel, dim3(p.N), dim3(256), 0, s, (const float*)part,
                      route_blocks, p.N, p.T, mean_prob);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_stats(const moe_problem_t& p, const int32_t* expert_counts,
+                               const float* mean_prob, const float* lse_sq, float* stats,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(router_stats_kernel, dim3(1), dim3(256), 0, s, expert_counts, mean_prob,
+                     lse_sq, p.T, p.N, p.K, stats);
   return hipGetLastError();
 }
 

@@ -81,8 +81,9 @@ def lib() -> ctypes.CDLL:
             L.moe_combine.argtypes = [P] + [vp] * 7 + [sz, vp]
             L.moe_layer_forward.argtypes = [P, vp, vp, ctypes.POINTER(MoeWeights),
                                             ctypes.POINTER(MoeLayerOutputs), vp, vp, sz, vp]
+            L.moe_router_stats.argtypes = [P] + [vp] * 5
             for f in ("moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
-                      "moe_layer_forward"):
+                      "moe_layer_forward", "moe_router_stats"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -231,6 +232,22 @@ def moe_grouped_ffn(p: MoeProblem, x_perm, offsets, w_gate, w_up, w_down, u=None
           _ptr(w_up), _ptr(w_down), _ptr(u), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
           _ptr(o["y_perm"]), _ptr(o["y_shared"]), _ptr(ws), ws.numel(), _stream(dev))
     return o
+
+
+STAT_NAMES = ("f_var", "p_var", "p_entropy", "z_loss")
+
+
+def moe_router_stats(p: MoeProblem, expert_counts, mean_prob, lse_sq) -> torch.Tensor:
+    """stats [4] fp32 on the device: variance of the assignment fractions,
+    variance and entropy of the mean probabilities, mean of lse^2."""
+    dev = mean_prob.device
+    _check(expert_counts, "expert_counts", (p.N,), torch.int32, dev)
+    _check(mean_prob, "mean_prob", (p.N,), torch.float32, dev)
+    _check(lse_sq, "lse_sq", (p.T,), torch.float32, dev)
+    stats = _empty((4,), torch.float32, dev)
+    _call("moe_router_stats", ctypes.byref(p), _ptr(expert_counts), _ptr(mean_prob), _ptr(lse_sq),
+          _ptr(stats), _stream(dev))
+    return stats
 
 
 def moe_combine(p: MoeProblem, u, y_perm, row_of, topk_gate, y_shared=None) -> torch.Tensor:

@@ -156,3 +156,16 @@ def test_binding_refuses_cpu_tensors():
     p = good(T=4)
     with pytest.raises(ValueError):
         M.moe_route(p, torch.zeros(4, 128, dtype=torch.bfloat16), torch.zeros(8, 128))
+
+
+def test_router_stats_argument_checks():
+    L = M.lib()
+    P = ctypes.byref(good())
+    f = lambda i: ctypes.c_void_p(FAKE + 256 * i)
+    assert L.moe_router_stats(P, None, f(1), f(2), f(3), None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_router_stats(P, f(0), None, f(2), f(3), None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_router_stats(P, f(0), f(1), None, f(3), None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_router_stats(P, f(0), f(1), f(2), None, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_router_stats(P, ctypes.c_void_p(FAKE + 2), f(1), f(2), f(3), None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_router_stats(ctypes.byref(good(N=300)), f(0), f(1), f(2), f(3), None) == M.MOE_ERR_UNSUPPORTED
+    assert L.moe_router_stats(ctypes.byref(good(T=0)), None, None, None, None, None) == M.MOE_OK

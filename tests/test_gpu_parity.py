@@ -411,3 +411,26 @@ def test_t_zero_is_a_no_op():
     u = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
     r = M.moe_route(p, u, torch.zeros(4, 64, device=DEV))
     assert r["topk_idx"].numel() == 0
+
+
+# ------------------------------------------------------ router statistics
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_router_stats(name):
+    """Statistics of the GPU side outputs against the oracle's on the same
+    values (fp32 outputs of double sums: 1e-6 relative)."""
+    w = W.WORKLOADS[name]
+    x = W.generate(w, only=W.ROUTER)
+    p = M.problem_of(w)
+    xg = gpu(x)
+    r = M.moe_route(p, xg["u"], xg["w_router"], xg["b_router"], xg["noise"])
+    d = M.moe_dispatch(p, xg["u"], r["topk_idx"])
+    st = M.moe_router_stats(p, d["expert_counts"], r["mean_prob"], r["lse_sq"])
+    torch.cuda.synchronize()
+    po = _io.problem(w)
+    ref = O.router_stats(po, host(d["expert_counts"]), host(r["mean_prob"]).astype(np.float64),
+                         host(r["lse_sq"]).astype(np.float64))
+    got = host(st).astype(np.float64)
+    say(f"{name}: stats {dict(zip(O.STAT_NAMES, got.tolist()))}")
+    for i, k in enumerate(O.STAT_NAMES):
+        assert got[i] == pytest.approx(ref[k], rel=1e-6, abs=1e-9), k
