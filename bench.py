@@ -129,6 +129,7 @@ def main():
     # ---- per-stage live timing on the same stream (same buffers)
     t = bufs.t
     R = int(t["offsets"][-1].item())
+    stats = torch.empty(4, dtype=torch.float32, device=dev)
     stage_args = {
         "route": ("moe_route", (P, vp(xg["u"]), vp(xg["w_router"]), vp(xg["b_router"]),
                                 vp(xg["noise"]), None, vp(t["topk_idx"]), vp(t["topk_gate"]),
@@ -142,6 +143,8 @@ def main():
                                             vp(t["y_perm"]), vp(t["y_shared"]), vp(ws), ws.numel(), sp)),
         "combine": ("moe_combine", (P, vp(xg["u"]), vp(t["y_perm"]), vp(t["row_of"]),
                                     vp(t["topk_gate"]), vp(t["y_shared"]), vp(t["out"]), None, 0, sp)),
+        "router_stats": ("moe_router_stats", (P, vp(t["expert_counts"]), vp(t["mean_prob"]),
+                                              vp(t["lse_sq"]), vp(stats), sp)),
     }
     stages_ms = {}
     for name, (fn, a) in stage_args.items():
