@@ -481,3 +481,57 @@ void oracle_router_stats(const oracle_problem* p, const int32_t* expert_counts,
   for (int t = 0; t < p->T; ++t) z += lse_sq[t];
   stats[3] = p->T > 0 ? z / (double)p->T : 0.0;
 }
+
+/* ------------------------------------------------------------------ */
+/* expert choice  [Glossary] sparse-MoE entry: experts select the       */
+/* top-k tokens; [MoE-notes] affinities s = Softmax_i(u_t^T e_i)        */
+/* ------------------------------------------------------------------ */
+
+int32_t oracle_ec_capacity(int32_t T, int32_t K, int32_t N, float cf) {
+  return oracle_capacity(T, K, N, cf > 0.0f ? cf : 1.0f);
+}
+
+typedef struct { double s; int32_t t; } ec_key;
+
+/* s descending, then token ascending */
+static int ec_cmp(const void* a, const void* b) {
+  const ec_key* x = (const ec_key*)a;
+  const ec_key* y = (const ec_key*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->t > y->t) - (x->t < y->t);
+}
+
+void oracle_ec_select(const oracle_problem* p, const double* probs, int32_t C,
+                      int32_t* expert_tokens, double* expert_gates, int32_t* row_of,
+                      double* gate_of) {
+  const int T = p->T, N = p->N;
+  ec_key* keys = (ec_key*)malloc(sizeof(ec_key) * (size_t)(T > 0 ? T : 1));
+  unsigned char* sel = (unsigned char*)malloc((size_t)(T > 0 ? T : 1));
+  for (size_t i = 0; i < (size_t)T * N; ++i) {
+    row_of[i] = -1;
+    gate_of[i] = 0.0;
+  }
+  for (int e = 0; e < N; ++e) {
+    for (int t = 0; t < T; ++t) {
+      keys[t].s = probs[(size_t)t * N + e];
+      keys[t].t = t;
+    }
+    qsort(keys, (size_t)T, sizeof(ec_key), ec_cmp);
+    memset(sel, 0, (size_t)T);
+    for (int j = 0; j < C && j < T; ++j) sel[keys[j].t] = 1;
+    /* the expert's rows hold its tokens in ascending token order */
+    int j = 0;
+    for (int t = 0; t < T; ++t) {
+      if (!sel[t]) continue;
+      const double g = probs[(size_t)t * N + e];
+      expert_tokens[(size_t)e * C + j] = t;
+      expert_gates[(size_t)e * C + j] = g;
+      row_of[(size_t)t * N + e] = e * C + j;
+      gate_of[(size_t)t * N + e] = g;
+      ++j;
+    }
+  }
+  free(keys);
+  free(sel);
+}

@@ -148,6 +148,22 @@ void oracle_layer_forward(const oracle_problem* p, const oracle_inputs* in,
 void oracle_router_stats(const oracle_problem* p, const int32_t* expert_counts,
                          const double* mean_prob, const double* lse_sq, double* stats);
 
+/* Expert choice ("Mixture of Experts (MoE)" glossary, sparse-MoE entry:
+ * experts select their top-k tokens).  Capacity C per expert: the token-
+ * choice capacity ceil(cf*T*K/N) capped at T, with cf <= 0 read as 1. */
+int32_t oracle_ec_capacity(int32_t T, int32_t K, int32_t N, float cf);
+
+/* Each expert e takes the C tokens with the largest probs[t][e] (ties: the
+ * lower token index); its rows e*C .. e*C+C-1 hold them in ascending token
+ * order.  probs [T][N] are the affinities s (as double; the GPU's fp32
+ * values may be passed widened, so that both sides decide on the same
+ * numbers).  C <= T.
+ *   expert_tokens [N][C], expert_gates [N][C]: token and gate s of each row
+ *   row_of [T][N]: row of (t, e) or -1;  gate_of [T][N]: s or 0          */
+void oracle_ec_select(const oracle_problem* p, const double* probs, int32_t C,
+                      int32_t* expert_tokens, double* expert_gates, int32_t* row_of,
+                      double* gate_of);
+
 #ifdef __cplusplus
 }
 #endif

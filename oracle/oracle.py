@@ -5,6 +5,7 @@ this module.  Arrays are numpy; bf16 data is passed as its raw uint16 bit
 pattern.  Every call builds the oracle library first if it is missing.
 """
 import ctypes
+import dataclasses
 import os
 from dataclasses import dataclass
 from typing import Dict, Optional
@@ -85,6 +86,9 @@ def lib():
         L.oracle_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.oracle_layer_forward.argtypes = [P, I] + [vp] * 11 + [ctypes.c_int]
         L.oracle_router_stats.argtypes = [P, vp, vp, vp, vp]
+        L.oracle_ec_capacity.argtypes = [i32, i32, i32, ctypes.c_float]
+        L.oracle_ec_capacity.restype = i32
+        L.oracle_ec_select.argtypes = [P, vp, i32, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -245,3 +249,29 @@ def router_stats(p: Problem, expert_counts, mean_prob, lse_sq) -> Dict[str, floa
     st = np.zeros(4, np.float64)
     lib().oracle_router_stats(ctypes.byref(p.c()), _ptr(cnt), _ptr(mp), _ptr(ls), _ptr(st))
     return dict(zip(STAT_NAMES, st.tolist()))
+
+
+def ec_capacity(T: int, K: int, N: int, cf: float) -> int:
+    return int(lib().oracle_ec_capacity(T, K, N, float(cf)))
+
+
+def ec_select(p: Problem, probs, C: int) -> Dict[str, np.ndarray]:
+    """Expert-choice selection from affinities probs [T][N] (see
+    oracle_ec_select)."""
+    pr = np.ascontiguousarray(probs, dtype=np.float64)
+    assert pr.shape == (p.T, p.N) and 0 <= C <= p.T
+    o = dict(expert_tokens=np.zeros((p.N, C), np.int32), expert_gates=np.zeros((p.N, C), np.float64),
+             row_of=np.zeros((p.T, p.N), np.int32), gate_of=np.zeros((p.T, p.N), np.float64))
+    lib().oracle_ec_select(ctypes.byref(p.c()), _ptr(pr), C, _ptr(o["expert_tokens"]),
+                           _ptr(o["expert_gates"]), _ptr(o["row_of"]), _ptr(o["gate_of"]))
+    return o
+
+
+def ec_layer_rows(p: Problem, x: Inputs, sel: Dict[str, np.ndarray], tokens=None,
+                  nthreads: Optional[int] = None) -> np.ndarray:
+    """Layer output of expert choice: u_t + sum over the experts that chose
+    t, in ascending expert order, of s * FFN_e(u_t) (+ shared experts) -- the
+    token-choice sum with one slot per expert."""
+    pe = dataclasses.replace(p, K=p.N)
+    idx = np.tile(np.arange(p.N, dtype=np.int32), (p.T, 1))
+    return layer_rows(pe, x, idx, sel["gate_of"], sel["row_of"], tokens, nthreads)

@@ -574,3 +574,72 @@ def test_router_stats_zipf_entropy():
     assert st["p_entropy"] == pytest.approx(ent, abs=1e-6)
     # every token selects the same K experts: the K largest-bias ones
     assert st["f_var"] == pytest.approx(((1.0 / w.K - 1.0 / N) ** 2 * w.K + (1.0 / N) ** 2 * (N - w.K)) / N, rel=1e-12)
+
+
+# ---------------------------------------------------------- expert choice
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 6), st.integers(1, 30), st.data())
+def test_ec_select_matches_sorting(N, T, data):
+    """Each expert takes the C tokens first in a sort by (affinity
+    descending, token ascending), then lists them in token order; values
+    from a tiny set so that ties are common."""
+    C = data.draw(st.integers(0, T))
+    vals = data.draw(st.lists(st.sampled_from([0.0, 0.125, 0.25, 0.5, 0.75]), min_size=T * N, max_size=T * N))
+    pr = np.array(vals, np.float64).reshape(T, N)
+    p = O.Problem(T=T, d=64, N=N, K=1, d_ff=64)
+    o = O.ec_select(p, pr, C)
+    for e in range(N):
+        chosen = sorted(sorted(range(T), key=lambda t: (-pr[t, e], t))[:C])
+        assert o["expert_tokens"][e].tolist() == chosen
+        assert o["expert_gates"][e].tolist() == [pr[t, e] for t in chosen]
+        for j, t in enumerate(chosen):
+            assert o["row_of"][t, e] == e * C + j and o["gate_of"][t, e] == pr[t, e]
+    # every expert holds exactly C tokens; rows are a bijection onto 0..N*C-1
+    rows = o["row_of"][o["row_of"] >= 0]
+    assert sorted(rows.tolist()) == list(range(N * C))
+
+
+def test_ec_capacity():
+    assert O.ec_capacity(4096, 1, 8, 1.25) == 640
+    assert O.ec_capacity(8192, 2, 8, 0.0) == 2048          # cf <= 0 read as 1: T*K/N
+    assert O.ec_capacity(10, 2, 3, 0.0) == 7               # ceil(20/3)
+    assert O.ec_capacity(10, 1, 1, 4.0) == 10              # capped at T
+
+
+def test_ec_worked_example_single_token():
+    """One token with the router scores [1, 0, 2, -1] of the worked example
+    ("MoE: Choosing Which MLPs to Use for Each Token", Figure 2): with C = 1
+    every expert takes it, so its gates are the softmax over all four."""
+    g = golden("worked_example.json")
+    p = O.Problem(T=1, d=8, N=4, K=2, d_ff=8, gating=O.GATE_SOFTMAX_TOPK)
+    r = O.route(p, np.array([g["scores"]], np.float32), want_probs=True)
+    o = O.ec_select(p, r["probs"], 1)
+    assert o["expert_tokens"].ravel().tolist() == [0, 0, 0, 0]
+    assert o["gate_of"][0] == pytest.approx(g["closed_forms"]["softmax_all"], abs=1e-15)
+
+
+def test_ec_with_c_equal_t_is_the_dense_softmax_mixture():
+    """C = T: every expert takes every token, so the layer is
+    u + sum_i s_i FFN_i(u) -- token choice with K = N under the all-expert
+    softmax gating, computed through the token-choice path."""
+    w = W.Workload("ecd", T=12, d=64, N=4, K=4, d_ff=64, gating="softmax_topk", seed=31, n_shared=1,
+                   d_ff_shared=64)
+    x = W.generate(w)
+    p = _io.problem(w)
+    xi = _io.inputs(p, x)
+    H = O.router_logits(p, xi)
+    r = O.route(p, H, want_probs=True)
+    sel = O.ec_select(p, r["probs"], w.T)
+    ec = O.ec_layer_rows(p, xi, sel)
+    dsp = O.dispatch(p, r["topk_idx"])
+    tc = O.layer_rows(p, xi, r["topk_idx"], r["topk_gate"], dsp["row_of"])
+    # same terms, summed in a different expert order (rank vs index)
+    assert ec == pytest.approx(tc, rel=1e-12, abs=1e-12)
+
+
+def test_ec_equal_affinities_pick_lowest_tokens():
+    T, N, C = 9, 3, 4
+    p = O.Problem(T=T, d=64, N=N, K=1, d_ff=64)
+    o = O.ec_select(p, np.full((T, N), 1.0 / N), C)
+    assert (o["expert_tokens"] == np.arange(C)).all()
