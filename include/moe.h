@@ -15,6 +15,7 @@
  *     moe_combine      gate-weighted un-permute and sum, plus the residual
  *     moe_layer_forward  the four stages in order on one stream
  *     moe_router_stats   load-balance and z statistics from the side outputs
+ *     moe_ec_*           expert-choice routing (experts select their tokens)
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is DEVICE memory owned by the caller (for example
@@ -234,6 +235,76 @@ typedef struct moe_layer_outputs {
 int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
                       const moe_weights_t* w, moe_layer_outputs_t* o, void* out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Expert choice ("Mixture of Experts (MoE)" glossary, sparse-MoE entry:
+ * expert choice lets the experts select their top-k tokens).
+ *   affinities  s[t][i] = Softmax over the N experts of token t's router
+ *               scores H (the same H as moe_route: fp32 router, bias,
+ *               noise), as in the MoE-layer equation;
+ *   selection   expert i takes the C tokens of largest s[.][i] (ties: the
+ *               lower token index), C = moe_ec_capacity(T, K, N, cf);
+ *   rows        expert i owns rows i*C .. i*C+C-1 of x_perm / y_perm, its
+ *               tokens in ascending token order;
+ *   output      out_t = u_t + sum over the experts i that chose t, in
+ *               ascending i, of s[t][i] * FFN_i(u_t), + sum of the shared
+ *               experts; fp32 accumulation, one rounding to elem.
+ * A token may be chosen by no expert (out_t = u_t + shared) or by several;
+ * every expert processes exactly C rows.  Problem fields as for token
+ * choice (K only sets C; gating is unused). */
+
+/* C = ceil(cf*T*K/N) capped at T, with cf <= 0 read as 1. */
+int32_t moe_ec_capacity(int32_t T, int32_t K, int32_t N, float cf);
+
+/* Workspace bytes of the expert-choice calls (0 for T == 0). */
+size_t moe_ec_workspace_size(const moe_problem_t* p);
+
+/* Router scores, affinities and the experts' selections.
+ * In:  u [T][d] elem; w_router [N][d], b_router [N] or NULL, noise [T][N]
+ *      or NULL (fp32), as for moe_route.
+ * Out: scores [T][N] fp32 or NULL; probs [N][T] fp32 (expert-major s);
+ *      expert_tokens [N][C] int32; expert_gates [N][C] fp32;
+ *      row_of [T][N] int32 (row of (t, i) or -1); gate_of [T][N] fp32
+ *      (s[t][i] or 0); offsets [N+1] int32 (i*C); mean_prob [N];
+ *      lse_sq [T] (as moe_route). */
+int moe_ec_route(const moe_problem_t* p, const void* u, const float* w_router,
+                 const float* b_router, const float* noise, float* scores, float* probs,
+                 int32_t* expert_tokens, float* expert_gates, int32_t* row_of, float* gate_of,
+                 int32_t* offsets, float* mean_prob, float* lse_sq, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* x_perm[i*C + j] = u[expert_tokens[i][j]]: x_perm [N*C][d] elem. */
+int moe_ec_dispatch(const moe_problem_t* p, const void* u, const int32_t* expert_tokens,
+                    void* x_perm, void* stream);
+
+/* out [T][d] elem from y_perm [N*C][d], row_of / gate_of [T][N] and y_shared
+ * [T][d] or NULL (as described above). */
+int moe_ec_combine(const moe_problem_t* p, const void* u, const void* y_perm,
+                   const int32_t* row_of, const float* gate_of, const void* y_shared, void* out,
+                   void* stream);
+
+/* Outputs and intermediates of the chained expert-choice pass. */
+typedef struct moe_ec_outputs {
+  float* scores;          /* [T][N] fp32 or NULL */
+  float* probs;           /* [N][T] fp32         */
+  int32_t* expert_tokens; /* [N][C]              */
+  float* expert_gates;    /* [N][C]              */
+  int32_t* row_of;        /* [T][N]              */
+  float* gate_of;         /* [T][N]              */
+  int32_t* offsets;       /* [N+1]               */
+  float* mean_prob;       /* [N]                 */
+  float* lse_sq;          /* [T]                 */
+  void* x_perm;           /* [N*C][d] elem       */
+  void* y_perm;           /* [N*C][d] elem       */
+  void* y_shared;         /* [T][d] elem or NULL */
+} moe_ec_outputs_t;
+
+/* moe_ec_route, moe_ec_dispatch, the grouped expert FFN over the N groups
+ * of C rows (and the shared experts), and moe_ec_combine, in order on
+ * `stream`; ws of at least moe_ec_workspace_size(p) bytes. */
+int moe_ec_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
+                         const moe_weights_t* w, moe_ec_outputs_t* o, void* out, void* ws,
+                         size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

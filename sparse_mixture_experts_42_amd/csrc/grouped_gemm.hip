@@ -498,7 +498,7 @@ hipError_t run_gemm(const GemmArgs& a, int epi, bool bf16, int bm, int mtiles, h
 
 }  // namespace
 
-hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
+hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void* x_perm,
                               const int32_t* offsets, const void* w_gate, const void* w_up,
                               const void* w_down, const void* u, const void* ws_gate,
                               const void* ws_up, const void* ws_down, void* y_perm,
@@ -506,7 +506,6 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
                               hipStream_t s) {
   const bool bf16 = p.dtype == MOE_BF16;
   const int epi1 = p.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
-  const int rows_alloc = p.T * p.K;
   // fp32 problems: one block per 128 rows; bf16: tiles sized to the mean
   // group (all groups share one tile height so the plan is one prefix sum)
   const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : 128;

@@ -31,9 +31,43 @@ Workspace workspace_layout(const moe_problem_t& p) {
   return w;
 }
 
+static int32_t ec_capacity_of(int32_t T, int32_t K, int32_t N, float cf) {
+  const float c = cf > 0.0f ? cf : 1.0f;
+  double v = ceil((double)c * (double)((int64_t)T * K) / (double)N);
+  if (v > (double)T) v = (double)T;
+  return (int32_t)v;
+}
+
+EcWorkspace ec_workspace_layout(const moe_problem_t& p) {
+  EcWorkspace w{};
+  const size_t T = (size_t)p.T, N = (size_t)p.N, K = (size_t)p.K;
+  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
+  const int rt = route_tokens_per_block(p);
+  w.route_blocks = (int)((T + rt - 1) / rt);
+  w.C = ec_capacity_of(p.T, p.K, p.N, p.capacity_factor);
+  size_t off = 0;
+  w.route_part = off;
+  off = align_up(off + (size_t)w.route_blocks * N * 4, kAlign);
+  w.scores = off;
+  off = align_up(off + T * N * 4, kAlign);
+  w.tk_idx = off;
+  off = align_up(off + T * K * 4, kAlign);
+  w.tk_gate = off;
+  off = align_up(off + T * K * 4, kAlign);
+  w.tiles = off;
+  off = align_up(off + 2 * (N + 2) * 4, kAlign);
+  w.act = off;
+  off = align_up(off + N * (size_t)w.C * (size_t)p.d_ff * es, kAlign);
+  w.act_shared = off;
+  if (p.n_shared > 0) off = align_up(off + T * (size_t)p.n_shared * p.d_ff_shared * es, kAlign);
+  w.total = off;
+  return w;
+}
+
 }  // namespace moe
 
 using moe::Workspace;
+using moe::EcWorkspace;
 
 namespace {
 
@@ -223,7 +257,7 @@ int moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* o
   const Workspace w = moe::workspace_layout(*p);
   MOE_TRY(check_ws(ws, ws_bytes, w.total));
   return hip_status(moe::launch_grouped_ffn(
-      *p, x_perm, offsets, w_gate, w_up, w_down, u, ws_gate, ws_up, ws_down, y_perm,
+      *p, p->T * p->K, x_perm, offsets, w_gate, w_up, w_down, u, ws_gate, ws_up, ws_down, y_perm,
       p->n_shared > 0 ? y_shared : nullptr, reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)),
       ws_at(ws, w.act), ws_at(ws, w.act_shared), static_cast<hipStream_t>(stream)));
 }
@@ -281,13 +315,149 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
                            reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)), w.disp_blocks, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   void* ysh = p->n_shared > 0 ? o->y_shared : nullptr;
-  e = moe::launch_grouped_ffn(*p, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u,
+  e = moe::launch_grouped_ffn(*p, p->T * p->K, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u,
                               wt->ws_gate, wt->ws_up, wt->ws_down, o->y_perm, ysh,
                               reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)), ws_at(ws, w.act),
                               ws_at(ws, w.act_shared), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(*p, u, o->y_perm, o->row_of, o->topk_gate, ysh, out, s);
   return hip_status(e);
+}
+
+// ------------------------------------------------------------ expert choice
+
+int32_t moe_ec_capacity(int32_t T, int32_t K, int32_t N, float cf) {
+  if (N <= 0 || T < 0 || K < 0) return -1;
+  return moe::ec_capacity_of(T, K, N, cf);
+}
+
+size_t moe_ec_workspace_size(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK || p->T == 0) return 0;
+  return moe::ec_workspace_layout(*p).total;
+}
+
+namespace {
+
+int check_ec_problem(const moe_problem_t* p) {
+  MOE_TRY(check_problem(p));
+  const int64_t C = moe::ec_capacity_of(p->T, p->K, p->N, p->capacity_factor);
+  if ((int64_t)p->N * C > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_ec_route(const moe_problem_t* p, const void* u, const float* w_router,
+                   const float* b_router, const float* noise, const float* scores,
+                   const float* probs, const int32_t* expert_tokens, const float* expert_gates,
+                   const int32_t* row_of, const float* gate_of, const int32_t* offsets,
+                   const float* mean_prob, const float* lse_sq) {
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(w_router, 16));
+  MOE_TRY(maybe(b_router, 4));
+  MOE_TRY(maybe(noise, 4));
+  MOE_TRY(maybe(scores, 4));
+  MOE_TRY(need(probs, 4));
+  MOE_TRY(need(expert_tokens, 4));
+  MOE_TRY(need(expert_gates, 4));
+  MOE_TRY(need(row_of, 4));
+  MOE_TRY(need(gate_of, 4));
+  MOE_TRY(need(offsets, 4));
+  MOE_TRY(need(mean_prob, 4));
+  MOE_TRY(need(lse_sq, 4));
+  if (noise != nullptr && !isfinite(p->noise_weight)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+hipError_t ec_route_launch(const moe_problem_t* p, const void* u, const float* w_router,
+                           const float* b_router, const float* noise, float* scores,
+                           float* probs, int32_t* expert_tokens, float* expert_gates,
+                           int32_t* row_of, float* gate_of, int32_t* offsets, float* mean_prob,
+                           float* lse_sq, void* ws, const EcWorkspace& w, hipStream_t s) {
+  float* sc = scores != nullptr ? scores : reinterpret_cast<float*>(ws_at(ws, w.scores));
+  hipError_t e = moe::launch_route(*p, u, w_router, b_router, noise, sc,
+                                   reinterpret_cast<int32_t*>(ws_at(ws, w.tk_idx)),
+                                   reinterpret_cast<float*>(ws_at(ws, w.tk_gate)), mean_prob,
+                                   lse_sq, reinterpret_cast<float*>(ws_at(ws, w.route_part)),
+                                   w.route_blocks, s);
+  if (e != hipSuccess) return e;
+  return moe::launch_ec_select(*p, sc, w.C, probs, expert_tokens, expert_gates, row_of, gate_of,
+                               offsets, s);
+}
+
+}  // namespace
+
+int moe_ec_route(const moe_problem_t* p, const void* u, const float* w_router,
+                 const float* b_router, const float* noise, float* scores, float* probs,
+                 int32_t* expert_tokens, float* expert_gates, int32_t* row_of, float* gate_of,
+                 int32_t* offsets, float* mean_prob, float* lse_sq, void* ws, size_t ws_bytes,
+                 void* stream) {
+  MOE_TRY(check_ec_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_ec_route(p, u, w_router, b_router, noise, scores, probs, expert_tokens,
+                         expert_gates, row_of, gate_of, offsets, mean_prob, lse_sq));
+  const EcWorkspace w = moe::ec_workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.tiles));
+  return hip_status(ec_route_launch(p, u, w_router, b_router, noise, scores, probs,
+                                    expert_tokens, expert_gates, row_of, gate_of, offsets,
+                                    mean_prob, lse_sq, ws, w, static_cast<hipStream_t>(stream)));
+}
+
+int moe_ec_dispatch(const moe_problem_t* p, const void* u, const int32_t* expert_tokens,
+                    void* x_perm, void* stream) {
+  MOE_TRY(check_ec_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(expert_tokens, 4));
+  MOE_TRY(need(x_perm, 16));
+  const int32_t C = moe::ec_capacity_of(p->T, p->K, p->N, p->capacity_factor);
+  return hip_status(moe::launch_ec_gather(*p, u, expert_tokens, p->N * C, x_perm,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_ec_combine(const moe_problem_t* p, const void* u, const void* y_perm,
+                   const int32_t* row_of, const float* gate_of, const void* y_shared, void* out,
+                   void* stream) {
+  MOE_TRY(check_ec_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(y_perm, 16));
+  MOE_TRY(need(row_of, 4));
+  MOE_TRY(need(gate_of, 4));
+  MOE_TRY(need(out, 16));
+  if (p->n_shared > 0) MOE_TRY(need(y_shared, 16));
+  return hip_status(moe::launch_ec_combine(*p, u, y_perm, row_of, gate_of,
+                                           p->n_shared > 0 ? y_shared : nullptr, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int moe_ec_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
+                         const moe_weights_t* wt, moe_ec_outputs_t* o, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  MOE_TRY(check_ec_problem(p));
+  if (p->T == 0) return MOE_OK;
+  if (wt == nullptr || o == nullptr) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ec_route(p, u, wt->w_router, wt->b_router, noise, o->scores, o->probs,
+                         o->expert_tokens, o->expert_gates, o->row_of, o->gate_of, o->offsets,
+                         o->mean_prob, o->lse_sq));
+  MOE_TRY(check_ffn(p, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u, wt->ws_gate,
+                    wt->ws_up, wt->ws_down, o->y_perm, o->y_shared));
+  MOE_TRY(need(out, 16));
+  const EcWorkspace w = moe::ec_workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = ec_route_launch(p, u, wt->w_router, wt->b_router, noise, o->scores, o->probs,
+                                 o->expert_tokens, o->expert_gates, o->row_of, o->gate_of,
+                                 o->offsets, o->mean_prob, o->lse_sq, ws, w, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int rows = p->N * w.C;
+  e = moe::launch_ec_gather(*p, u, o->expert_tokens, rows, o->x_perm, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  void* ysh = p->n_shared > 0 ? o->y_shared : nullptr;
+  e = moe::launch_grouped_ffn(*p, rows, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down,
+                              u, wt->ws_gate, wt->ws_up, wt->ws_down, o->y_perm, ysh,
+                              reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)), ws_at(ws, w.act),
+                              ws_at(ws, w.act_shared), s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_ec_combine(*p, u, o->y_perm, o->row_of, o->gate_of, ysh, out, s));
 }
 
 }  // extern "C"

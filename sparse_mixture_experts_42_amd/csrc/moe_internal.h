@@ -67,7 +67,8 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                            void* x_perm, int32_t* blk_count, int32_t* blk_base,
                            int disp_blocks, hipStream_t s);
 
-hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
+// rows_alloc: rows of x_perm / y_perm / act (T*K for token choice).
+hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void* x_perm,
                               const int32_t* offsets, const void* w_gate, const void* w_up,
                               const void* w_down, const void* u, const void* ws_gate,
                               const void* ws_up, const void* ws_down, void* y_perm,
@@ -77,5 +78,29 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, const void* x_perm,
 hipError_t launch_combine(const moe_problem_t& p, const void* u, const void* y_perm,
                           const int32_t* row_of, const float* topk_gate,
                           const void* y_shared, void* out, hipStream_t s);
+
+// expert choice (expert_choice.hip)
+hipError_t launch_ec_select(const moe_problem_t& p, const float* scores, int32_t C,
+                            float* probsT, int32_t* expert_tokens, float* expert_gates,
+                            int32_t* row_of, float* gate_of, int32_t* offsets, hipStream_t s);
+hipError_t launch_ec_gather(const moe_problem_t& p, const void* u, const int32_t* tokens,
+                            int rows, void* x_perm, hipStream_t s);
+hipError_t launch_ec_combine(const moe_problem_t& p, const void* u, const void* y_perm,
+                             const int32_t* row_of, const float* gate_of, const void* y_shared,
+                             void* out, hipStream_t s);
+
+struct EcWorkspace {
+  size_t route_part;   // fp32 [route_blocks][N]
+  size_t scores;       // fp32 [T][N]      router scores when the caller keeps none
+  size_t tk_idx;       // int32 [T][K]     token-choice top-K of the router (unused)
+  size_t tk_gate;      // fp32 [T][K]
+  size_t tiles;        // int32 [2][N+2]
+  size_t act;          // elem [N*C][d_ff]
+  size_t act_shared;   // elem [T][n_shared*d_ff_shared]
+  size_t total;
+  int route_blocks;
+  int C;
+};
+EcWorkspace ec_workspace_layout(const moe_problem_t& p);
 
 }  // namespace moe

@@ -46,6 +46,12 @@ class MoeLayerOutputs(ctypes.Structure):
                  "y_shared")]
 
 
+class MoeEcOutputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("scores", "probs", "expert_tokens", "expert_gates", "row_of", "gate_of",
+                 "offsets", "mean_prob", "lse_sq", "x_perm", "y_perm", "y_shared")]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn}: {moe_status_string(status)}")
@@ -82,8 +88,18 @@ def lib() -> ctypes.CDLL:
             L.moe_layer_forward.argtypes = [P, vp, vp, ctypes.POINTER(MoeWeights),
                                             ctypes.POINTER(MoeLayerOutputs), vp, vp, sz, vp]
             L.moe_router_stats.argtypes = [P] + [vp] * 5
+            L.moe_ec_capacity.argtypes = [i32, i32, i32, ctypes.c_float]
+            L.moe_ec_capacity.restype = i32
+            L.moe_ec_workspace_size.argtypes = [P]
+            L.moe_ec_workspace_size.restype = sz
+            L.moe_ec_route.argtypes = [P] + [vp] * 14 + [sz, vp]
+            L.moe_ec_dispatch.argtypes = [P] + [vp] * 4
+            L.moe_ec_combine.argtypes = [P] + [vp] * 7
+            L.moe_ec_layer_forward.argtypes = [P, vp, vp, ctypes.POINTER(MoeWeights),
+                                               ctypes.POINTER(MoeEcOutputs), vp, vp, sz, vp]
             for f in ("moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
-                      "moe_layer_forward", "moe_router_stats"):
+                      "moe_layer_forward", "moe_router_stats", "moe_ec_route",
+                      "moe_ec_dispatch", "moe_ec_combine", "moe_ec_layer_forward"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -322,4 +338,123 @@ def layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], want_s
                      x.get("ws_gate"), x.get("ws_up"), x.get("ws_down"))
     bufs = LayerBuffers(p, u.device, want_scores)
     moe_layer_forward(p, u, x.get("noise"), w, bufs)
+    return bufs.t
+
+
+# ------------------------------------------------------------ expert choice
+
+def moe_ec_capacity(T: int, K: int, N: int, cf: float) -> int:
+    return int(lib().moe_ec_capacity(int(T), int(K), int(N), float(cf)))
+
+
+def moe_ec_workspace_size(p: MoeProblem) -> int:
+    return int(lib().moe_ec_workspace_size(ctypes.byref(p)))
+
+
+_ec_ws_cache: Dict[int, torch.Tensor] = {}
+
+
+def ec_workspace(p: MoeProblem, device) -> torch.Tensor:
+    """A cached workspace buffer (uint8) big enough for the expert-choice calls of p."""
+    n = max(moe_ec_workspace_size(p), 256)
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    buf = _ec_ws_cache.get(key)
+    if buf is None or buf.numel() < n:
+        buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        _ec_ws_cache[key] = buf
+    return buf
+
+
+def moe_ec_route(p: MoeProblem, u, w_router, b_router=None, noise=None, want_scores=True,
+                 ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    dev = u.device
+    C = moe_ec_capacity(p.T, p.K, p.N, p.capacity_factor)
+    _check(u, "u", (p.T, p.d), TORCH_DTYPE[p.dtype], dev)
+    _check(w_router, "w_router", (p.N, p.d), torch.float32, dev)
+    _check(b_router, "b_router", (p.N,), torch.float32, dev, optional=True)
+    _check(noise, "noise", (p.T, p.N), torch.float32, dev, optional=True)
+    f32, i32 = torch.float32, torch.int32
+    o = dict(scores=_empty((p.T, p.N), f32, dev) if want_scores else None,
+             probs=_empty((p.N, p.T), f32, dev),
+             expert_tokens=_empty((p.N, C), i32, dev), expert_gates=_empty((p.N, C), f32, dev),
+             row_of=_empty((p.T, p.N), i32, dev), gate_of=_empty((p.T, p.N), f32, dev),
+             offsets=_empty((p.N + 1,), i32, dev), mean_prob=_empty((p.N,), f32, dev),
+             lse_sq=_empty((p.T,), f32, dev))
+    ws = ec_workspace(p, dev) if ws is None else ws
+    _call("moe_ec_route", ctypes.byref(p), _ptr(u), _ptr(w_router), _ptr(b_router), _ptr(noise),
+          _ptr(o["scores"]), _ptr(o["probs"]), _ptr(o["expert_tokens"]), _ptr(o["expert_gates"]),
+          _ptr(o["row_of"]), _ptr(o["gate_of"]), _ptr(o["offsets"]), _ptr(o["mean_prob"]),
+          _ptr(o["lse_sq"]), _ptr(ws), ws.numel(), _stream(dev))
+    return o
+
+
+def moe_ec_dispatch(p: MoeProblem, u, expert_tokens) -> torch.Tensor:
+    dev = u.device
+    et = TORCH_DTYPE[p.dtype]
+    C = moe_ec_capacity(p.T, p.K, p.N, p.capacity_factor)
+    _check(u, "u", (p.T, p.d), et, dev)
+    _check(expert_tokens, "expert_tokens", (p.N, C), torch.int32, dev)
+    x_perm = _empty((p.N * C, p.d), et, dev)
+    _call("moe_ec_dispatch", ctypes.byref(p), _ptr(u), _ptr(expert_tokens), _ptr(x_perm),
+          _stream(dev))
+    return x_perm
+
+
+def moe_ec_combine(p: MoeProblem, u, y_perm, row_of, gate_of, y_shared=None) -> torch.Tensor:
+    dev = u.device
+    et = TORCH_DTYPE[p.dtype]
+    C = moe_ec_capacity(p.T, p.K, p.N, p.capacity_factor)
+    _check(u, "u", (p.T, p.d), et, dev)
+    _check(y_perm, "y_perm", (p.N * C, p.d), et, dev)
+    _check(row_of, "row_of", (p.T, p.N), torch.int32, dev)
+    _check(gate_of, "gate_of", (p.T, p.N), torch.float32, dev)
+    _check(y_shared, "y_shared", (p.T, p.d), et, dev, optional=p.n_shared == 0)
+    out = _empty((p.T, p.d), et, dev)
+    _call("moe_ec_combine", ctypes.byref(p), _ptr(u), _ptr(y_perm), _ptr(row_of), _ptr(gate_of),
+          _ptr(y_shared), _ptr(out), _stream(dev))
+    return out
+
+
+class EcBuffers:
+    """Preallocated outputs and intermediates of moe_ec_layer_forward."""
+
+    def __init__(self, p: MoeProblem, device, want_scores=True):
+        et = TORCH_DTYPE[p.dtype]
+        C = moe_ec_capacity(p.T, p.K, p.N, p.capacity_factor)
+        e = lambda shape, dt: _empty(shape, dt, device)
+        f32, i32 = torch.float32, torch.int32
+        self.C = C
+        self.t = dict(
+            scores=e((p.T, p.N), f32) if want_scores else None, probs=e((p.N, p.T), f32),
+            expert_tokens=e((p.N, C), i32), expert_gates=e((p.N, C), f32),
+            row_of=e((p.T, p.N), i32), gate_of=e((p.T, p.N), f32), offsets=e((p.N + 1,), i32),
+            mean_prob=e((p.N,), f32), lse_sq=e((p.T,), f32),
+            x_perm=e((p.N * C, p.d), et), y_perm=e((p.N * C, p.d), et),
+            y_shared=e((p.T, p.d), et) if p.n_shared > 0 else None,
+            out=e((p.T, p.d), et))
+        self.c = MoeEcOutputs(*[None if self.t[n] is None else self.t[n].data_ptr()
+                                for n, _ in MoeEcOutputs._fields_])
+
+
+def moe_ec_layer_forward(p: MoeProblem, u, noise, weights: MoeWeights, bufs: EcBuffers,
+                         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The chained expert-choice pass into preallocated buffers; returns
+    bufs.t['out'].  The tensors behind `weights` must stay alive while the work runs."""
+    dev = u.device
+    _check(u, "u", (p.T, p.d), TORCH_DTYPE[p.dtype], dev)
+    _check(noise, "noise", (p.T, p.N), torch.float32, dev, optional=True)
+    ws = ec_workspace(p, dev) if ws is None else ws
+    _call("moe_ec_layer_forward", ctypes.byref(p), _ptr(u), _ptr(noise), ctypes.byref(weights),
+          ctypes.byref(bufs.c), _ptr(bufs.t["out"]), _ptr(ws), ws.numel(), _stream(dev))
+    return bufs.t["out"]
+
+
+def ec_layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], want_scores=True) -> Dict[str, torch.Tensor]:
+    """Convenience: allocate buffers and run the expert-choice pass on
+    workload tensors x (keys as produced by workloads.generate, on the GPU)."""
+    w = make_weights(p, x["w_router"], x.get("b_router"), x["w_gate"], x.get("w_up"), x["w_down"],
+                     x.get("ws_gate"), x.get("ws_up"), x.get("ws_down"))
+    bufs = EcBuffers(p, u.device, want_scores)
+    moe_ec_layer_forward(p, u, x.get("noise"), w, bufs)
     return bufs.t

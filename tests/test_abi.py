@@ -169,3 +169,68 @@ def test_router_stats_argument_checks():
     assert L.moe_router_stats(P, ctypes.c_void_p(FAKE + 2), f(1), f(2), f(3), None) == M.MOE_ERR_INVALID_ARG
     assert L.moe_router_stats(ctypes.byref(good(N=300)), f(0), f(1), f(2), f(3), None) == M.MOE_ERR_UNSUPPORTED
     assert L.moe_router_stats(ctypes.byref(good(T=0)), None, None, None, None, None) == M.MOE_OK
+
+
+# ------------------------------------------------------------ expert choice
+
+def test_ec_capacity_agrees_with_oracle():
+    rng = np.random.default_rng(12)
+    assert M.moe_ec_capacity(8192, 2, 8, 0.0) == 2048      # cf <= 0 read as 1
+    assert M.moe_ec_capacity(10, 1, 1, 4.0) == 10          # capped at T
+    assert M.moe_ec_capacity(0, 2, 8, 1.0) == 0
+    assert M.moe_ec_capacity(10, 1, 0, 1.0) == -1
+    for _ in range(3000):
+        T, N = int(rng.integers(0, 50000)), int(rng.integers(1, 257))
+        K = int(rng.integers(1, min(N, 16) + 1))
+        cf = float(np.float32(rng.choice([rng.uniform(-1.0, 8.0), rng.integers(0, 5) * 0.25])))
+        assert M.moe_ec_capacity(T, K, N, cf) == O.ec_capacity(T, K, N, cf), (T, K, N, cf)
+
+
+def test_ec_workspace_size():
+    assert M.moe_ec_workspace_size(good(T=0)) == 0
+    assert M.moe_ec_workspace_size(good(K=9)) == 0
+    a = M.moe_ec_workspace_size(good(T=1000))
+    # the gated activations dominate: N*C*d_ff elements, C = T*K/N here
+    assert a >= 1000 * 2 * 192 * 2 and a % 256 == 0
+    b = M.moe_ec_workspace_size(good(T=1000, capacity_factor=3.0))
+    assert b >= 3 * 1000 * 2 * 192 * 2 > a
+
+
+def ec_route_call(p, ws_bytes=0, **ptr):
+    names = ("u", "w_router", "b_router", "noise", "scores", "probs", "expert_tokens",
+             "expert_gates", "row_of", "gate_of", "offsets", "mean_prob", "lse_sq")
+    args = {n: fake(i + 1) for i, n in enumerate(names)}
+    args.update(b_router=None, noise=None)
+    args.update(ptr)
+    return M.lib().moe_ec_route(ctypes.byref(p), *[args[n] for n in names], fake(30), ws_bytes,
+                                None)
+
+
+def test_ec_entry_points_check_before_launch():
+    L = M.lib()
+    p = good(n_shared=1, d_ff_shared=128)
+    P = ctypes.byref(p)
+    f = fake
+    for over, status in ((dict(K=0), M.MOE_ERR_INVALID_ARG), (dict(N=300), M.MOE_ERR_UNSUPPORTED),
+                         (dict(d=96), M.MOE_ERR_UNSUPPORTED)):
+        assert ec_route_call(good(**over), 1 << 40) == status
+    assert ec_route_call(p, 1 << 40, probs=None) == M.MOE_ERR_INVALID_ARG
+    assert ec_route_call(p, 1 << 40, row_of=None) == M.MOE_ERR_INVALID_ARG
+    assert ec_route_call(p, 1 << 40, u=ctypes.c_void_p(FAKE + 8)) == M.MOE_ERR_INVALID_ARG
+    assert ec_route_call(good(noise_weight=float("nan")), 1 << 40, noise=f(9)) == M.MOE_ERR_INVALID_ARG
+    assert ec_route_call(p) == M.MOE_ERR_WORKSPACE
+    assert ec_route_call(p, 64) == M.MOE_ERR_WORKSPACE
+    assert ec_route_call(good(T=0), 0, u=None, probs=None) == M.MOE_OK
+    # dispatch / combine: pointers
+    assert L.moe_ec_dispatch(P, f(1), None, f(3), None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_ec_dispatch(P, f(1), f(2), None, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_ec_combine(P, f(1), f(2), f(3), f(4), None, f(6), None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_ec_combine(P, f(1), f(2), None, f(4), f(5), f(6), None) == M.MOE_ERR_INVALID_ARG
+    # layer: null structs, then a short workspace, then a missing output
+    assert L.moe_ec_layer_forward(P, f(1), None, None, None, f(2), f(3), 1 << 40, None) == M.MOE_ERR_INVALID_ARG
+    w = M.MoeWeights(*[FAKE + 4096 * i for i in range(8)])
+    o = M.MoeEcOutputs(*[FAKE + 4096 * (20 + i) for i in range(12)])
+    need = M.moe_ec_workspace_size(p)
+    assert L.moe_ec_layer_forward(P, f(1), None, ctypes.byref(w), ctypes.byref(o), f(2), f(3), need - 256, None) == M.MOE_ERR_WORKSPACE
+    o.y_shared = None
+    assert L.moe_ec_layer_forward(P, f(1), None, ctypes.byref(w), ctypes.byref(o), f(2), f(3), need, None) == M.MOE_ERR_INVALID_ARG
