@@ -9,7 +9,9 @@ fp32 router), seeded synthetic inputs.
 Prints one JSON line: tokens/s of the whole pass, the roofline of the
 dominant stage (the grouped expert GEMMs, live HIP-event timing on the
 launch stream), per-stage times, and the CPU oracle timed on a bounded
-sample of the same workload on the host cores.
+sample of the same workload on the host cores.  The expert-choice pass
+(moe_ec_layer_forward, experts selecting their tokens) is timed after it on
+the same batch and weights and reported beside the token-choice line.
 """
 import argparse
 import ctypes
@@ -62,6 +64,8 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-expert-choice", action="store_true",
+                    help="skip the expert-choice pass timed after the token-choice one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device three times (a transfer of "
                          "known size, to scale HBM byte counters)")
@@ -163,6 +167,47 @@ def main():
         stages_ms[name] = e0.elapsed_time(e1) / n
     log("stages (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_ms.items()))
 
+    # ---- expert-choice pass on the same workload (same inputs and weights)
+    ec = None
+    if not args.no_expert_choice:
+        ecb = M.EcBuffers(p, dev, want_scores=False)
+        ecws = M.ec_workspace(p, dev)
+        et = ecb.t
+        ec_calls = {
+            "layer": ("moe_ec_layer_forward", (P, vp(xg["u"]), vp(xg["noise"]), ctypes.byref(weights),
+                                               ctypes.byref(ecb.c), vp(et["out"]), vp(ecws),
+                                               ecws.numel(), sp)),
+            "route": ("moe_ec_route", (P, vp(xg["u"]), vp(xg["w_router"]), vp(xg["b_router"]),
+                                       vp(xg["noise"]), None, vp(et["probs"]), vp(et["expert_tokens"]),
+                                       vp(et["expert_gates"]), vp(et["row_of"]), vp(et["gate_of"]),
+                                       vp(et["offsets"]), vp(et["mean_prob"]), vp(et["lse_sq"]),
+                                       vp(ecws), ecws.numel(), sp)),
+            "dispatch": ("moe_ec_dispatch", (P, vp(xg["u"]), vp(et["expert_tokens"]), vp(et["x_perm"]), sp)),
+            "combine": ("moe_ec_combine", (P, vp(xg["u"]), vp(et["y_perm"]), vp(et["row_of"]),
+                                           vp(et["gate_of"]), vp(et["y_shared"]), vp(et["out"]), sp)),
+        }
+        ec_ms = {}
+        for name, (fn, a) in ec_calls.items():
+            f = getattr(L, fn)
+            for _ in range(2):
+                f(*a)
+            n = max(args.steps, 10)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                st = f(*a)
+                if st != 0:
+                    raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ec_ms[name] = e0.elapsed_time(e1) / n
+        log("expert choice (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in ec_ms.items()))
+        ec = {"capacity": ecb.C, "ms_per_step": round(ec_ms["layer"], 4),
+              "tokens_per_s": round(w.T / (ec_ms["layer"] * 1e-3), 1),
+              "stages_ms": {k: round(v, 4) for k, v in ec_ms.items() if k != "layer"},
+              "note": "moe_ec_layer_forward on the same batch and weights, HIP-event time per pass"}
+        del ecb, ecws
+
     # ---- roofline of the grouped expert GEMMs (algorithmic flops per call)
     mults = 3 if w.act == "swiglu" else 2
     flops = 2.0 * R * w.d * w.d_ff * mults
@@ -232,6 +277,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},
         "hbm_frac": hbm,
         "cpu_baseline": cpu,
+        "expert_choice": ec,
     }
     print(json.dumps(line), flush=True)
 
