@@ -30,6 +30,7 @@ struct GemmArgs {
   const int32_t* tiles;     // [G+1] prefix of full-height row tiles per group
   const int32_t* tails;     // [G+1] prefix of short tail tiles per group
   int tail_rows;            // tallest tail tile (0: no tail tiles)
+  int ext_rows;             // rows a group's last full tile may run past its height
   int G;
   int M;                    // rows of the single group when offsets == null
   int rows_alloc;           // rows addressable through A (loads are clamped)
@@ -51,14 +52,19 @@ __device__ __forceinline__ float epilogue(float g, float up) {
 }
 
 // Row tiles of a group of n rows: full-height tiles (the last may be partly
-// filled), plus one short tail tile when the remainder is at most tail_rows
-// rows, so that a group a few rows past a multiple of the tile height does
-// not cost a whole extra full-height tile.
-__host__ __device__ inline void split_rows(int n, int BM, int tail_rows, int& full, int& tail) {
-  const int rem = n % BM;
-  const bool t = tail_rows > 0 && rem > 0 && rem <= tail_rows;
-  full = n / BM + (rem > 0 && !t ? 1 : 0);
-  tail = t ? 1 : 0;
+// filled).  A group a few rows past a multiple of the tile height does not
+// pay for a whole extra tile: when it has a full tile and the remainder is at
+// most ext_rows rows, its last full tile is extended by the remainder (one
+// taller tile that reuses the same weight panels); a group shorter than one
+// tile with at most tail_rows rows gets one short tail tile instead.
+__host__ __device__ inline void split_rows(int n, int BM, int tail_rows, int ext_rows, int& full,
+                                           int& tail) {
+  const int q = n / BM, rem = n % BM;
+  full = q;
+  tail = 0;
+  if (rem == 0 || (q > 0 && rem <= ext_rows)) return;
+  if (tail_rows > 0 && rem <= tail_rows) tail = 1;
+  else full = q + 1;
 }
 
 // Locate the row block: returns false when the block has no work.
@@ -89,10 +95,10 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int
 constexpr int kPatchN = 4;   // n-tiles per patch: an XCD works on m-tiles x 4 n-tiles of one group
 
 // Full-height tiles of all groups (single-group form: from M).
-__device__ __forceinline__ int full_tiles_total(const GemmArgs& a, int BM) {
+__host__ __device__ inline int full_tiles_total(const GemmArgs& a, int BM) {
   if (a.offsets != nullptr) return a.tiles[a.G];
   int f, t;
-  split_rows(a.M, BM, a.tail_rows, f, t);
+  split_rows(a.M, BM, a.tail_rows, a.ext_rows, f, t);
   return f;
 }
 
@@ -102,8 +108,9 @@ __device__ __forceinline__ int full_tiles_total(const GemmArgs& a, int BM) {
 // remapped so that each XCD owns a contiguous run of logical tiles, and
 // logical tiles walk each group in patches of (all its row tiles) x kPatchN
 // n-tiles, so the activation and weight panels of a patch are fetched into
-// one L2 once and shared by the blocks of the patch.
-__device__ __forceinline__ void find_tile_2d(const GemmArgs& a, int BM, int ntiles, int h, int real,
+// one L2 once and shared by the blocks of the patch.  rows is at most BM,
+// except for a group's last tile, which may run up to ext_rows further.
+__host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntiles, int h, int real,
                                              int& g, int& row0, int& rows, int& nt) {
   int mt_g, base;
   const int full = real - real % 8;
@@ -132,12 +139,12 @@ __device__ __forceinline__ void find_tile_2d(const GemmArgs& a, int BM, int ntil
   row0 = (a.offsets == nullptr ? 0 : a.offsets[g]) + mt * BM;
   const int end = a.offsets == nullptr ? a.M : a.offsets[g + 1];
   rows = end - row0;
-  if (rows > BM) rows = BM;
+  if (mt < mt_g - 1 && rows > BM) rows = BM;
 }
 
 // Tail tile h (counted from the first tail block): n-tile fastest.  Returns
 // false past the last tail tile.
-__device__ __forceinline__ bool find_tail(const GemmArgs& a, int BM, int ntiles, int h, int& g,
+__host__ __device__ inline bool find_tail(const GemmArgs& a, int BM, int ntiles, int h, int& g,
                                           int& row0, int& rows, int& nt) {
   if (a.tail_rows == 0) return false;
   const int ti = h / ntiles;
@@ -145,7 +152,7 @@ __device__ __forceinline__ bool find_tail(const GemmArgs& a, int BM, int ntiles,
   int full, end;
   if (a.offsets == nullptr) {
     int t;
-    split_rows(a.M, BM, a.tail_rows, full, t);
+    split_rows(a.M, BM, a.tail_rows, a.ext_rows, full, t);
     if (ti >= t) return false;
     g = 0;
     row0 = full * BM;
@@ -363,13 +370,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   }
 }
 
-// Groups of many rows: 256x256 tiles on 8 waves (128x64 each), and 64-row
-// tail tiles (32x64 per wave) for groups a few rows past a multiple of 256.
+// Groups of many rows: 256x256 tiles on 8 waves (128x64 each).  A group's
+// last tile grows to 320 rows (160x64 per wave) when the group ends at most
+// 64 rows past a multiple of 256, and groups of at most 64 rows get a 64-row
+// tail tile (32x64 per wave).
 constexpr int kTailRows = 64;
+constexpr int kExtRows = 64;
 
 template <int EPI>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
-  __shared__ u32x4 sA[2][256 * 8];
+  __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
   __shared__ u32x4 sB[2][256 * 8];
   constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
   const int ntiles = (a.Ndim + BNH - 1) / BNH;
@@ -378,7 +388,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
   int g, row0, rows, by;
   if (h < real) {
     find_tile_2d(a, 256, ntiles, h, real, g, row0, rows, by);
-    gemm_tile<EPI, 256, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
+    if (rows > 256) gemm_tile<EPI, 256 + kExtRows, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
+    else gemm_tile<EPI, 256, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
   } else if (find_tail(a, 256, ntiles, h - real, g, row0, rows, by)) {
     gemm_tile<EPI, kTailRows, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
   }
@@ -428,12 +439,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs a, int B
 // Prefix sums over the groups of their full-height and tail row tiles
 // (split_rows), one block: tiles[g], tails[g] for g = 0..G.
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, int G, int BMr,
-                                                        int tail_rows, int32_t* tiles,
-                                                        int32_t* tails) {
+                                                        int tail_rows, int ext_rows,
+                                                        int32_t* tiles, int32_t* tails) {
   __shared__ int32_t s[256], t[256];
   const int g = threadIdx.x;
   int f = 0, tl = 0;
-  if (g < G) split_rows(offsets[g + 1] - offsets[g], BMr, tail_rows, f, tl);
+  if (g < G) split_rows(offsets[g + 1] - offsets[g], BMr, tail_rows, ext_rows, f, tl);
   s[g] = f;
   t[g] = tl;
   __syncthreads();
@@ -510,12 +521,13 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   // group (all groups share one tile height so the plan is one prefix sum)
   const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : 128;
   const int tail_rows = bf16 && bm == 256 ? kTailRows : 0;
+  const int ext_rows = bf16 && bm == 256 ? kExtRows : 0;
   // grid bound: at most rows/bm + 1 full tiles and one tail tile per group
   const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N + (tail_rows > 0 ? p.N : 0);
   int32_t* tails = tiles + (p.N + 2);
 
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, offsets, p.N, bm, tail_rows,
-                     tiles, tails);
+                     ext_rows, tiles, tails);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -529,6 +541,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g1.tiles = tiles;
   g1.tails = tails;
   g1.tail_rows = tail_rows;
+  g1.ext_rows = ext_rows;
   g1.G = p.N;
   g1.rows_alloc = rows_alloc;
   g1.Ndim = p.d_ff;
@@ -562,10 +575,11 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     const int ws_w = p.n_shared * p.d_ff_shared;
     const int sbm = bf16 ? pick_tiles(p.T).bm : 128;
     const int s_tail = bf16 && sbm == 256 ? kTailRows : 0;
+    const int s_ext = bf16 && sbm == 256 ? kExtRows : 0;
     int mt = (p.T + sbm - 1) / sbm;
     if (s_tail > 0) {
       int f, t;
-      split_rows(p.T, sbm, s_tail, f, t);
+      split_rows(p.T, sbm, s_tail, s_ext, f, t);
       mt = f + t;
     }
     GemmArgs s1{};
@@ -577,6 +591,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     s1.tiles = nullptr;
     s1.tails = nullptr;
     s1.tail_rows = s_tail;
+    s1.ext_rows = s_ext;
     s1.G = 1;
     s1.M = p.T;
     s1.rows_alloc = p.T;

@@ -223,11 +223,14 @@ def test_grouped_ffn_ragged(T, N, K, d, dff, act, shared):
 
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
 def test_grouped_ffn_group_sizes_around_tile_multiples(act):
-    """Groups of 0, 1, 255, 257, 300, 320, 321 and 600 rows (256-row tiles
-    with short tails for remainders of at most 64 rows) and a shared expert
-    over 1050 tokens (4 full tiles and a 26-row tail): every row checked."""
-    sizes = [257, 320, 321, 300, 0, 255, 1, 600]
-    T, K, d, dff = 1050, 2, 128, 192
+    """Groups of 0 .. 600 rows around multiples of the 256-row tile: a last
+    tile extended by 1, 44, 64 rows (257, 300, 320, 576), not extended (321,
+    600: a partly filled third tile), exact multiples (512), short groups
+    with a 64-row tail tile (1, 64) or one partly filled tile (65, 255), and
+    a shared expert over 1050 tokens (its fourth tile extended by 26 rows):
+    every row checked."""
+    sizes = [257, 320, 321, 300, 0, 255, 1, 600, 64, 65, 576, 512]
+    T, K, d, dff = 1050, 4, 128, 192
     w = W.Workload("tails", T=T, d=d, N=len(sizes), K=K, d_ff=dff, act=act, n_shared=1,
                    d_ff_shared=128, seed=77, dtype="bf16")
     x = W.generate(w)
