@@ -98,19 +98,76 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* blk_c
 // bits as dispatch_count_kernel's), computes the rows of its tokens, writes
 // row_of and token_of_row, then copies each token row (read once, 16-byte
 // vectors) to every kept row.
+//
+// SCAN: when all chunk counts fit in LDS (chunks x N <= kScanInBlock), every
+// block runs the scan itself on the chunk counts -- the per-expert running
+// sums over the chunks before its own, the capacity and the expert offsets
+// (the same fixed-order integer sums as dispatch_scan_kernel) -- and block 0
+// writes expert_counts, kept_counts and offsets.  That saves a launch of the
+// one-block scan kernel, whose cost is mostly launch latency.  Otherwise the
+// scan kernel has written blk_base and offsets.
 constexpr int kRowTok = 16;                 // tokens per block
 constexpr int kVecPerLane = 8;              // 16-byte vectors in flight per lane
+constexpr int kScanInBlock = 4096;          // chunk counts one block scans itself (16 KB)
 static_assert(kTok % kRowTok == 0, "blocks tile the mask chunks");
 
+template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
-    const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T, int N, int K,
+    const int32_t* topk_idx, const int32_t* blk_count, int chunks, const int32_t* blk_base,
+    int32_t* offsets, int32_t* expert_counts, int32_t* kept_counts, int T, int N, int K,
     int32_t capacity, int32_t* row_of, int32_t* token_of_row, const u32x4* u, u32x4* x_perm,
     int vec_per_row) {
   __shared__ uint32_t mask[256 * kWords];
   __shared__ int32_t srow[kRowTok * 16];
+  __shared__ int32_t s_cnt[SCAN ? kScanInBlock : 1];
+  __shared__ int32_t s_base[SCAN ? 256 : 1];
+  __shared__ int32_t s_off[SCAN ? 257 : 1];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kRowTok;           // first token of this block
   const int chunk = t0 / kTok;
+  if constexpr (SCAN) {
+    for (int i = tid; i < chunks * N; i += 256) s_cnt[i] = blk_count[i];
+    __syncthreads();
+    int kept = 0;
+    if (tid < N) {
+      int run = 0, mine = 0;
+      for (int c = 0; c < chunks; ++c) {
+        if (c == chunk) mine = run;
+        run += s_cnt[c * N + tid];
+      }
+      s_base[tid] = mine;
+      kept = (capacity >= 0 && run > capacity) ? capacity : run;
+      if (blockIdx.x == 0) {
+        expert_counts[tid] = run;
+        kept_counts[tid] = kept;
+      }
+    }
+    // inclusive scan of the kept counts over the experts (s_cnt is free now)
+    __syncthreads();
+    s_cnt[tid] = kept;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = tid >= o ? s_cnt[tid - o] : 0;
+      __syncthreads();
+      s_cnt[tid] += v;
+      __syncthreads();
+    }
+    if (tid < N) s_off[tid + 1] = s_cnt[tid];
+    if (tid == 0) s_off[0] = 0;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      if (tid < N) offsets[tid] = s_off[tid];
+      if (tid == 0) offsets[N] = s_off[N];      // N may be 256: past the last thread
+    }
+  }
+  auto base_of = [&](int e) -> int32_t {
+    if constexpr (SCAN) return s_base[e];
+    else return blk_base[(size_t)chunk * N + e];
+  };
+  auto off_of = [&](int e) -> int32_t {
+    if constexpr (SCAN) return s_off[e];
+    else return offsets[e];
+  };
   build_masks(mask, topk_idx, T, N, K, tid, chunk * kTok + tid);
   if (tid < kRowTok) {
     const int t = t0 + tid;
@@ -124,9 +181,9 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
         if (e >= 0 && e < N) {
           int r = __popc(mask[e * kWords + w0] & below);
           for (int w = 0; w < w0; ++w) r += __popc(mask[e * kWords + w]);
-          const int rank = blk_base[(size_t)chunk * N + e] + r;
+          const int rank = base_of(e) + r;
           if (capacity < 0 || rank < capacity) {
-            row = offsets[e] + rank;
+            row = off_of(e) + rank;
             token_of_row[row] = t;
           }
         }
@@ -138,7 +195,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   // rows past the kept total hold no token
   const int64_t total = (int64_t)T * K;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t r = offsets[N] + (int64_t)blockIdx.x * 256 + tid; r < total; r += stride)
+  for (int64_t r = off_of(N) + (int64_t)blockIdx.x * 256 + tid; r < total; r += stride)
     token_of_row[r] = -1;
   __syncthreads();
 
@@ -180,17 +237,26 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                      p.N, p.K, blk_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, (const int32_t*)blk_count,
-                     blk_base, disp_blocks, p.N, capacity, expert_counts, kept_counts, offsets);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool scan_in_block = (int64_t)disp_blocks * p.N <= kScanInBlock;
+  if (!scan_in_block) {
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, (const int32_t*)blk_count,
+                       blk_base, disp_blocks, p.N, capacity, expert_counts, kept_counts, offsets);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
   const int vec_per_row = (int)((size_t)p.d * es / 16);
   const unsigned blocks = (unsigned)((p.T + kRowTok - 1) / kRowTok);
-  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(blocks), dim3(256), 0, s, topk_idx,
-                     (const int32_t*)blk_base, (const int32_t*)offsets, p.T, p.N, p.K, capacity,
-                     row_of, token_of_row, static_cast<const u32x4*>(u),
-                     static_cast<u32x4*>(x_perm), vec_per_row);
+  if (scan_in_block)
+    hipLaunchKernelGGL(dispatch_permute_kernel<true>, dim3(blocks), dim3(256), 0, s, topk_idx,
+                       (const int32_t*)blk_count, disp_blocks, (const int32_t*)blk_base, offsets,
+                       expert_counts, kept_counts, p.T, p.N, p.K, capacity, row_of, token_of_row,
+                       static_cast<const u32x4*>(u), static_cast<u32x4*>(x_perm), vec_per_row);
+  else
+    hipLaunchKernelGGL(dispatch_permute_kernel<false>, dim3(blocks), dim3(256), 0, s, topk_idx,
+                       (const int32_t*)blk_count, disp_blocks, (const int32_t*)blk_base, offsets,
+                       expert_counts, kept_counts, p.T, p.N, p.K, capacity, row_of, token_of_row,
+                       static_cast<const u32x4*>(u), static_cast<u32x4*>(x_perm), vec_per_row);
   return hipGetLastError();
 }
 

@@ -140,8 +140,13 @@ def test_dispatch_full_size(name):
 
 @pytest.mark.parametrize("T,N,K,cf,skew", [(1, 1, 1, 0.0, 0.0), (3, 4, 2, 0.0, 0.0), (300, 7, 3, 0.0, 2.0),
                                            (1000, 16, 2, 0.05, 0.0), (777, 256, 16, 0.0, 1.2),
-                                           (2049, 8, 1, 1.25, 3.0), (513, 64, 6, 0.7, 0.5)])
+                                           (2049, 8, 1, 1.25, 3.0), (513, 64, 6, 0.7, 0.5),
+                                           (16384, 64, 6, 1.1, 1.0), (16385, 64, 6, 1.1, 1.0),
+                                           (5000, 256, 8, 0.0, 0.5)])
 def test_dispatch_edges(T, N, K, cf, skew):
+    """Edge shapes; the last three put 4096 chunk counts (scanned inside the
+    row-copy blocks) and 4160 / 5120 (scanned by the one-block scan kernel)
+    behind the ranks."""
     ref = _dispatch_case(T, N, K, 64, "bf16", cf, 17 + T, skew)
     if cf > 0:
         assert (ref["expert_counts"] - ref["kept_counts"]).sum() > 0   # drops happen
