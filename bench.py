@@ -167,6 +167,53 @@ def main():
         stages_ms[name] = e0.elapsed_time(e1) / n
     log("stages (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_ms.items()))
 
+    # ---- the same stages with cold caches: a 1 GiB buffer is read before
+    # each timed call, evicting the 256 MB Infinity Cache and the L2s (read,
+    # not written: a written buffer would leave up to 256 MB of dirty lines
+    # whose write-back lands inside the timed call); the median of the
+    # per-call event times
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    stages_cold_ms = {}
+    for name, (fn, a) in stage_args.items():
+        f = getattr(L, fn)
+        n = max(args.steps, 10)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for b, e in ev:
+            flush.sum()
+            b.record(stream)
+            st = f(*a)
+            e.record(stream)
+            if st != 0:
+                raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
+        torch.cuda.synchronize()
+        stages_cold_ms[name] = float(np.median([b.elapsed_time(e) for b, e in ev]))
+    # attainable HBM reference: a device-to-device copy of 128 MiB (256 MiB
+    # moved, the size of the combine stage's traffic), warm and cold as above
+    src = torch.ones(1 << 25, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    n = max(args.steps, 10)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_warm_ms = e0.elapsed_time(e1) / n
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for b, e in ev:
+        flush.sum()
+        b.record(stream)
+        dst.copy_(src)
+        e.record(stream)
+    torch.cuda.synchronize()
+    copy_cold_ms = float(np.median([b.elapsed_time(e) for b, e in ev]))
+    copy_bytes = 2 * src.numel() * 4
+    del flush, src, dst
+    log("stages, cold caches (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_cold_ms.items()))
+    log(f"copy of 128 MiB: warm {copy_warm_ms:.4f} ms, cold {copy_cold_ms:.4f} ms")
+
     # ---- expert-choice pass on the same workload (same inputs and weights)
     ec = None
     if not args.no_expert_choice:
@@ -228,6 +275,8 @@ def main():
         + (w.T * w.d * es if w.n_shared else 0)
     hbm = {k: round(b / (stages_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
            for k, b in (("route", route_bytes), ("dispatch", disp_bytes), ("combine", comb_bytes))}
+    hbm_cold = {k: round(b / (stages_cold_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                for k, b in (("route", route_bytes), ("dispatch", disp_bytes), ("combine", comb_bytes))}
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -276,6 +325,13 @@ def main():
         "grouped_gemm_pct_bf16_peak": round(100 * roofline["frac"], 2),
         "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},
         "hbm_frac": hbm,
+        "stages_ms_cold": {k: round(v, 4) for k, v in stages_cold_ms.items()},
+        "hbm_frac_cold": hbm_cold,
+        "copy_reference": {"bytes": copy_bytes,
+                           "warm_frac": round(copy_bytes / (copy_warm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "cold_frac": round(copy_bytes / (copy_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "note": "device-to-device copy of 128 MiB, the attainable HBM fraction "
+                                   "for a transfer of the combine stage's size"},
         "cpu_baseline": cpu,
         "expert_choice": ec,
     }

@@ -15,8 +15,6 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxK = 16;
-
 __device__ __forceinline__ void unpack8(const u32x4& q, float* f) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -34,6 +32,23 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+__device__ __forceinline__ void unpack(const u32x4& q, float* f, bool bf16) {
+  if (bf16) {
+    unpack8(q, f);
+  } else {
+    f[0] = __uint_as_float(q.x);
+    f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z);
+    f[3] = __uint_as_float(q.w);
+  }
+}
+
+// Each lane owns kChunk vectors of a row at a time and issues all their
+// loads of one source row (u, then each expert row, then the shared row)
+// before using any: 8 KB per wave in flight per source instead of 1 KB,
+// which is what keeps HBM busy when nothing is cached.
+constexpr int kChunk = 8;
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* u, const u32x4* y_perm,
                                                       const int32_t* row_of, const float* gate,
@@ -44,59 +59,59 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* u, const u32x
   const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
   for (int t = wave_id; t < T; t += nwaves) {
-    int rows[kMaxK];
-    float g[kMaxK];
+    const size_t tb = (size_t)t * vec_per_row;
+    for (int v0 = lane; v0 < vec_per_row; v0 += 64 * kChunk) {
+      float acc[kChunk][EV];
+      u32x4 q[kChunk];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
-      rows[k] = -1;
-      g[k] = 0.0f;
-      if (k < K) {
-        rows[k] = row_of[(size_t)t * K + k];
-        g[k] = gate[(size_t)t * K + k];
-      }
-    }
-    for (int v = lane; v < vec_per_row; v += 64) {
-      float acc[EV], tmp[EV];
-      const u32x4 qu = u[(size_t)t * vec_per_row + v];
-      if constexpr (BF16) unpack8(qu, acc);
-      else {
-        acc[0] = __uint_as_float(qu.x);
-        acc[1] = __uint_as_float(qu.y);
-        acc[2] = __uint_as_float(qu.z);
-        acc[3] = __uint_as_float(qu.w);
+      for (int c = 0; c < kChunk; ++c) {
+        const int v = v0 + 64 * c;
+        q[c] = v < vec_per_row ? u[tb + v] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int k = 0; k < kMaxK; ++k) {
-        if (k < K && rows[k] >= 0) {
-          const u32x4 qy = y_perm[(size_t)rows[k] * vec_per_row + v];
-          if constexpr (BF16) unpack8(qy, tmp);
-          else {
-            tmp[0] = __uint_as_float(qy.x);
-            tmp[1] = __uint_as_float(qy.y);
-            tmp[2] = __uint_as_float(qy.z);
-            tmp[3] = __uint_as_float(qy.w);
-          }
+      for (int c = 0; c < kChunk; ++c) unpack(q[c], acc[c], BF16);
+      for (int k = 0; k < K; ++k) {
+        const int row = row_of[(size_t)t * K + k];
+        if (row < 0) continue;
+        const float g = gate[(size_t)t * K + k];
+        const size_t rb = (size_t)row * vec_per_row;
 #pragma unroll
-          for (int i = 0; i < EV; ++i) acc[i] = fmaf(g[k], tmp[i], acc[i]);
+        for (int c = 0; c < kChunk; ++c) {
+          const int v = v0 + 64 * c;
+          q[c] = v < vec_per_row ? y_perm[rb + v] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+          float tmp[EV];
+          unpack(q[c], tmp, BF16);
+#pragma unroll
+          for (int i = 0; i < EV; ++i) acc[c][i] = fmaf(g, tmp[i], acc[c][i]);
         }
       }
       if (y_shared != nullptr) {
-        const u32x4 qs = y_shared[(size_t)t * vec_per_row + v];
-        if constexpr (BF16) unpack8(qs, tmp);
-        else {
-          tmp[0] = __uint_as_float(qs.x);
-          tmp[1] = __uint_as_float(qs.y);
-          tmp[2] = __uint_as_float(qs.z);
-          tmp[3] = __uint_as_float(qs.w);
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+          const int v = v0 + 64 * c;
+          q[c] = v < vec_per_row ? y_shared[tb + v] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < EV; ++i) acc[i] += tmp[i];
+        for (int c = 0; c < kChunk; ++c) {
+          float tmp[EV];
+          unpack(q[c], tmp, BF16);
+#pragma unroll
+          for (int i = 0; i < EV; ++i) acc[c][i] += tmp[i];
+        }
       }
-      u32x4 o;
-      if constexpr (BF16) o = pack8(acc);
-      else o = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                     __float_as_uint(acc[3])};
-      out[(size_t)t * vec_per_row + v] = o;
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int v = v0 + 64 * c;
+        if (v >= vec_per_row) continue;
+        if constexpr (BF16)
+          out[tb + v] = pack8(acc[c]);
+        else
+          out[tb + v] = u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
+                              __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])};
+      }
     }
   }
 }

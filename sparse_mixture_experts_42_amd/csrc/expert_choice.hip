@@ -145,16 +145,26 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(
   }
 }
 
-// x_perm[r] = u[expert_tokens[r]]: one wave per row, 16-byte vectors
+// x_perm[r] = u[expert_tokens[r]]: one wave per row, 16-byte vectors, eight
+// per lane loaded before any is stored
 __global__ __launch_bounds__(256) void ec_gather_kernel(const u32x4* u, const int32_t* tokens,
                                                         u32x4* x_perm, int rows,
                                                         int vec_per_row) {
+  constexpr int CH = 8;
   const int lane = threadIdx.x & 63;
   const int nw = gridDim.x * 4;
   for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += nw) {
     const u32x4* src = u + (size_t)tokens[r] * vec_per_row;
     u32x4* dst = x_perm + (size_t)r * vec_per_row;
-    for (int v = lane; v < vec_per_row; v += 64) dst[v] = src[v];
+    for (int v0 = lane; v0 < vec_per_row; v0 += 64 * CH) {
+      u32x4 q[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (v0 + 64 * c < vec_per_row) q[c] = src[v0 + 64 * c];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (v0 + 64 * c < vec_per_row) dst[v0 + 64 * c] = q[c];
+    }
   }
 }
 
@@ -176,6 +186,8 @@ __device__ __forceinline__ void unpack(const u32x4& q, float* f, bool bf16) {
 // ascending expert order, into an LDS list of (row, gate); the token's
 // vectors then accumulate in fp32 in the order u, list, shared, and are
 // rounded once.
+constexpr int kChunk = 8;    // 16-byte vectors per lane in flight
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void ec_combine_kernel(const u32x4* u, const u32x4* y_perm,
                                                          const int32_t* row_of,
@@ -202,32 +214,67 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const u32x4* u, const u
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    for (int v = lane; v < vec_per_row; v += 64) {
-      float acc[EV], tmp[EV];
-      unpack(u[(size_t)t * vec_per_row + v], acc, BF16);
+    // each lane issues the loads of kChunk vectors of one source row before
+    // using any of them (8 KB per wave in flight per source row)
+    const size_t tb = (size_t)t * vec_per_row;
+    for (int v0 = lane; v0 < vec_per_row; v0 += 64 * kChunk) {
+      float acc[kChunk][EV];
+      u32x4 q[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int v = v0 + 64 * c;
+        q[c] = v < vec_per_row ? u[tb + v] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) unpack(q[c], acc[c], BF16);
       for (int j = 0; j < n; ++j) {
-        unpack(y_perm[(size_t)lrow[wv][j] * vec_per_row + v], tmp, BF16);
+        const size_t rb = (size_t)lrow[wv][j] * vec_per_row;
         const float g = lgate[wv][j];
 #pragma unroll
-        for (int q = 0; q < EV; ++q) acc[q] = fmaf(g, tmp[q], acc[q]);
+        for (int c = 0; c < kChunk; ++c) {
+          const int v = v0 + 64 * c;
+          q[c] = v < vec_per_row ? y_perm[rb + v] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+          float tmp[EV];
+          unpack(q[c], tmp, BF16);
+#pragma unroll
+          for (int i = 0; i < EV; ++i) acc[c][i] = fmaf(g, tmp[i], acc[c][i]);
+        }
       }
       if (y_shared != nullptr) {
-        unpack(y_shared[(size_t)t * vec_per_row + v], tmp, BF16);
 #pragma unroll
-        for (int q = 0; q < EV; ++q) acc[q] += tmp[q];
-      }
-      u32x4 o;
-      if constexpr (BF16) {
-        uint32_t w[4];
+        for (int c = 0; c < kChunk; ++c) {
+          const int v = v0 + 64 * c;
+          q[c] = v < vec_per_row ? y_shared[tb + v] : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          w[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
-        o = u32x4{w[0], w[1], w[2], w[3]};
-      } else {
-        o = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                  __float_as_uint(acc[3])};
+        for (int c = 0; c < kChunk; ++c) {
+          float tmp[EV];
+          unpack(q[c], tmp, BF16);
+#pragma unroll
+          for (int i = 0; i < EV; ++i) acc[c][i] += tmp[i];
+        }
       }
-      out[(size_t)t * vec_per_row + v] = o;
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int v = v0 + 64 * c;
+        if (v >= vec_per_row) continue;
+        u32x4 o;
+        if constexpr (BF16) {
+          uint32_t w[4];
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2)
+            w[q2] = (uint32_t)f32_to_bf16(acc[c][2 * q2]) |
+                    ((uint32_t)f32_to_bf16(acc[c][2 * q2 + 1]) << 16);
+          o = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+          o = u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
+                    __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])};
+        }
+        out[tb + v] = o;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
