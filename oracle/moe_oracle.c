@@ -535,3 +535,310 @@ void oracle_ec_select(const oracle_problem* p, const double* probs, int32_t C,
   free(keys);
   free(sel);
 }
+
+/* ------------------------------------------------------------------ */
+/* backward pass: the chain rule through the forward definitions above  */
+/* (combine, gating, router, expert FFNs), one token or row at a time.   */
+/* The pages give the forward pass; its gradient is the plain calculus   */
+/* of those definitions with the routing held fixed.                     */
+/* ------------------------------------------------------------------ */
+
+void oracle_combine_backward(const oracle_problem* p, const double* d_out, const void* y,
+                             const int32_t* row_of, const double* gate, double* dy,
+                             double* d_gate) {
+  const int d = p->d, K = p->K;
+  for (int t = 0; t < p->T; ++t) {
+    const double* o = d_out + (size_t)t * d;
+    for (int k = 0; k < K; ++k) {
+      const int32_t row = row_of[(size_t)t * K + k];
+      double acc = 0.0;
+      if (row >= 0) {
+        const double g = gate[(size_t)t * K + k];
+        for (int j = 0; j < d; ++j) {
+          dy[(size_t)row * d + j] = g * o[j];
+          acc += o[j] * load_elem(y, p->dtype, (size_t)row * d + j);
+        }
+      }
+      d_gate[(size_t)t * K + k] = acc;
+    }
+  }
+}
+
+/* dH for one token */
+static void gate_jacobian_row(const oracle_problem* p, const float* h, const int32_t* idx,
+                              const double* gate, const double* dg, double* dH) {
+  const int N = p->N, K = p->K;
+  double gdg = 0.0;
+  for (int k = 0; k < K; ++k) gdg += gate[k] * dg[k];
+  for (int i = 0; i < N; ++i) dH[i] = 0.0;
+  if (p->gating == OR_GATE_SOFTMAX_TOPK) {
+    /* g_k = s_{e_k}: ds_i/dH_l = s_i (delta_il - s_l) */
+    double m = (double)h[0];
+    for (int i = 1; i < N; ++i)
+      if ((double)h[i] > m) m = (double)h[i];
+    double Z = 0.0;
+    for (int i = 0; i < N; ++i) Z += exp((double)h[i] - m);
+    for (int i = 0; i < N; ++i) {
+      double delta = 0.0;
+      for (int k = 0; k < K; ++k)
+        if (idx[k] == i) delta = dg[k];
+      const double s = exp((double)h[i] - m) / Z;
+      dH[i] = s * (delta - gdg);
+    }
+  } else {
+    /* g = softmax over the selected scores: dg_k/dH_{e_m} = g_k (delta_km - g_m) */
+    for (int k = 0; k < K; ++k) dH[idx[k]] = gate[k] * (dg[k] - gdg);
+  }
+}
+
+void oracle_route_backward(const oracle_problem* p, const float* H, const int32_t* topk_idx,
+                           const double* topk_gate, const double* d_gate, double* dH) {
+  const int N = p->N, K = p->K;
+  for (int t = 0; t < p->T; ++t)
+    gate_jacobian_row(p, H + (size_t)t * N, topk_idx + (size_t)t * K,
+                      topk_gate + (size_t)t * K, d_gate + (size_t)t * K, dH + (size_t)t * N);
+}
+
+typedef struct {
+  const oracle_problem* p; const oracle_inputs* in; const double* dH;
+  double* dw_router; double* du_router;
+} router_grad_ctx;
+
+/* dW_router rows i in [i0, i1) */
+static void router_dw_range(void* vctx, int i0, int i1) {
+  router_grad_ctx* c = (router_grad_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  for (int i = i0; i < i1; ++i)
+    for (int j = 0; j < p->d; ++j) {
+      double acc = 0.0;
+      for (int t = 0; t < p->T; ++t)
+        acc += c->dH[(size_t)t * p->N + i] * load_elem(c->in->u, p->dtype, (size_t)t * p->d + j);
+      c->dw_router[(size_t)i * p->d + j] = acc;
+    }
+}
+
+/* du_router rows t in [t0, t1) */
+static void router_du_range(void* vctx, int t0, int t1) {
+  router_grad_ctx* c = (router_grad_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  for (int t = t0; t < t1; ++t)
+    for (int j = 0; j < p->d; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < p->N; ++i)
+        acc += c->dH[(size_t)t * p->N + i] * (double)c->in->w_router[(size_t)i * p->d + j];
+      c->du_router[(size_t)t * p->d + j] = acc;
+    }
+}
+
+void oracle_router_param_grads(const oracle_problem* p, const oracle_inputs* in,
+                               const double* dH, double* dw_router, double* db_router,
+                               double* du_router, int nthreads) {
+  router_grad_ctx c = {p, in, dH, dw_router, du_router};
+  if (dw_router) parallel_for(p->N, nthreads, router_dw_range, &c);
+  if (db_router)
+    for (int i = 0; i < p->N; ++i) {
+      double acc = 0.0;
+      for (int t = 0; t < p->T; ++t) acc += dH[(size_t)t * p->N + i];
+      db_router[i] = acc;
+    }
+  if (du_router) parallel_for(p->T, nthreads, router_du_range, &c);
+}
+
+static double sigmoid(double g) { return 1.0 / (1.0 + exp(-g)); }
+
+/* weights of a routed expert (e >= 0) or of shared expert s (e = -1-s) */
+typedef struct {
+  int dff;
+  const void *wg, *wu, *wd;
+  size_t wg_off, wd_off;
+} expert_weights;
+
+static expert_weights weights_of(const oracle_problem* p, const oracle_inputs* in, int e) {
+  expert_weights w;
+  if (e >= 0) {
+    w.dff = p->d_ff;
+    w.wg = in->w_gate; w.wu = in->w_up; w.wd = in->w_down;
+    w.wg_off = (size_t)e * p->d_ff * p->d;
+    w.wd_off = (size_t)e * p->d * p->d_ff;
+  } else {
+    const int s = -1 - e;
+    w.dff = p->d_ff_shared;
+    w.wg = in->ws_gate; w.wu = in->ws_up; w.wd = in->ws_down;
+    w.wg_off = (size_t)s * p->d_ff_shared * p->d;
+    w.wd_off = (size_t)s * p->d * p->d_ff_shared;
+  }
+  return w;
+}
+
+/* hidden unit f of one row: g, v and (from dy) the gradients dG, dU and the
+ * stored activation a */
+static void unit_backward(const oracle_problem* p, const expert_weights* w, const void* x,
+                          size_t x_off, const double* dy, int f, double* dG, double* dU,
+                          double* a_stored) {
+  const int d = p->d;
+  const double g = dot_elems(x, x_off, w->wg, w->wg_off + (size_t)f * d, p->dtype, d);
+  double dA = 0.0;
+  for (int j = 0; j < d; ++j)
+    dA += dy[j] * load_elem(w->wd, p->dtype, w->wd_off + (size_t)j * w->dff + f);
+  if (p->act == OR_ACT_SWIGLU) {
+    const double v = dot_elems(x, x_off, w->wu, w->wg_off + (size_t)f * d, p->dtype, d);
+    const double sg = sigmoid(g);
+    const double silu = g * sg;
+    *dG = dA * v * sg * (1.0 + g * (1.0 - sg));
+    *dU = dA * silu;
+    if (a_stored) *a_stored = round_storage(silu * v, p->dtype);
+  } else {
+    *dG = g > 0.0 ? dA : 0.0;
+    *dU = 0.0;
+    if (a_stored) *a_stored = round_storage(g > 0.0 ? g : 0.0, p->dtype);
+  }
+}
+
+/* dx += backward of expert e on one row */
+static void expert_backward(const oracle_problem* p, const oracle_inputs* in, int e,
+                            const void* x, size_t x_off, const double* dy, double* dx) {
+  const expert_weights w = weights_of(p, in, e);
+  const int d = p->d;
+  for (int f = 0; f < w.dff; ++f) {
+    double dG, dU;
+    unit_backward(p, &w, x, x_off, dy, f, &dG, &dU, NULL);
+    for (int i = 0; i < d; ++i) {
+      dx[i] += dG * load_elem(w.wg, p->dtype, w.wg_off + (size_t)f * d + i);
+      if (p->act == OR_ACT_SWIGLU)
+        dx[i] += dU * load_elem(w.wu, p->dtype, w.wg_off + (size_t)f * d + i);
+    }
+  }
+}
+
+typedef struct {
+  const oracle_problem* p; const oracle_inputs* in; const void* x;
+  const int32_t* expert_of_row; const double* dy; double* dx;
+} ffn_bwd_ctx;
+
+static void ffn_bwd_range(void* vctx, int r0, int r1) {
+  ffn_bwd_ctx* c = (ffn_bwd_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  const int d = p->d;
+  for (int r = r0; r < r1; ++r) {
+    double* dx = c->dx + (size_t)r * d;
+    const double* dy = c->dy + (size_t)r * d;
+    for (int i = 0; i < d; ++i) dx[i] = 0.0;
+    const int e = c->expert_of_row[r];
+    if (e >= 0) {
+      expert_backward(p, c->in, e, c->x, (size_t)r * d, dy, dx);
+    } else {
+      for (int s = 0; s < p->n_shared; ++s)
+        expert_backward(p, c->in, -1 - s, c->x, (size_t)r * d, dy, dx);
+    }
+  }
+}
+
+void oracle_ffn_backward_rows(const oracle_problem* p, const oracle_inputs* in, int32_t n_rows,
+                              const void* x, const int32_t* expert_of_row, const double* dy,
+                              double* dx, int nthreads) {
+  ffn_bwd_ctx c = {p, in, x, expert_of_row, dy, dx};
+  parallel_for(n_rows, nthreads, ffn_bwd_range, &c);
+}
+
+typedef struct {
+  const oracle_problem* p; const oracle_inputs* in; int expert; int n_rows;
+  const void* x; const double* dy; const int32_t* f_list;
+  double *dwg, *dwu, *dwd;
+} wgrad_ctx;
+
+static void wgrad_range(void* vctx, int q0, int q1) {
+  wgrad_ctx* c = (wgrad_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  const int d = p->d;
+  const expert_weights w = weights_of(p, c->in, c->expert);
+  for (int q = q0; q < q1; ++q) {
+    const int f = c->f_list[q];
+    double* g_row = c->dwg + (size_t)q * d;
+    double* u_row = c->dwu ? c->dwu + (size_t)q * d : NULL;
+    double* d_col = c->dwd + (size_t)q * d;
+    for (int i = 0; i < d; ++i) {
+      g_row[i] = 0.0;
+      if (u_row) u_row[i] = 0.0;
+      d_col[i] = 0.0;
+    }
+    for (int r = 0; r < c->n_rows; ++r) {
+      double dG, dU, a;
+      const double* dy = c->dy + (size_t)r * d;
+      unit_backward(p, &w, c->x, (size_t)r * d, dy, f, &dG, &dU, &a);
+      for (int i = 0; i < d; ++i) {
+        const double xi = load_elem(c->x, p->dtype, (size_t)r * d + i);
+        g_row[i] += dG * xi;
+        if (u_row) u_row[i] += dU * xi;
+        d_col[i] += dy[i] * a;
+      }
+    }
+  }
+}
+
+void oracle_ffn_weight_grads(const oracle_problem* p, const oracle_inputs* in, int32_t expert,
+                             int32_t n_rows, const void* x, const double* dy, int32_t n_f,
+                             const int32_t* f_list, double* dw_gate_rows, double* dw_up_rows,
+                             double* dw_down_cols, int nthreads) {
+  wgrad_ctx c = {p, in, expert, n_rows, x, dy, f_list, dw_gate_rows,
+                 p->act == OR_ACT_SWIGLU ? dw_up_rows : NULL, dw_down_cols};
+  parallel_for(n_f, nthreads, wgrad_range, &c);
+}
+
+typedef struct {
+  const oracle_problem* p; const oracle_inputs* in; const float* H;
+  const int32_t* topk_idx; const double* topk_gate; const int32_t* row_of;
+  const double* d_out; const int32_t* tokens; double *du, *d_gate, *dH;
+} layer_bwd_ctx;
+
+static void layer_bwd_range(void* vctx, int r0, int r1) {
+  layer_bwd_ctx* c = (layer_bwd_ctx*)vctx;
+  const oracle_problem* p = c->p;
+  const int d = p->d, K = p->K, N = p->N;
+  double* act = (double*)malloc(sizeof(double) * (size_t)max_width(p));
+  double* ytmp = (double*)malloc(sizeof(double) * (size_t)d);
+  double* y = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dy = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int r = r0; r < r1; ++r) {
+    const int t = c->tokens ? c->tokens[r] : r;
+    const double* o = c->d_out + (size_t)t * d;
+    const size_t u_off = (size_t)t * d;
+    double* du = c->du + (size_t)r * d;
+    double* dg = c->d_gate + (size_t)r * K;
+    double* dH = c->dH + (size_t)r * N;
+    for (int j = 0; j < d; ++j) du[j] = o[j];                 /* residual */
+    for (int k = 0; k < K; ++k) {
+      dg[k] = 0.0;
+      if (c->row_of[(size_t)t * K + k] < 0) continue;        /* dropped */
+      const int e = c->topk_idx[(size_t)t * K + k];
+      const double g = c->topk_gate[(size_t)t * K + k];
+      expert_output(p, c->in, e, c->in->u, u_off, act, ytmp, y);
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j) acc += o[j] * y[j];
+      dg[k] = acc;
+      for (int j = 0; j < d; ++j) dy[j] = g * o[j];
+      expert_backward(p, c->in, e, c->in->u, u_off, dy, du);
+    }
+    for (int s = 0; s < p->n_shared; ++s)
+      expert_backward(p, c->in, -1 - s, c->in->u, u_off, o, du);
+    gate_jacobian_row(p, c->H + (size_t)t * N, c->topk_idx + (size_t)t * K,
+                      c->topk_gate + (size_t)t * K, dg, dH);
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < N; ++i) acc += dH[i] * (double)c->in->w_router[(size_t)i * d + j];
+      du[j] += acc;
+    }
+  }
+  free(act);
+  free(ytmp);
+  free(y);
+  free(dy);
+}
+
+void oracle_layer_backward_rows(const oracle_problem* p, const oracle_inputs* in,
+                                const float* H, const int32_t* topk_idx,
+                                const double* topk_gate, const int32_t* row_of,
+                                const double* d_out, int32_t n_tokens, const int32_t* tokens,
+                                double* du, double* d_gate, double* dH, int nthreads) {
+  layer_bwd_ctx c = {p, in, H, topk_idx, topk_gate, row_of, d_out, tokens, du, d_gate, dH};
+  parallel_for(n_tokens, nthreads, layer_bwd_range, &c);
+}

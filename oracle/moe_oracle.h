@@ -164,6 +164,76 @@ void oracle_ec_select(const oracle_problem* p, const double* probs, int32_t C,
                       int32_t* expert_tokens, double* expert_gates, int32_t* row_of,
                       double* gate_of);
 
+/* ------------------------------------------------------------------ */
+/* Backward pass.  The gradient of the layer output with respect to u,   */
+/* the router weights and bias and the expert weights, given d_out =      */
+/* dL/dh.  The routing (Top-K sets, capacity drops) is held fixed, as it  */
+/* is piecewise constant in the inputs; gradients reach the router        */
+/* through the gates.  Everything in double; the forward values that the  */
+/* method materialises (H in fp32, act and y in the storage type) enter   */
+/* as stored.                                                             */
+/* ------------------------------------------------------------------ */
+
+/* Combine backward:
+ *   dy[row][j]   = gate[t][k] * d_out[t][j]       for kept (t, k), row = row_of[t][k]
+ *   d_gate[t][k] = sum_j d_out[t][j] * y[row][j]  (0 for a dropped assignment)
+ * y [T*K][d] elem, d_out [T][d]; rows of dy that no kept assignment
+ * references are left untouched. */
+void oracle_combine_backward(const oracle_problem* p, const double* d_out, const void* y,
+                             const int32_t* row_of, const double* gate, double* dy,
+                             double* d_gate);
+
+/* Gating Jacobian, dH [T][N] from d_gate [T][K]:
+ *   SOFTMAX_TOPK (g_k = s_{e_k}, s = softmax over all N of H):
+ *     dH_i = s_i (delta_i - sum_k g_k dg_k),  delta_i = dg_k if i = e_k, else 0
+ *   TOPK_SOFTMAX (g = softmax over the K selected scores):
+ *     dH_{e_k} = g_k (dg_k - sum_m g_m dg_m), every other dH_i = 0 */
+void oracle_route_backward(const oracle_problem* p, const float* H, const int32_t* topk_idx,
+                           const double* topk_gate, const double* d_gate, double* dH);
+
+/* Router parameters:  dw_router[i][j] = sum_t dH[t][i] u[t][j];
+ * db_router[i] = sum_t dH[t][i];  du_router[t][j] = sum_i dH[t][i] w_router[i][j].
+ * Any output may be NULL. */
+void oracle_router_param_grads(const oracle_problem* p, const oracle_inputs* in,
+                               const double* dH, double* dw_router, double* db_router,
+                               double* du_router, int nthreads);
+
+/* Expert FFN backward for n rows: row r is the input x + r*d of expert
+ * expert_of_row[r] (0..N-1 routed; -1: every shared expert, each receiving
+ * the same dy), dy [n][d] the gradient of its output, dx [n][d] the
+ * gradient of its input.  With g = W_gate x, v = W_up x, a = SiLU(g) v:
+ *   dA = W_down^T dy,  dG = dA v SiLU'(g),  dU = dA SiLU(g),
+ *   dx = W_gate^T dG + W_up^T dU
+ * (ReLU FFN: dG = dA [g > 0], dx = W_1^T dG). */
+void oracle_ffn_backward_rows(const oracle_problem* p, const oracle_inputs* in, int32_t n_rows,
+                              const void* x, const int32_t* expert_of_row, const double* dy,
+                              double* dx, int nthreads);
+
+/* Weight gradients of one expert for selected hidden units f = f_list[q]:
+ *   dw_gate_rows[q][:] = sum_r dG[r][f] x[r][:]     (row f of dW_gate)
+ *   dw_up_rows[q][:]   = sum_r dU[r][f] x[r][:]     (row f of dW_up; NULL for ReLU)
+ *   dw_down_cols[q][:] = sum_r dy[r][:] a[r][f]     (column f of dW_down)
+ * over the n rows of x (elem) and dy (double) that the expert processed;
+ * a is the stored activation (rounded to the storage type).  expert =
+ * 0..N-1 for a routed expert, -1-s for shared expert s. */
+void oracle_ffn_weight_grads(const oracle_problem* p, const oracle_inputs* in, int32_t expert,
+                             int32_t n_rows, const void* x, const double* dy, int32_t n_f,
+                             const int32_t* f_list, double* dw_gate_rows, double* dw_up_rows,
+                             double* dw_down_cols, int nthreads);
+
+/* Whole-layer backward for a list of tokens (tokens == NULL: all T),
+ * from the routing of a forward pass:
+ *   d_gate[r][k] = <d_out_t, y_{t,k}>, y recomputed and rounded as stored
+ *   dH[r][:]     the gating Jacobian applied to d_gate
+ *   du[r][:]     = d_out_t + sum_{k kept} dx_{e_k}(g_k d_out_t)
+ *                  + dx_shared(d_out_t) + W_router^T dH[r]
+ * with t = tokens[r].  d_out [T][d]. */
+void oracle_layer_backward_rows(const oracle_problem* p, const oracle_inputs* in,
+                                const float* H, const int32_t* topk_idx,
+                                const double* topk_gate, const int32_t* row_of,
+                                const double* d_out, int32_t n_tokens, const int32_t* tokens,
+                                double* du, double* d_gate, double* dH, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -89,6 +89,14 @@ def lib():
         L.oracle_ec_capacity.argtypes = [i32, i32, i32, ctypes.c_float]
         L.oracle_ec_capacity.restype = i32
         L.oracle_ec_select.argtypes = [P, vp, i32, vp, vp, vp, vp]
+        L.oracle_combine_backward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.oracle_route_backward.argtypes = [P, vp, vp, vp, vp, vp]
+        L.oracle_router_param_grads.argtypes = [P, I, vp, vp, vp, vp, ctypes.c_int]
+        L.oracle_ffn_backward_rows.argtypes = [P, I, i32, vp, vp, vp, vp, ctypes.c_int]
+        L.oracle_ffn_weight_grads.argtypes = [P, I, i32, i32, vp, vp, i32, vp, vp, vp, vp,
+                                              ctypes.c_int]
+        L.oracle_layer_backward_rows.argtypes = [P, I, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                                 ctypes.c_int]
         _lib = L
     return _lib
 
@@ -275,3 +283,92 @@ def ec_layer_rows(p: Problem, x: Inputs, sel: Dict[str, np.ndarray], tokens=None
     pe = dataclasses.replace(p, K=p.N)
     idx = np.tile(np.arange(p.N, dtype=np.int32), (p.T, 1))
     return layer_rows(pe, x, idx, sel["gate_of"], sel["row_of"], tokens, nthreads)
+
+
+# ------------------------------------------------------------------ backward
+
+def _f64(a, shape=None):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None:
+        assert a.shape == tuple(shape), (a.shape, shape)
+    return a
+
+
+def combine_backward(p: Problem, d_out, y, row_of, gate) -> Dict[str, np.ndarray]:
+    """dy [T*K][d] (rows no kept assignment references are 0) and d_gate [T][K]."""
+    do = _f64(d_out, (p.T, p.d))
+    yy = _elem_array(y, p.dtype)
+    rof = np.ascontiguousarray(row_of, dtype=np.int32)
+    g = _f64(gate, (p.T, p.K))
+    assert yy.shape == (p.T * p.K, p.d) and rof.shape == (p.T, p.K)
+    o = dict(dy=np.zeros((p.T * p.K, p.d)), d_gate=np.zeros((p.T, p.K)))
+    lib().oracle_combine_backward(ctypes.byref(p.c()), _ptr(do), _ptr(yy), _ptr(rof), _ptr(g),
+                                  _ptr(o["dy"]), _ptr(o["d_gate"]))
+    return o
+
+
+def route_backward(p: Problem, H, topk_idx, topk_gate, d_gate) -> np.ndarray:
+    """dH [T][N]: the gating Jacobian applied to d_gate."""
+    h = np.ascontiguousarray(H, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    g = _f64(topk_gate, (p.T, p.K))
+    dg = _f64(d_gate, (p.T, p.K))
+    dH = np.zeros((p.T, p.N))
+    lib().oracle_route_backward(ctypes.byref(p.c()), _ptr(h), _ptr(idx), _ptr(g), _ptr(dg), _ptr(dH))
+    return dH
+
+
+def router_param_grads(p: Problem, x: Inputs, dH, nthreads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """dw_router [N][d], db_router [N], du_router [T][d] from dH [T][N]."""
+    h = _f64(dH, (p.T, p.N))
+    o = dict(dw_router=np.zeros((p.N, p.d)), db_router=np.zeros(p.N), du_router=np.zeros((p.T, p.d)))
+    lib().oracle_router_param_grads(ctypes.byref(p.c()), ctypes.byref(x.c), _ptr(h),
+                                    _ptr(o["dw_router"]), _ptr(o["db_router"]), _ptr(o["du_router"]),
+                                    nthreads or nthreads_default())
+    return o
+
+
+def ffn_backward_rows(p: Problem, x: Inputs, rows, expert_of_row, dy,
+                      nthreads: Optional[int] = None) -> np.ndarray:
+    """dx [n][d] of the expert FFN of each row (-1: the shared experts)."""
+    xr = _elem_array(rows, p.dtype)
+    eor = np.ascontiguousarray(expert_of_row, dtype=np.int32)
+    n = len(eor)
+    dyy = _f64(dy, (n, p.d))
+    dx = np.zeros((n, p.d))
+    lib().oracle_ffn_backward_rows(ctypes.byref(p.c()), ctypes.byref(x.c), n, _ptr(xr), _ptr(eor),
+                                   _ptr(dyy), _ptr(dx), nthreads or nthreads_default())
+    return dx
+
+
+def ffn_weight_grads(p: Problem, x: Inputs, expert: int, rows, dy, f_list,
+                     nthreads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Rows f of dW_gate and dW_up, columns f of dW_down (as [n_f][d]) of one
+    expert (routed 0..N-1, shared s as -1-s) over the given rows."""
+    xr = _elem_array(rows, p.dtype)
+    n = xr.shape[0]
+    dyy = _f64(dy, (n, p.d))
+    fl = np.ascontiguousarray(f_list, dtype=np.int32)
+    o = dict(dw_gate=np.zeros((len(fl), p.d)), dw_up=np.zeros((len(fl), p.d)),
+             dw_down=np.zeros((len(fl), p.d)))
+    lib().oracle_ffn_weight_grads(ctypes.byref(p.c()), ctypes.byref(x.c), int(expert), n, _ptr(xr),
+                                  _ptr(dyy), len(fl), _ptr(fl), _ptr(o["dw_gate"]), _ptr(o["dw_up"]),
+                                  _ptr(o["dw_down"]), nthreads or nthreads_default())
+    return o
+
+
+def layer_backward_rows(p: Problem, x: Inputs, H, topk_idx, topk_gate, row_of, d_out, tokens=None,
+                        nthreads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """du, d_gate and dH of the listed tokens (all when tokens is None)."""
+    h = np.ascontiguousarray(H, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    g = _f64(topk_gate, (p.T, p.K))
+    rof = np.ascontiguousarray(row_of, dtype=np.int32)
+    do = _f64(d_out, (p.T, p.d))
+    tk = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = p.T if tk is None else len(tk)
+    o = dict(du=np.zeros((n, p.d)), d_gate=np.zeros((n, p.K)), dH=np.zeros((n, p.N)))
+    lib().oracle_layer_backward_rows(ctypes.byref(p.c()), ctypes.byref(x.c), _ptr(h), _ptr(idx), _ptr(g),
+                                     _ptr(rof), _ptr(do), n, _ptr(tk), _ptr(o["du"]), _ptr(o["d_gate"]),
+                                     _ptr(o["dH"]), nthreads or nthreads_default())
+    return o
