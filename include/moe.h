@@ -16,6 +16,7 @@
  *     moe_layer_forward  the four stages in order on one stream
  *     moe_router_stats   load-balance and z statistics from the side outputs
  *     moe_ec_*           expert-choice routing (experts select their tokens)
+ *     moe_layer_backward the gradients of the layer (training)
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is DEVICE memory owned by the caller (for example
@@ -235,6 +236,73 @@ typedef struct moe_layer_outputs {
 int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
                       const moe_weights_t* w, moe_layer_outputs_t* o, void* out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Backward pass.  The gradient of the layer output h (MoE-layer equation
+ * of "Mixture-of-Experts (MoE)", ML notes, through the stages of "From
+ * Router to Combine") with respect to u, the router weights and bias and
+ * the routed and shared expert weights, given d_out = dL/dh, for bf16
+ * problems.  The Top-K sets and capacity decisions of the forward pass are
+ * held fixed (they are piecewise constant in the inputs); gradients reach
+ * the router through the gates:
+ *   dY[row]      = g_{t,k} d_out_t                          (kept (t, k))
+ *   d_gate[t][k] = <d_out_t, y_perm[row]>                   (0 if dropped)
+ *   d_scores     = the gating variant's Jacobian applied to d_gate
+ *                  SOFTMAX_TOPK: dH_i = s_i (delta_i - sum_k g_k dg_k)
+ *                  TOPK_SOFTMAX: dH_{e_k} = g_k (dg_k - sum_m g_m dg_m)
+ *   dA = dY W_down,  dG = dA v SiLU'(g),  dU = dA SiLU(g)   (g, v recomputed)
+ *   dX = W_gate^T dG + W_up^T dU;   dW_down = sum_rows dY a^T,
+ *   dW_gate = sum_rows dG x^T,  dW_up = sum_rows dU x^T
+ *   dW_router = sum_t dH_t u_t^T,  db = sum_t dH_t
+ *   du_t = d_out_t + sum_k dX[row_of[t][k]] + dX_shared_t + W_router^T dH_t
+ * Shared experts: the same with dY = d_out over every token.  The noise
+ * input gets no gradient.
+ * Precision: dY, dA, a, dG, dU and dX are stored in bf16; every GEMM and
+ * every sum accumulates in fp32 in a fixed order; du and the expert weight
+ * gradients are rounded once to bf16; router gradients are fp32.
+ * Results are bit-identical run to run. */
+
+/* What the backward needs from the forward pass (its outputs). */
+typedef struct moe_saved {
+  const float* scores;      /* [T][N] fp32; may be NULL for MOE_GATE_TOPK_SOFTMAX */
+  const int32_t* topk_idx;  /* [T][K] */
+  const float* topk_gate;   /* [T][K] */
+  const int32_t* row_of;    /* [T][K] */
+  const int32_t* offsets;   /* [N+1] */
+  const void* x_perm;       /* [T*K][d] elem */
+  const void* y_perm;       /* [T*K][d] elem */
+} moe_saved_t;
+
+/* Gradients (device pointers, all written).  Weight gradients have the
+ * shapes of the weights in moe_weights_t; dw_up (and dws_up) NULL for ReLU;
+ * the dws_* are required iff n_shared > 0.  The last four are optional
+ * intermediates (NULL: kept in the workspace). */
+typedef struct moe_grads {
+  void* du;                 /* [T][d] elem  */
+  float* dw_router;         /* [N][d] fp32  */
+  float* db_router;         /* [N] fp32 or NULL */
+  void* dw_gate;
+  void* dw_up;
+  void* dw_down;
+  void* dws_gate;
+  void* dws_up;
+  void* dws_down;
+  float* d_gate;            /* [T][K] fp32 or NULL */
+  float* d_scores;          /* [T][N] fp32 or NULL */
+  void* dy_perm;            /* [T*K][d] elem or NULL (rows past offsets[N] unspecified) */
+  void* dx_perm;            /* [T*K][d] elem or NULL (rows past offsets[N] unspecified) */
+} moe_grads_t;
+
+/* Workspace bytes of moe_layer_backward (0 for T == 0 or an invalid p). */
+size_t moe_backward_workspace_size(const moe_problem_t* p);
+
+/* The backward pass on `stream`.  In: u, the weights, the forward's saved
+ * outputs and d_out [T][d] elem.  Errors: UNSUPPORTED for fp32 problems;
+ * INVALID_ARG for a missing required pointer (scores with SOFTMAX_TOPK
+ * gating); WORKSPACE if ws_bytes < moe_backward_workspace_size(p). */
+int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_t* w,
+                       const moe_saved_t* s, const void* d_out, moe_grads_t* g, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Expert choice ("Mixture of Experts (MoE)" glossary, sparse-MoE entry:

@@ -19,7 +19,14 @@
 namespace moe {
 namespace {
 
-enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+// Epilogues.  The two backward ones run on the recomputed gate (and up)
+// accumulators of GEMM-1 with the activation gradient dA = dY W_down as the
+// extra input D: they write the activation a (to C, for dW_down) and the
+// pre-activation gradients (to C2, [rows][2*Ndim]: dG then dU; ReLU: dG).
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_RELU_BWD = 4 };
+
+template <int EPI>
+constexpr bool gated() { return EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD; }
 
 struct GemmArgs {
   const void* A;            // activations [rows_alloc][lda]
@@ -40,6 +47,11 @@ struct GemmArgs {
   int kseg;                 // K-segment length of B (Kdim when unsegmented)
   size_t kseg_stride;       // elements between K-segments of B
   size_t b_group_stride;    // elements between consecutive groups' B
+  // backward epilogues: D = dA [rows][ldd]; C2 = pre-activation gradients
+  const void* D;
+  int ldd;
+  void* C2;
+  int ldc2;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -199,25 +211,75 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-__device__ __forceinline__ float silu_fast(float g) {
-  // g * sigmoid(g) with the hardware exp2 and reciprocal
-  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  // 1 / (1 + e^-g) with the hardware exp2 and reciprocal
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+__device__ __forceinline__ float silu_fast(float g) { return g * sigmoid_fast(g); }
+
+// ---------------------------------------------------- k-major operands
+// The backward GEMMs read operands whose reduction index k is the row index
+// of a row-major array (W_down as [d][d_ff] for dY W_down, the stacked
+// [W_gate; W_up] for dGU W, and every operand of the weight gradients,
+// which reduce over the rows of a group).  Such a tile, 64 k-rows x 256
+// columns (512 bytes a row), is loaded row by row into LDS and transposed
+// on the way to the matrix cores by ds_read_b64_tr_b16.
+//
+// LDS layout: 16-byte chunk c of tile row r sits at slot c ^ 4*(r%4).  A
+// transposing read fetches, per 16 lanes, 8 bytes from 4 consecutive rows
+// at 4 consecutive 8-byte positions; with the XOR the 32 lanes of each half
+// wave hit 16 different 16-byte bank groups.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// voffset (bytes, from the tile's first row and column) of direct load q of
+// a k-major tile: the instruction fills LDS rows 2q and 2q+1; lane l writes
+// slot l%32 of row 2q + l/32, which holds chunk (l%32) ^ 4*(row%4).
+__device__ __forceinline__ uint32_t kmajor_voff(int q, int lane, int ld) {
+  const int r = 2 * q + (lane >> 5);
+  const int c = (lane & 31) ^ (4 * (r & 3));
+  return (uint32_t)(r * ld + c * 8) * 2u;
+}
+
+// MFMA operand of a k-major LDS tile: lane l gets column col0 + l%32 at the
+// eight k = 16*kk + 8*(l/32) .. +7.  Each 16-lane group of a transposing
+// read hands lane i element i%4 of the 8 bytes that lane 4j + i/4 of the
+// group addressed (as its j-th element), so lane s of a group addresses row
+// k0 + s/4, columns 4*(s%4) .. +3 past the group's first column.
+__device__ __forceinline__ bf16x8 read_kmajor(const char* tile, int kk, int col0, int lane) {
+  const int s = lane & 15;
+  const int row = 16 * kk + 8 * (lane >> 5) + (s >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int off = row * 512 + (((col >> 3) ^ (4 * (row & 3))) << 4) + ((col >> 2) & 1) * 8;
+  // rows row and row+4 have the same row%4, hence the same slot
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off + 4 * 512));
+  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
 }
 
 // One BM x BN output tile of group g (rows [row0, row0+rows), n-tile by),
 // staged through the caller's LDS arrays (at least BM and BN rows a stage).
-template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN>
+//
+// BT: B is k-major (B[k][n] row-major, n contiguous; see above) instead of
+// [n][k]; only with EPI_NONE and BN = 256.
+template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN, bool BT = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, int rows, int by,
                                           u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN]) {
   constexpr int NW = WGM * WGN;                   // waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;     // 32x32 accumulators per wave
-  constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW;   // 1-KB direct loads per wave per stage
+  constexpr bool GATED = gated<EPI>();
+  // 1-KB direct loads per wave per stage
+  constexpr int AI = BM / 8 / NW, BI = BT ? 32 / NW : BN / 8 / NW;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(AI >= 1 && BI >= 1, "every wave loads A and B rows");
-  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+  static_assert(!GATED || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
   static_assert(SAN >= BM * 8 && SBN >= BN * 8, "LDS stages hold the tile");
-  constexpr int BNH = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per tile
+  static_assert(!BT || (EPI == EPI_NONE && BN == 256), "k-major B: plain epilogue, 256 columns");
+  constexpr int BNH = GATED ? BN / 2 : BN;        // output columns per tile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -249,7 +311,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   // the same columns.
   const uint16_t* Bsrc = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
   int b_local0 = wave * (BN / NW);
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (GATED) {
     if (wave >= NW / 2) {
       Bsrc = static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride;
       b_local0 -= BN / 2;
@@ -268,7 +330,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   auto issue = [&](int kt, int buf) {
     const int kb = kt * BK;
     const int seg = kb / a.kseg;
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bsrc + (size_t)seg * a.kseg_stride, b_bytes);
     const uint32_t ka = (uint32_t)kb * 2, kbb = (uint32_t)(kb - seg * a.kseg) * 2;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
@@ -276,6 +337,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
                                                (odd ? a_voff_o : a_voff_e) + i * a_step + ka, 0, 0, 0);
     }
+    if constexpr (BT) {
+      // k-major B: segment 0 from B0, segment 1 from B1; rows of the
+      // segment, columns n0 .. n0+255
+      const uint16_t* base = static_cast<const uint16_t*>(seg == 0 ? a.B0 : a.B1) +
+                             (size_t)g * a.b_group_stride + n0;
+      const __amdgpu_buffer_rsrc_t rBT =
+          make_rsrc(base, (uint32_t)((size_t)a.kseg * a.ldb - n0) * 2u);
+      const uint32_t krow = (uint32_t)(kb - seg * a.kseg) * (uint32_t)a.ldb * 2u;
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rBT, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
+                                                 kmajor_voff(wave * BI + i, lane, a.ldb) + krow,
+                                                 0, 0, 0);
+      return;
+    }
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bsrc + (size_t)seg * a.kseg_stride, b_bytes);
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const bool odd = ((wave * BI + i) & 1) != 0;
@@ -294,7 +371,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
 
   // first row of each n-tile of this wave inside the B tile
   auto brow = [&](int j) {
-    if constexpr (EPI == EPI_SWIGLU)
+    if constexpr (GATED)
       return j < TN / 2 ? wn * (WTN / 2) + 32 * j : BN / 2 + wn * (WTN / 2) + 32 * (j - TN / 2);
     else
       return wn * WTN + 32 * j;
@@ -313,8 +390,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
     for (int i = 0; i < TM; ++i)
       fa[0][i] = __builtin_bit_cast(bf16x8, sA[buf][swz(wm * WTM + i * 32 + (lane & 31), (lane >> 5))]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      fb[0][j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), (lane >> 5))]);
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (BT) fb[0][j] = read_kmajor((const char*)&sB[buf][0], 0, brow(j), lane);
+      else fb[0][j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), (lane >> 5))]);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int cur = kk & 1;
@@ -324,8 +403,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
         for (int i = 0; i < TM; ++i)
           fa[cur ^ 1][i] = __builtin_bit_cast(bf16x8, sA[buf][swz(wm * WTM + i * 32 + (lane & 31), c)]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          fb[cur ^ 1][j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), c)]);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (BT) fb[cur ^ 1][j] = read_kmajor((const char*)&sB[buf][0], kk + 1, brow(j), lane);
+          else fb[cur ^ 1][j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), c)]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -340,8 +421,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
 
   // epilogue: lane holds column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4
   uint16_t* C = static_cast<uint16_t*>(a.C);
-  constexpr int OUT_TN = EPI == EPI_SWIGLU ? TN / 2 : TN;
-  const int col_base = n0 + (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) + (lane & 31);
+  constexpr int OUT_TN = GATED ? TN / 2 : TN;
+  const int col_base = n0 + (GATED ? wn * (WTN / 2) : wn * WTN) + (lane & 31);
+  if constexpr (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) {
+    // a = act(g[, v]) to C; dG (and dU) from dA to C2
+    const uint16_t* D = static_cast<const uint16_t*>(a.D);
+    uint16_t* C2 = static_cast<uint16_t*>(a.C2);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < OUT_TN; ++j) {
+        const int col = col_base + 32 * j;
+        if (col >= a.Ndim) continue;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          f32x2 pa, pg, pu;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int r = wm * WTM + i * 32 + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
+            const float da = r < rows ? bf16_to_f32(D[(size_t)(row0 + r) * a.ldd + col]) : 0.0f;
+            const float gv = acc[i][j][v + q];
+            if constexpr (EPI == EPI_SWIGLU_BWD) {
+              const float up = acc[i][j + TN / 2][v + q];
+              const float sg = sigmoid_fast(gv);
+              const float sl = gv * sg;
+              pa[q] = sl * up;
+              pg[q] = da * up * sg * (1.0f + gv * (1.0f - sg));
+              pu[q] = da * sl;
+            } else {
+              pa[q] = gv > 0.0f ? gv : 0.0f;
+              pg[q] = gv > 0.0f ? da : 0.0f;
+              pu[q] = 0.0f;
+            }
+          }
+          const uint32_t qa = __builtin_bit_cast(uint32_t, __builtin_convertvector(pa, bf16x2));
+          const uint32_t qg = __builtin_bit_cast(uint32_t, __builtin_convertvector(pg, bf16x2));
+          const uint32_t qu = __builtin_bit_cast(uint32_t, __builtin_convertvector(pu, bf16x2));
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int r = wm * WTM + i * 32 + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
+            if (r >= rows) continue;
+            const size_t row = (size_t)(row0 + r);
+            C[row * a.ldc + col] = (uint16_t)(q ? qa >> 16 : qa & 0xffffu);
+            C2[row * a.ldc2 + col] = (uint16_t)(q ? qg >> 16 : qg & 0xffffu);
+            if constexpr (EPI == EPI_SWIGLU_BWD)
+              C2[row * a.ldc2 + a.Ndim + col] = (uint16_t)(q ? qu >> 16 : qu & 0xffffu);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -377,37 +507,177 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
 constexpr int kTailRows = 64;
 constexpr int kExtRows = 64;
 
-template <int EPI>
+template <int EPI, bool BT = false>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
   __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
   __shared__ u32x4 sB[2][256 * 8];
-  constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
+  constexpr int BNH = gated<EPI>() ? 128 : 256;
   const int ntiles = (a.Ndim + BNH - 1) / BNH;
   const int real = full_tiles_total(a, 256) * ntiles;
   const int h = blockIdx.x;
   int g, row0, rows, by;
   if (h < real) {
     find_tile_2d(a, 256, ntiles, h, real, g, row0, rows, by);
-    if (rows > 256) gemm_tile<EPI, 256 + kExtRows, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
-    else gemm_tile<EPI, 256, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
+    if (rows > 256) gemm_tile<EPI, 256 + kExtRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
+    else gemm_tile<EPI, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
   } else if (find_tail(a, 256, ntiles, h - real, g, row0, rows, by)) {
-    gemm_tile<EPI, kTailRows, 256, 2, 4>(a, g, row0, rows, by, sA, sB);
+    gemm_tile<EPI, kTailRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
   }
 }
 
 // Groups of a few rows (decode-sized batches): 32x256 tiles on 4 waves.
-template <int EPI>
+template <int EPI, bool BT = false>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_small_kernel(GemmArgs a) {
   __shared__ u32x4 sA[2][32 * 8];
   __shared__ u32x4 sB[2][256 * 8];
-  constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
+  constexpr int BNH = gated<EPI>() ? 128 : 256;
   const int ntiles = (a.Ndim + BNH - 1) / BNH;
   const int real = full_tiles_total(a, 32) * ntiles;
   const int h = blockIdx.x;
   if (h >= real) return;
   int g, row0, rows, by;
   find_tile_2d(a, 32, ntiles, h, real, g, row0, rows, by);
-  gemm_tile<EPI, 32, 256, 1, 4>(a, g, row0, rows, by, sA, sB);
+  gemm_tile<EPI, 32, 256, 1, 4, 32 * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
+}
+
+// ------------------------------------------------------ weight gradients
+// dW = A^T B per group, reducing over the group's rows: A [rows][lda]
+// supplies the output rows m (its columns), B [rows][ldb] the output
+// columns n.  Both operands are k-major (the rows are the reduction), so
+// both go through the transposing LDS reads.  256x256 output tiles on 8
+// waves of 128x64; one block per (group, m-tile, n-tile), looping over the
+// group's rows 64 at a time (rows past the group read as zero through the
+// buffer descriptors' sizes).  An empty group writes zeros.
+struct WgradArgs {
+  const void* A;
+  int lda;
+  const void* B;
+  int ldb;
+  const int32_t* offsets;   // [G+1] row groups, or null: one group of Krows rows
+  int G, Krows;
+  int M, N;                 // output rows (A columns) and columns (B columns)
+  void* C;                  // output rows m < msplit
+  void* C2;                 // output rows m >= msplit (as row m - msplit)
+  int msplit;
+  size_t c_group_stride;    // elements between consecutive groups' outputs
+  int ldc;
+  int nseg;                 // column n goes to segment n / nseg ...
+  size_t nseg_stride;       // ... at nseg_stride elements per segment, column n % nseg
+};
+
+__global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
+  __shared__ u32x4 sA[2][256 * 8];
+  __shared__ u32x4 sB[2][256 * 8];
+  constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2, PER = 32 / NW;
+  const int mtn = (a.M + 255) / 256, ntn = (a.N + 255) / 256;
+  const int per_g = mtn * ntn, total = a.G * per_g;
+  const int h = blockIdx.x;
+  if (h >= total) return;
+  // XCD-contiguous runs of tiles (consecutive blocks go to different XCDs)
+  const int full = total - total % 8;
+  const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
+  const int g = __builtin_amdgcn_readfirstlane(L / per_g);
+  const int rem = L - g * per_g;
+  const int mt = __builtin_amdgcn_readfirstlane(rem / ntn);
+  const int nt = __builtin_amdgcn_readfirstlane(rem - mt * ntn);
+  const int r0 = __builtin_amdgcn_readfirstlane(a.offsets ? a.offsets[g] : 0);
+  const int rows = __builtin_amdgcn_readfirstlane(a.offsets ? a.offsets[g + 1] - r0 : a.Krows);
+  const int m0 = mt * 256, n0 = nt * 256;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const long long abytes = ((long long)rows * a.lda - m0) * 2;
+  const long long bbytes = ((long long)rows * a.ldb - n0) * 2;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+      static_cast<const uint16_t*>(a.A) + (size_t)r0 * a.lda + m0, (uint32_t)(abytes > 0 ? abytes : 0));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+      static_cast<const uint16_t*>(a.B) + (size_t)r0 * a.ldb + n0, (uint32_t)(bbytes > 0 ? bbytes : 0));
+  lds_t* ldsA[2] = {(lds_t*)&sA[0][wave * PER * 64], (lds_t*)&sA[1][wave * PER * 64]};
+  lds_t* ldsB[2] = {(lds_t*)&sB[0][wave * PER * 64], (lds_t*)&sB[1][wave * PER * 64]};
+
+  auto issue = [&](int kt, int buf) {
+    const uint32_t ka = (uint32_t)kt * BK * (uint32_t)a.lda * 2u;
+    const uint32_t kb = (uint32_t)kt * BK * (uint32_t)a.ldb * 2u;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
+                                               kmajor_voff(wave * PER + i, lane, a.lda) + ka, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
+                                               kmajor_voff(wave * PER + i, lane, a.ldb) + kb, 0, 0, 0);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int nk = (rows + BK - 1) / BK;
+  if (nk > 0) {
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+    const char* tA = (const char*)&sA[buf][0];
+    const char* tB = (const char*)&sB[buf][0];
+    bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = read_kmajor(tA, 0, wm * WTM + 32 * i, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = read_kmajor(tB, 0, wn * WTN + 32 * j, lane);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = read_kmajor(tA, kk + 1, wm * WTM + 32 * i, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = read_kmajor(tB, kk + 1, wn * WTN + 32 * j, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // epilogue: lane holds column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + wn * WTN + 32 * j + (lane & 31);
+    if (n >= a.N) continue;
+    const size_t ncol = (size_t)(n / a.nseg) * a.nseg_stride + (size_t)(n % a.nseg);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        f32x2 pr;
+        pr[0] = acc[i][j][v];
+        pr[1] = acc[i][j][v + 1];
+        const uint32_t packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int m = m0 + wm * WTM + 32 * i + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
+          if (m >= a.M) continue;
+          uint16_t* out = static_cast<uint16_t*>(m < a.msplit ? a.C : a.C2) + (size_t)g * a.c_group_stride;
+          const int mr = m < a.msplit ? m : m - a.msplit;
+          out[(size_t)mr * a.ldc + ncol] = (uint16_t)(q ? packed >> 16 : packed & 0xffffu);
+        }
+      }
+    }
+  }
 }
 
 // --------------------------------------------------------------- fp32
@@ -473,14 +743,14 @@ struct TileShape { int bm; };
 
 TileShape pick_tiles(int rows_per_group) { return TileShape{rows_per_group >= 128 ? 256 : 32}; }
 
-template <int EPI>
+template <int EPI, bool BT = false>
 hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
-  constexpr int BNH = EPI == EPI_SWIGLU ? 128 : 256;
+  constexpr int BNH = gated<EPI>() ? 128 : 256;
   dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
   if (bm == 256)
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<EPI>, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL(grouped_gemm_bf16_small_kernel<EPI>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_small_kernel<EPI, BT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -619,6 +889,201 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     if ((e = run_gemm(s2, EPI_NONE, bf16, sbm, mt, s)) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// ----------------------------------------------------------- backward
+// The expert FFN backward, from the forward's rows and the output
+// gradients dY (see the header of this file for the forward GEMMs):
+//   dA  = dY W_down                      (k-major W_down)
+//   G, U recomputed by GEMM-1; its backward epilogue writes the stored
+//        activation a and dG = dA v SiLU'(g), dU = dA SiLU(g)   (ReLU: dG)
+//   dX  = [dG dU] [W_gate; W_up]         (k-major weights, two segments)
+//   dW_down[e] = dY_e^T a_e,  [dW_gate; dW_up][e] = [dG dU]_e^T X_e
+// and the same for the shared experts over all tokens with dY = d_out.
+namespace {
+
+WgradArgs wgrad_args(const void* A, int lda, const void* B, int ldb, const int32_t* offsets, int G,
+                     int Krows, int M, int N, void* C, void* C2, int msplit, size_t c_group_stride,
+                     int ldc, int nseg, size_t nseg_stride) {
+  WgradArgs w{};
+  w.A = A;
+  w.lda = lda;
+  w.B = B;
+  w.ldb = ldb;
+  w.offsets = offsets;
+  w.G = G;
+  w.Krows = Krows;
+  w.M = M;
+  w.N = N;
+  w.C = C;
+  w.C2 = C2;
+  w.msplit = msplit;
+  w.c_group_stride = c_group_stride;
+  w.ldc = ldc;
+  w.nseg = nseg;
+  w.nseg_stride = nseg_stride;
+  return w;
+}
+
+hipError_t run_wgrad(const WgradArgs& w, hipStream_t s) {
+  const long long blocks = (long long)w.G * ((w.M + 255) / 256) * ((w.N + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)blocks), dim3(512), 0, s, w);
+  return hipGetLastError();
+}
+
+hipError_t run_bwd_epi(const GemmArgs& a, bool swiglu, int bm, int mtiles, hipStream_t s) {
+  return swiglu ? launch_bf16<EPI_SWIGLU_BWD>(a, bm, mtiles, s)
+                : launch_bf16<EPI_RELU_BWD>(a, bm, mtiles, s);
+}
+
+}  // namespace
+
+hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, const FfnBwdBuffers& b,
+                                       hipStream_t s) {
+  const bool swiglu = p.act == MOE_ACT_SWIGLU;
+  const int dff = p.d_ff, d = p.d;
+  const int bm = pick_tiles(rows_alloc / p.N).bm;
+  const int tail_rows = bm == 256 ? kTailRows : 0;
+  const int ext_rows = bm == 256 ? kExtRows : 0;
+  const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N + (tail_rows > 0 ? p.N : 0);
+  int32_t* tiles = b.tiles;
+  int32_t* tails = tiles + (p.N + 2);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, b.offsets, p.N, bm, tail_rows,
+                     ext_rows, tiles, tails);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // routed experts: dA = dY W_down
+  GemmArgs base{};
+  base.offsets = b.offsets;
+  base.tiles = tiles;
+  base.tails = tails;
+  base.tail_rows = tail_rows;
+  base.ext_rows = ext_rows;
+  base.G = p.N;
+  base.rows_alloc = rows_alloc;
+  GemmArgs n1 = base;
+  n1.A = b.dy_perm;
+  n1.lda = d;
+  n1.B0 = b.w_down;
+  n1.b_group_stride = (size_t)d * dff;
+  n1.ldb = dff;
+  n1.Kdim = d;
+  n1.kseg = d;
+  n1.Ndim = dff;
+  n1.C = b.dA;
+  n1.ldc = dff;
+  if ((e = launch_bf16<EPI_NONE, true>(n1, bm, mtiles_max, s)) != hipSuccess) return e;
+  // GEMM-1 again, backward epilogue: a and [dG dU]
+  GemmArgs r1 = base;
+  r1.A = b.x_perm;
+  r1.lda = d;
+  r1.B0 = b.w_gate;
+  r1.B1 = b.w_up;
+  r1.b_group_stride = (size_t)dff * d;
+  r1.ldb = d;
+  r1.Kdim = d;
+  r1.kseg = d;
+  r1.Ndim = dff;
+  r1.C = b.act;
+  r1.ldc = dff;
+  r1.D = b.dA;
+  r1.ldd = dff;
+  r1.C2 = b.dgu;
+  r1.ldc2 = swiglu ? 2 * dff : dff;
+  if ((e = run_bwd_epi(r1, swiglu, bm, mtiles_max, s)) != hipSuccess) return e;
+  // dX = [dG dU] [W_gate; W_up]
+  GemmArgs n2 = base;
+  n2.A = b.dgu;
+  n2.lda = swiglu ? 2 * dff : dff;
+  n2.B0 = b.w_gate;
+  n2.B1 = b.w_up;
+  n2.b_group_stride = (size_t)dff * d;
+  n2.ldb = d;
+  n2.Kdim = swiglu ? 2 * dff : dff;
+  n2.kseg = dff;
+  n2.Ndim = d;
+  n2.C = b.dx_perm;
+  n2.ldc = d;
+  if ((e = launch_bf16<EPI_NONE, true>(n2, bm, mtiles_max, s)) != hipSuccess) return e;
+  // weight gradients
+  if ((e = run_wgrad(wgrad_args(b.dy_perm, d, b.act, dff, b.offsets, p.N, 0, d, dff, b.dw_down,
+                                nullptr, d, (size_t)d * dff, dff, dff, 0),
+                     s)) != hipSuccess)
+    return e;
+  if ((e = run_wgrad(wgrad_args(b.dgu, swiglu ? 2 * dff : dff, b.x_perm, d, b.offsets, p.N, 0,
+                                swiglu ? 2 * dff : dff, d, b.dw_gate, b.dw_up, dff,
+                                (size_t)dff * d, d, d, 0),
+                     s)) != hipSuccess)
+    return e;
+
+  if (p.n_shared == 0) return hipSuccess;
+  // shared experts over all T tokens, dY = d_out
+  const int dffs = p.d_ff_shared, wsw = p.n_shared * dffs;
+  const int sbm = pick_tiles(p.T).bm;
+  const int s_tail = sbm == 256 ? kTailRows : 0;
+  const int s_ext = sbm == 256 ? kExtRows : 0;
+  int mt = (p.T + sbm - 1) / sbm;
+  if (s_tail > 0) {
+    int f, t;
+    split_rows(p.T, sbm, s_tail, s_ext, f, t);
+    mt = f + t;
+  }
+  GemmArgs sb{};
+  sb.G = 1;
+  sb.M = p.T;
+  sb.rows_alloc = p.T;
+  sb.tail_rows = s_tail;
+  sb.ext_rows = s_ext;
+  for (int k = 0; k < p.n_shared; ++k) {
+    GemmArgs a1 = sb;
+    a1.A = b.d_out;
+    a1.lda = d;
+    a1.B0 = static_cast<const uint16_t*>(b.ws_down) + (size_t)k * d * dffs;
+    a1.ldb = dffs;
+    a1.Kdim = d;
+    a1.kseg = d;
+    a1.Ndim = dffs;
+    a1.C = static_cast<uint16_t*>(b.dA_s) + (size_t)k * dffs;
+    a1.ldc = wsw;
+    if ((e = launch_bf16<EPI_NONE, true>(a1, sbm, mt, s)) != hipSuccess) return e;
+  }
+  GemmArgs sr = sb;
+  sr.A = b.u;
+  sr.lda = d;
+  sr.B0 = b.ws_gate;
+  sr.B1 = b.ws_up;
+  sr.ldb = d;
+  sr.Kdim = d;
+  sr.kseg = d;
+  sr.Ndim = wsw;
+  sr.C = b.act_s;
+  sr.ldc = wsw;
+  sr.D = b.dA_s;
+  sr.ldd = wsw;
+  sr.C2 = b.dgu_s;
+  sr.ldc2 = swiglu ? 2 * wsw : wsw;
+  if ((e = run_bwd_epi(sr, swiglu, sbm, mt, s)) != hipSuccess) return e;
+  GemmArgs s2 = sb;
+  s2.A = b.dgu_s;
+  s2.lda = swiglu ? 2 * wsw : wsw;
+  s2.B0 = b.ws_gate;
+  s2.B1 = b.ws_up;
+  s2.ldb = d;
+  s2.Kdim = swiglu ? 2 * wsw : wsw;
+  s2.kseg = wsw;
+  s2.Ndim = d;
+  s2.C = b.dx_shared;
+  s2.ldc = d;
+  if ((e = launch_bf16<EPI_NONE, true>(s2, sbm, mt, s)) != hipSuccess) return e;
+  if ((e = run_wgrad(wgrad_args(b.d_out, d, b.act_s, wsw, nullptr, 1, p.T, d, wsw, b.dws_down,
+                                nullptr, d, 0, dffs, dffs, (size_t)d * dffs),
+                     s)) != hipSuccess)
+    return e;
+  return run_wgrad(wgrad_args(b.dgu_s, swiglu ? 2 * wsw : wsw, b.u, d, nullptr, 1, p.T,
+                              swiglu ? 2 * wsw : wsw, d, b.dws_gate, b.dws_up, wsw, 0, d, d, 0),
+                   s);
 }
 
 }  // namespace moe

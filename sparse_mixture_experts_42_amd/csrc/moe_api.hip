@@ -64,6 +64,37 @@ EcWorkspace ec_workspace_layout(const moe_problem_t& p) {
   return w;
 }
 
+BwdWorkspace bwd_workspace_layout(const moe_problem_t& p) {
+  BwdWorkspace w{};
+  const size_t T = (size_t)p.T, N = (size_t)p.N, K = (size_t)p.K, d = (size_t)p.d;
+  const size_t rows = T * K, dff = (size_t)p.d_ff, es = 2;
+  const size_t gu = p.act == MOE_ACT_SWIGLU ? 2 : 1;
+  const size_t wsw = (size_t)p.n_shared * p.d_ff_shared;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, kAlign);
+    return at;
+  };
+  w.tiles = take(2 * (N + 2) * 4);
+  w.dy_perm = take(rows * d * es);
+  w.dA = take(rows * dff * es);
+  w.act = take(rows * dff * es);
+  w.dgu = take(rows * gu * dff * es);
+  w.dx_perm = take(rows * d * es);
+  w.d_gate = take(T * K * 4);
+  w.dH = take(T * N * 4);
+  w.partial = take((size_t)router_grad_slices(p.T) * N * (d + 1) * 4);
+  if (p.n_shared > 0) {
+    w.dA_s = take(T * wsw * es);
+    w.act_s = take(T * wsw * es);
+    w.dgu_s = take(T * gu * wsw * es);
+    w.dx_shared = take(T * d * es);
+  }
+  w.total = off;
+  return w;
+}
+
 }  // namespace moe
 
 using moe::Workspace;
@@ -322,6 +353,123 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(*p, u, o->y_perm, o->row_of, o->topk_gate, ysh, out, s);
   return hip_status(e);
+}
+
+// ------------------------------------------------------------ backward
+
+namespace {
+
+// backward-specific limits: bf16 only; every operand a buffer descriptor
+// addresses (a group's rows of the widest row-major operand) under 4 GB
+int check_backward_problem(const moe_problem_t* p) {
+  MOE_TRY(check_problem(p));
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  long long ld = p->d;
+  const long long gu = p->act == MOE_ACT_SWIGLU ? 2 : 1;
+  if (gu * p->d_ff > ld) ld = gu * p->d_ff;
+  if (gu * p->n_shared * (long long)p->d_ff_shared > ld) ld = gu * p->n_shared * (long long)p->d_ff_shared;
+  if ((long long)p->T * ld * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+size_t moe_backward_workspace_size(const moe_problem_t* p) {
+  if (check_backward_problem(p) != MOE_OK || p->T == 0) return 0;
+  return moe::bwd_workspace_layout(*p).total;
+}
+
+int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_t* w,
+                       const moe_saved_t* sv, const void* d_out, moe_grads_t* g, void* ws,
+                       size_t ws_bytes, void* stream) {
+  MOE_TRY(check_backward_problem(p));
+  if (p->T == 0) return MOE_OK;
+  if (w == nullptr || sv == nullptr || g == nullptr) return MOE_ERR_INVALID_ARG;
+  const bool swiglu = p->act == MOE_ACT_SWIGLU;
+  const bool shared = p->n_shared > 0;
+  MOE_TRY(need(u, 16));
+  MOE_TRY(need(d_out, 16));
+  MOE_TRY(need(w->w_router, 16));
+  MOE_TRY(need(w->w_gate, 16));
+  MOE_TRY(need(w->w_down, 16));
+  if (swiglu) MOE_TRY(need(w->w_up, 16));
+  if (p->gating == MOE_GATE_SOFTMAX_TOPK) MOE_TRY(need(sv->scores, 4));
+  else MOE_TRY(maybe(sv->scores, 4));
+  MOE_TRY(need(sv->topk_idx, 4));
+  MOE_TRY(need(sv->topk_gate, 4));
+  MOE_TRY(need(sv->row_of, 4));
+  MOE_TRY(need(sv->offsets, 4));
+  MOE_TRY(need(sv->x_perm, 16));
+  MOE_TRY(need(sv->y_perm, 16));
+  MOE_TRY(need(g->du, 16));
+  MOE_TRY(need(g->dw_router, 4));
+  MOE_TRY(maybe(g->db_router, 4));
+  MOE_TRY(need(g->dw_gate, 16));
+  MOE_TRY(need(g->dw_down, 16));
+  if (swiglu) MOE_TRY(need(g->dw_up, 16));
+  if (shared) {
+    MOE_TRY(need(w->ws_gate, 16));
+    MOE_TRY(need(w->ws_down, 16));
+    MOE_TRY(need(g->dws_gate, 16));
+    MOE_TRY(need(g->dws_down, 16));
+    if (swiglu) {
+      MOE_TRY(need(w->ws_up, 16));
+      MOE_TRY(need(g->dws_up, 16));
+    }
+  }
+  MOE_TRY(maybe(g->d_gate, 4));
+  MOE_TRY(maybe(g->d_scores, 4));
+  MOE_TRY(maybe(g->dy_perm, 16));
+  MOE_TRY(maybe(g->dx_perm, 16));
+  const moe::BwdWorkspace L = moe::bwd_workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, L.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* d_gate = g->d_gate ? g->d_gate : reinterpret_cast<float*>(ws_at(ws, L.d_gate));
+  float* dH = g->d_scores ? g->d_scores : reinterpret_cast<float*>(ws_at(ws, L.dH));
+  void* dy = g->dy_perm ? g->dy_perm : ws_at(ws, L.dy_perm);
+  void* dx = g->dx_perm ? g->dx_perm : ws_at(ws, L.dx_perm);
+
+  hipError_t e = moe::launch_combine_backward(*p, d_out, sv->y_perm, sv->row_of, sv->topk_gate,
+                                               dy, d_gate, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_route_backward(*p, sv->scores, sv->topk_idx, sv->topk_gate, d_gate, dH, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_router_param_grads(*p, u, dH, reinterpret_cast<float*>(ws_at(ws, L.partial)),
+                                     g->dw_router, g->db_router, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::FfnBwdBuffers b{};
+  b.offsets = sv->offsets;
+  b.x_perm = sv->x_perm;
+  b.dy_perm = dy;
+  b.w_gate = w->w_gate;
+  b.w_up = w->w_up;
+  b.w_down = w->w_down;
+  b.tiles = reinterpret_cast<int32_t*>(ws_at(ws, L.tiles));
+  b.dA = ws_at(ws, L.dA);
+  b.act = ws_at(ws, L.act);
+  b.dgu = ws_at(ws, L.dgu);
+  b.dx_perm = dx;
+  b.dw_gate = g->dw_gate;
+  b.dw_up = g->dw_up;
+  b.dw_down = g->dw_down;
+  if (shared) {
+    b.u = u;
+    b.d_out = d_out;
+    b.ws_gate = w->ws_gate;
+    b.ws_up = w->ws_up;
+    b.ws_down = w->ws_down;
+    b.dA_s = ws_at(ws, L.dA_s);
+    b.act_s = ws_at(ws, L.act_s);
+    b.dgu_s = ws_at(ws, L.dgu_s);
+    b.dx_shared = ws_at(ws, L.dx_shared);
+    b.dws_gate = g->dws_gate;
+    b.dws_up = g->dws_up;
+    b.dws_down = g->dws_down;
+  }
+  e = moe::launch_grouped_ffn_backward(*p, p->T * p->K, b, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_du(*p, dH, w->w_router, d_out, dx, sv->row_of,
+                                   shared ? b.dx_shared : nullptr, g->du, s));
 }
 
 // ------------------------------------------------------------ expert choice

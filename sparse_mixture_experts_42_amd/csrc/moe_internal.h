@@ -79,6 +79,64 @@ hipError_t launch_combine(const moe_problem_t& p, const void* u, const void* y_p
                           const int32_t* row_of, const float* topk_gate,
                           const void* y_shared, void* out, hipStream_t s);
 
+// backward of the expert FFNs (grouped_gemm.hip); every pointer is device
+// memory, elem typed unless noted, shapes per the layer's problem
+struct FfnBwdBuffers {
+  const int32_t* offsets;   // [N+1] expert row offsets of the forward
+  const void* x_perm;       // [rows][d]     forward rows
+  const void* dy_perm;      // [rows][d]     gradients of the expert outputs
+  const void *w_gate, *w_up, *w_down;
+  int32_t* tiles;           // [2][N+2] workspace
+  void* dA;                 // [rows][d_ff]  workspace
+  void* act;                // [rows][d_ff]  workspace
+  void* dgu;                // [rows][2*d_ff] workspace (ReLU: [rows][d_ff])
+  void* dx_perm;            // [rows][d]     gradients of the rows
+  void *dw_gate, *dw_up, *dw_down;
+  // shared experts (n_shared > 0)
+  const void* u;            // [T][d]
+  const void* d_out;        // [T][d]
+  const void *ws_gate, *ws_up, *ws_down;
+  void* dA_s;               // [T][n_shared*d_ff_shared] workspace
+  void* act_s;              // [T][n_shared*d_ff_shared] workspace
+  void* dgu_s;              // [T][2*n_shared*d_ff_shared] workspace
+  void* dx_shared;          // [T][d]
+  void *dws_gate, *dws_up, *dws_down;
+};
+hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc,
+                                       const FfnBwdBuffers& b, hipStream_t s);
+
+// backward, apart from the expert GEMMs (backward.hip)
+int router_grad_slices(int T);
+hipError_t launch_combine_backward(const moe_problem_t& p, const void* d_out, const void* y_perm,
+                                   const int32_t* row_of, const float* gate, void* dy_perm,
+                                   float* d_gate, hipStream_t s);
+hipError_t launch_route_backward(const moe_problem_t& p, const float* scores,
+                                 const int32_t* topk_idx, const float* gate, const float* d_gate,
+                                 float* dH, hipStream_t s);
+hipError_t launch_router_param_grads(const moe_problem_t& p, const void* u, const float* dH,
+                                     float* partial, float* dw_router, float* db_router,
+                                     hipStream_t s);
+hipError_t launch_du(const moe_problem_t& p, const float* dH, const float* w_router,
+                     const void* d_out, const void* dx_perm, const int32_t* row_of,
+                     const void* dx_shared, void* du, hipStream_t s);
+
+struct BwdWorkspace {
+  size_t tiles;        // int32 [2][N+2]
+  size_t dy_perm;      // elem [T*K][d]
+  size_t dA;           // elem [T*K][d_ff]
+  size_t act;          // elem [T*K][d_ff]
+  size_t dgu;          // elem [T*K][2*d_ff] (ReLU: d_ff)
+  size_t dx_perm;      // elem [T*K][d]
+  size_t d_gate;       // fp32 [T][K]
+  size_t dH;           // fp32 [T][N]
+  size_t partial;      // fp32 [slices][N][d+1]
+  size_t dA_s, act_s;  // elem [T][n_shared*d_ff_shared]
+  size_t dgu_s;        // elem [T][2*n_shared*d_ff_shared]
+  size_t dx_shared;    // elem [T][d]
+  size_t total;
+};
+BwdWorkspace bwd_workspace_layout(const moe_problem_t& p);
+
 // expert choice (expert_choice.hip)
 hipError_t launch_ec_select(const moe_problem_t& p, const float* scores, int32_t C,
                             float* probsT, int32_t* expert_tokens, float* expert_gates,

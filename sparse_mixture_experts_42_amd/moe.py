@@ -52,6 +52,17 @@ class MoeEcOutputs(ctypes.Structure):
                  "offsets", "mean_prob", "lse_sq", "x_perm", "y_perm", "y_shared")]
 
 
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("scores", "topk_idx", "topk_gate", "row_of", "offsets", "x_perm", "y_perm")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("du", "dw_router", "db_router", "dw_gate", "dw_up", "dw_down", "dws_gate",
+                 "dws_up", "dws_down", "d_gate", "d_scores", "dy_perm", "dx_perm")]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn}: {moe_status_string(status)}")
@@ -97,9 +108,14 @@ def lib() -> ctypes.CDLL:
             L.moe_ec_combine.argtypes = [P] + [vp] * 7
             L.moe_ec_layer_forward.argtypes = [P, vp, vp, ctypes.POINTER(MoeWeights),
                                                ctypes.POINTER(MoeEcOutputs), vp, vp, sz, vp]
+            L.moe_backward_workspace_size.argtypes = [P]
+            L.moe_backward_workspace_size.restype = sz
+            L.moe_layer_backward.argtypes = [P, vp, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeSaved),
+                                             vp, ctypes.POINTER(MoeGrads), vp, sz, vp]
             for f in ("moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
                       "moe_layer_forward", "moe_router_stats", "moe_ec_route",
-                      "moe_ec_dispatch", "moe_ec_combine", "moe_ec_layer_forward"):
+                      "moe_ec_dispatch", "moe_ec_combine", "moe_ec_layer_forward",
+                      "moe_layer_backward"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -458,3 +474,81 @@ def ec_layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], wan
     bufs = EcBuffers(p, u.device, want_scores)
     moe_ec_layer_forward(p, u, x.get("noise"), w, bufs)
     return bufs.t
+
+
+# ------------------------------------------------------------------ backward
+
+def moe_backward_workspace_size(p: MoeProblem) -> int:
+    return int(lib().moe_backward_workspace_size(ctypes.byref(p)))
+
+
+_bwd_ws_cache: Dict[int, torch.Tensor] = {}
+
+
+def backward_workspace(p: MoeProblem, device) -> torch.Tensor:
+    """A cached workspace buffer (uint8) big enough for moe_layer_backward of p."""
+    n = max(moe_backward_workspace_size(p), 256)
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    buf = _bwd_ws_cache.get(key)
+    if buf is None or buf.numel() < n:
+        _bwd_ws_cache.pop(key, None)
+        buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        _bwd_ws_cache[key] = buf
+    return buf
+
+
+def saved_of(fwd: Dict[str, torch.Tensor]) -> MoeSaved:
+    """The forward outputs the backward reads (LayerBuffers.t or layer_forward's dict)."""
+    ptr = lambda n: None if fwd.get(n) is None else fwd[n].data_ptr()
+    return MoeSaved(*[ptr(n) for n, _ in MoeSaved._fields_])
+
+
+class BwdBuffers:
+    """Gradients (and, if asked, the intermediates d_gate, d_scores, dy_perm,
+    dx_perm) of moe_layer_backward."""
+
+    def __init__(self, p: MoeProblem, device, intermediates=True):
+        et = TORCH_DTYPE[p.dtype]
+        e = lambda shape, dt: _empty(shape, dt, device)
+        relu = p.act == MOE_ACT_RELU
+        sh = p.n_shared > 0
+        f32 = torch.float32
+        self.t = dict(
+            du=e((p.T, p.d), et), dw_router=e((p.N, p.d), f32), db_router=e((p.N,), f32),
+            dw_gate=e((p.N, p.d_ff, p.d), et), dw_up=None if relu else e((p.N, p.d_ff, p.d), et),
+            dw_down=e((p.N, p.d, p.d_ff), et),
+            dws_gate=e((p.n_shared, p.d_ff_shared, p.d), et) if sh else None,
+            dws_up=e((p.n_shared, p.d_ff_shared, p.d), et) if sh and not relu else None,
+            dws_down=e((p.n_shared, p.d, p.d_ff_shared), et) if sh else None,
+            d_gate=e((p.T, p.K), f32) if intermediates else None,
+            d_scores=e((p.T, p.N), f32) if intermediates else None,
+            dy_perm=e((p.T * p.K, p.d), et) if intermediates else None,
+            dx_perm=e((p.T * p.K, p.d), et) if intermediates else None)
+        self.c = MoeGrads(*[None if self.t[n] is None else self.t[n].data_ptr()
+                            for n, _ in MoeGrads._fields_])
+
+
+def moe_layer_backward(p: MoeProblem, u, weights: MoeWeights, fwd: Dict[str, torch.Tensor], d_out,
+                       bufs: BwdBuffers, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """The backward pass into preallocated gradient buffers; fwd holds the
+    forward's outputs (scores may be None for top-K-then-softmax gating)."""
+    dev = u.device
+    et = TORCH_DTYPE[p.dtype]
+    _check(u, "u", (p.T, p.d), et, dev)
+    _check(d_out, "d_out", (p.T, p.d), et, dev)
+    saved = saved_of(fwd)
+    ws = backward_workspace(p, dev) if ws is None else ws
+    _call("moe_layer_backward", ctypes.byref(p), _ptr(u), ctypes.byref(weights), ctypes.byref(saved),
+          _ptr(d_out), ctypes.byref(bufs.c), _ptr(ws), ws.numel(), _stream(dev))
+    return bufs.t
+
+
+def layer_backward(p: MoeProblem, x: Dict[str, Optional[torch.Tensor]], fwd: Dict[str, torch.Tensor],
+                   d_out, intermediates=True) -> Dict[str, torch.Tensor]:
+    """Convenience: allocate gradients and run the backward on workload
+    tensors x (on the GPU) and the forward outputs fwd."""
+    w = make_weights(p, x["w_router"], x.get("b_router"), x["w_gate"], x.get("w_up"), x["w_down"],
+                     x.get("ws_gate"), x.get("ws_up"), x.get("ws_down"))
+    bufs = BwdBuffers(p, x["u"].device, intermediates)
+    return moe_layer_backward(p, x["u"], w, fwd, d_out, bufs)

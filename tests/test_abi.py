@@ -234,3 +234,39 @@ def test_ec_entry_points_check_before_launch():
     assert L.moe_ec_layer_forward(P, f(1), None, ctypes.byref(w), ctypes.byref(o), f(2), f(3), need - 256, None) == M.MOE_ERR_WORKSPACE
     o.y_shared = None
     assert L.moe_ec_layer_forward(P, f(1), None, ctypes.byref(w), ctypes.byref(o), f(2), f(3), need, None) == M.MOE_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ backward
+
+def test_backward_workspace_size():
+    assert M.moe_backward_workspace_size(good(T=0)) == 0
+    assert M.moe_backward_workspace_size(good(dtype="f32")) == 0       # bf16 only
+    a = M.moe_backward_workspace_size(good(T=1000))
+    # dY, dA, a, [dG dU] and dX rows: (d + d_ff + d_ff + 2 d_ff + d) per row
+    assert a >= 1000 * 2 * (128 + 4 * 192 + 128) * 2 and a % 256 == 0
+    assert M.moe_backward_workspace_size(good(T=1000, n_shared=1, d_ff_shared=128)) > a
+
+
+def test_backward_checks_before_launch():
+    L = M.lib()
+    f = fake
+    p = good(gating="softmax_topk", n_shared=1, d_ff_shared=128)
+    P = ctypes.byref(p)
+    w = M.MoeWeights(*[FAKE + 4096 * i for i in range(8)])
+    sv = M.MoeSaved(*[FAKE + 4096 * (20 + i) for i in range(7)])
+    g = M.MoeGrads(*[FAKE + 4096 * (40 + i) for i in range(13)])
+    need = M.moe_backward_workspace_size(p)
+    call = lambda pp, ww, ss, gg, wsb: L.moe_layer_backward(ctypes.byref(pp), f(1), ww, ss, f(2), gg,
+                                                             f(3), wsb, None)
+    W_, S_, G_ = ctypes.byref(w), ctypes.byref(sv), ctypes.byref(g)
+    assert call(good(dtype="f32"), W_, S_, G_, need) == M.MOE_ERR_UNSUPPORTED
+    assert call(good(K=0), W_, S_, G_, need) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_backward(P, f(1), None, S_, f(2), G_, f(3), need, None) == M.MOE_ERR_INVALID_ARG
+    assert call(p, W_, S_, G_, need - 256) == M.MOE_ERR_WORKSPACE
+    sv.scores = None      # softmax over all experts needs the scores
+    assert call(p, W_, S_, G_, need) == M.MOE_ERR_INVALID_ARG
+    q = good(gating="topk_softmax", n_shared=1, d_ff_shared=128)
+    assert call(q, W_, S_, G_, M.moe_backward_workspace_size(q) - 256) == M.MOE_ERR_WORKSPACE
+    g.dws_down = None     # shared experts need their gradients
+    assert call(q, W_, S_, G_, 1 << 40) == M.MOE_ERR_INVALID_ARG
+    assert call(good(T=0), W_, S_, G_, 0) == M.MOE_OK
