@@ -66,6 +66,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-expert-choice", action="store_true",
                     help="skip the expert-choice pass timed after the token-choice one")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward pass timed after the forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device three times (a transfer of "
                          "known size, to scale HBM byte counters)")
@@ -97,7 +99,7 @@ def main():
     xg = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
     weights = M.make_weights(p, xg["w_router"], xg["b_router"], xg["w_gate"], xg["w_up"],
                              xg["w_down"], xg["ws_gate"], xg["ws_up"], xg["ws_down"])
-    bufs = M.LayerBuffers(p, dev, want_scores=False)
+    bufs = M.LayerBuffers(p, dev, want_scores=w.gating == "softmax_topk")
     ws = M.workspace(p, dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -255,6 +257,40 @@ def main():
               "note": "moe_ec_layer_forward on the same batch and weights, HIP-event time per pass"}
         del ecb, ecws
 
+    # ---- backward pass on the same batch (gradients of every parameter)
+    bwd = None
+    if not args.no_backward and w.dtype == "bf16":
+        g = torch.Generator().manual_seed(w.seed + 1)
+        d_out = torch.randn(w.T, w.d, generator=g).to(torch.bfloat16).to(dev)
+        bb = M.BwdBuffers(p, dev, intermediates=False)
+        bws = M.backward_workspace(p, dev)
+        saved = M.saved_of(bufs.t)
+        bwd_args = (P, vp(xg["u"]), ctypes.byref(weights), ctypes.byref(saved), vp(d_out),
+                    ctypes.byref(bb.c), vp(bws), bws.numel(), sp)
+        if bufs.t["scores"] is None and w.gating == "softmax_topk":
+            raise RuntimeError("the backward of softmax-over-all gating needs the scores")
+        for _ in range(2):
+            L.moe_layer_backward(*bwd_args)
+        n = max(args.steps, 10)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            st = L.moe_layer_backward(*bwd_args)
+            if st != 0:
+                raise RuntimeError(f"moe_layer_backward: {M.moe_status_string(st)}")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / n
+        gu = 2 if w.act == "swiglu" else 1
+        # dA, recomputed GEMM-1, dX, dW_down, dW_gate/up: 2*R*d*d_ff*(1 + gu + gu + 1 + gu)
+        bflops = 2.0 * R * w.d * w.d_ff * (2 + 3 * gu)
+        bflops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * (2 + 3 * gu)
+        log(f"backward: {bwd_ms:.3f} ms per pass, {bflops / (bwd_ms * 1e-3) / 1e12:.1f} TFLOP/s in its GEMMs")
+        bwd = {"ms_per_step": round(bwd_ms, 4), "tokens_per_s": round(w.T / (bwd_ms * 1e-3), 1),
+               "gemm_flops": bflops, "gemm_tflops_over_pass": round(bflops / (bwd_ms * 1e-3) / 1e12, 1),
+               "note": "moe_layer_backward (all gradients) on the same batch, HIP-event time per pass"}
+        del bb, bws
+
     # ---- roofline of the grouped expert GEMMs (algorithmic flops per call)
     mults = 3 if w.act == "swiglu" else 2
     flops = 2.0 * R * w.d * w.d_ff * mults
@@ -334,6 +370,7 @@ def main():
                                    "for a transfer of the combine stage's size"},
         "cpu_baseline": cpu,
         "expert_choice": ec,
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
 

@@ -129,52 +129,59 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float* scores, con
   }
 }
 
-// Router parameter gradients, first level: for a slice of kRouterTok tokens
-// and 64 columns j of [u | 1], partial[s][i][j] = sum_t dH[t][i] u'[t][j]
-// (u'[t][d] = 1 gives the bias gradient).  Thread (c, eg) owns column c and
-// experts eg, eg+4, ...; tokens are staged 32 at a time through LDS.
+// Router parameter gradients, first level: for a slice of kRouterTok tokens,
+// partial[s][i][j] = sum_t dH[t][i] u'[t][j] over the columns j of [u | 1]
+// (u'[t][d] = 1 gives the bias gradient).  A 64-expert x 64-column tile per
+// block, 4x4 per thread; dH and u' go through LDS 32 tokens at a time.
 constexpr int kRouterTok = 512;
 
 __global__ __launch_bounds__(256) void router_dw_partial_kernel(const uint16_t* u, const float* dH,
                                                                 float* partial, int T, int d,
                                                                 int N) {
-  __shared__ float sdH[32][257];
-  __shared__ float su[32][64];
-  const int c = threadIdx.x & 63, eg = threadIdx.x >> 6;
-  const int j0 = blockIdx.x * 64, s = blockIdx.y;
+  __shared__ float sH[32][65];
+  __shared__ float sU[32][64];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int j0 = blockIdx.x * 64, e0 = blockIdx.z * 64, s = blockIdx.y;
   const int t_begin = s * kRouterTok;
   const int t_end = t_begin + kRouterTok < T ? t_begin + kRouterTok : T;
-  float acc[64];
+  float acc[4][4];
 #pragma unroll
-  for (int q = 0; q < 64; ++q) acc[q] = 0.0f;
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
   for (int t0 = t_begin; t0 < t_end; t0 += 32) {
     __syncthreads();
-    for (int i = threadIdx.x; i < 32 * N; i += 256) {
-      const int tt = i / N, e = i - tt * N;
-      sdH[tt][e] = t0 + tt < t_end ? dH[(size_t)(t0 + tt) * N + e] : 0.0f;
-    }
     for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-      const int tt = i >> 6, cc = i & 63, j = j0 + cc;
+      const int tt = i >> 6, cc = i & 63;
+      const int t = t0 + tt, e = e0 + cc, j = j0 + cc;
+      sH[tt][cc] = (t < t_end && e < N) ? dH[(size_t)t * N + e] : 0.0f;
       float v = 0.0f;
-      if (t0 + tt < t_end) v = j < d ? bf16_to_f32(u[(size_t)(t0 + tt) * d + j]) : (j == d ? 1.0f : 0.0f);
-      su[tt][cc] = v;
+      if (t < t_end) v = j < d ? bf16_to_f32(u[(size_t)t * d + j]) : (j == d ? 1.0f : 0.0f);
+      sU[tt][cc] = v;
     }
     __syncthreads();
+#pragma unroll 8
     for (int tt = 0; tt < 32; ++tt) {
-      const float uv = su[tt][c];
+      float hv[4], uv[4];
 #pragma unroll
-      for (int q = 0; q < 64; ++q) {
-        const int e = eg + 4 * q;
-        if (e < N) acc[q] = fmaf(sdH[tt][e], uv, acc[q]);
-      }
+      for (int a = 0; a < 4; ++a) hv[a] = sH[tt][4 * ty + a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) uv[b] = sU[tt][4 * tx + b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(hv[a], uv[b], acc[a][b]);
     }
   }
-  const int j = j0 + c;
-  if (j > d) return;
 #pragma unroll
-  for (int q = 0; q < 64; ++q) {
-    const int e = eg + 4 * q;
-    if (e < N) partial[((size_t)s * N + e) * (d + 1) + j] = acc[q];
+  for (int a = 0; a < 4; ++a) {
+    const int e = e0 + 4 * ty + a;
+    if (e >= N) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + 4 * tx + b;
+      if (j <= d) partial[((size_t)s * N + e) * (d + 1) + j] = acc[a][b];
+    }
   }
 }
 
@@ -298,7 +305,8 @@ hipError_t launch_router_param_grads(const moe_problem_t& p, const void* u, cons
                                      float* partial, float* dw_router, float* db_router,
                                      hipStream_t s) {
   const int slices = router_grad_slices(p.T);
-  hipLaunchKernelGGL(router_dw_partial_kernel, dim3((p.d + 1 + 63) / 64, slices), dim3(256), 0, s,
+  hipLaunchKernelGGL(router_dw_partial_kernel, dim3((p.d + 1 + 63) / 64, slices, (p.N + 63) / 64),
+                     dim3(256), 0, s,
                      static_cast<const uint16_t*>(u), dH, partial, p.T, p.d, p.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
