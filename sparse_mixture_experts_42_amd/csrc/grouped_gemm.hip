@@ -237,7 +237,7 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 // voffset (bytes, from the tile's first row and column) of direct load q of
 // a k-major tile: the instruction fills LDS rows 2q and 2q+1; lane l writes
 // slot l%32 of row 2q + l/32, which holds chunk (l%32) ^ 4*(row%4).
-__device__ __forceinline__ uint32_t kmajor_voff(int q, int lane, int ld) {
+__host__ __device__ inline uint32_t kmajor_voff(int q, int lane, int ld) {
   const int r = 2 * q + (lane >> 5);
   const int c = (lane & 31) ^ (4 * (r & 3));
   return (uint32_t)(r * ld + c * 8) * 2u;
@@ -248,12 +248,16 @@ __device__ __forceinline__ uint32_t kmajor_voff(int q, int lane, int ld) {
 // read hands lane i element i%4 of the 8 bytes that lane 4j + i/4 of the
 // group addressed (as its j-th element), so lane s of a group addresses row
 // k0 + s/4, columns 4*(s%4) .. +3 past the group's first column.
-__device__ __forceinline__ bf16x8 read_kmajor(const char* tile, int kk, int col0, int lane) {
+__host__ __device__ inline int kmajor_read_off(int kk, int col0, int lane) {
   const int s = lane & 15;
   const int row = 16 * kk + 8 * (lane >> 5) + (s >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-  const int off = row * 512 + (((col >> 3) ^ (4 * (row & 3))) << 4) + ((col >> 2) & 1) * 8;
-  // rows row and row+4 have the same row%4, hence the same slot
+  return row * 512 + (((col >> 3) ^ (4 * (row & 3))) << 4) + ((col >> 2) & 1) * 8;
+}
+
+__device__ __forceinline__ bf16x8 read_kmajor(const char* tile, int kk, int col0, int lane) {
+  const int off = kmajor_read_off(kk, col0, lane);
+  // the second read is 4 rows further: same row%4, hence the same slot
   const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
   const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off + 4 * 512));
   const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
