@@ -17,6 +17,8 @@ Workspace workspace_layout(const moe_problem_t& p) {
   size_t off = 0;
   w.route_part = off;
   off = align_up(off + (size_t)w.route_blocks * N * 4, kAlign);
+  w.route_pre = off;
+  off = align_up(off + route_pre_bytes(p), kAlign);
   w.disp_count = off;
   off = align_up(off + (size_t)w.disp_blocks * N * 4, kAlign);
   w.disp_base = off;
@@ -48,6 +50,8 @@ EcWorkspace ec_workspace_layout(const moe_problem_t& p) {
   size_t off = 0;
   w.route_part = off;
   off = align_up(off + (size_t)w.route_blocks * N * 4, kAlign);
+  w.route_pre = off;
+  off = align_up(off + route_pre_bytes(p), kAlign);
   w.scores = off;
   off = align_up(off + T * N * 4, kAlign);
   w.tk_idx = off;
@@ -257,7 +261,9 @@ int moe_route(const moe_problem_t* p, const void* u, const float* w_router,
   return hip_status(moe::launch_route(*p, u, w_router, b_router, noise, scores, topk_idx,
                                       topk_gate, mean_prob, lse_sq,
                                       reinterpret_cast<float*>(ws_at(ws, w.route_part)),
-                                      w.route_blocks, static_cast<hipStream_t>(stream)));
+                                      w.route_blocks,
+                                      reinterpret_cast<float*>(ws_at(ws, w.route_pre)),
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int moe_dispatch(const moe_problem_t* p, const void* u, const int32_t* topk_idx,
@@ -337,7 +343,8 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
   hipError_t e = moe::launch_route(*p, u, wt->w_router, wt->b_router, noise, o->scores,
                                    o->topk_idx, o->topk_gate, o->mean_prob, o->lse_sq,
                                    reinterpret_cast<float*>(ws_at(ws, w.route_part)),
-                                   w.route_blocks, s);
+                                   w.route_blocks, reinterpret_cast<float*>(ws_at(ws, w.route_pre)),
+                                   s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int32_t C = moe_capacity(p->T, p->K, p->N, p->capacity_factor);
   e = moe::launch_dispatch(*p, u, o->topk_idx, C, o->expert_counts, o->kept_counts, o->offsets,
@@ -525,7 +532,8 @@ hipError_t ec_route_launch(const moe_problem_t* p, const void* u, const float* w
                                    reinterpret_cast<int32_t*>(ws_at(ws, w.tk_idx)),
                                    reinterpret_cast<float*>(ws_at(ws, w.tk_gate)), mean_prob,
                                    lse_sq, reinterpret_cast<float*>(ws_at(ws, w.route_part)),
-                                   w.route_blocks, s);
+                                   w.route_blocks, reinterpret_cast<float*>(ws_at(ws, w.route_pre)),
+                                   s);
   if (e != hipSuccess) return e;
   return moe::launch_ec_select(*p, sc, w.C, probs, expert_tokens, expert_gates, row_of, gate_of,
                                offsets, s);

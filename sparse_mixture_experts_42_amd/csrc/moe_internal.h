@@ -35,10 +35,15 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // Router launch shape: each block owns `tok` tokens (16, 32 or 64).
 int route_tokens_per_block(const moe_problem_t& p);
+// Few-token batches: d-slices of the split-k logits (0: fused path) and the
+// workspace they need ([slices][T][N] fp32).
+int route_pre_splits(const moe_problem_t& p);
+size_t route_pre_bytes(const moe_problem_t& p);
 constexpr int kDispatchTok = 256;   // tokens per dispatch block
 
 struct Workspace {
   size_t route_part;   // fp32 [route_blocks][N]   per-block softmax sums
+  size_t route_pre;    // fp32 [slices][T][N]       split-k logits (few tokens)
   size_t disp_count;   // int32 [disp_blocks][N]  per-block expert counts
   size_t disp_base;    // int32 [disp_blocks][N]  per-block rank base
   size_t tiles;        // int32 [2][N+2]          grouped-GEMM full and tail tile prefixes
@@ -55,7 +60,8 @@ Workspace workspace_layout(const moe_problem_t& p);
 hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_router,
                         const float* b_router, const float* noise, float* scores,
                         int32_t* topk_idx, float* topk_gate, float* mean_prob,
-                        float* lse_sq, float* part, int route_blocks, hipStream_t s);
+                        float* lse_sq, float* part, int route_blocks, float* pre,
+                        hipStream_t s);
 
 hipError_t launch_router_stats(const moe_problem_t& p, const int32_t* expert_counts,
                                const float* mean_prob, const float* lse_sq, float* stats,
@@ -149,6 +155,7 @@ hipError_t launch_ec_combine(const moe_problem_t& p, const void* u, const void* 
 
 struct EcWorkspace {
   size_t route_part;   // fp32 [route_blocks][N]
+  size_t route_pre;    // fp32 [slices][T][N]
   size_t scores;       // fp32 [T][N]      router scores when the caller keeps none
   size_t tk_idx;       // int32 [T][K]     token-choice top-K of the router (unused)
   size_t tk_gate;      // fp32 [T][K]

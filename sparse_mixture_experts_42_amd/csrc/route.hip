@@ -39,6 +39,8 @@ struct RouteArgs {
   float* topk_gate;    // [T][K]
   float* lse_sq;       // [T]
   float* part;         // [blocks][N]
+  const float* pre;    // [pre_splits][T][N] partial logits (split-k path) or null
+  int pre_splits;
   int T, d, N, K, gating;
 };
 
@@ -94,7 +96,10 @@ __device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
 // operand registers of the 16x16x4 MFMA, two 32-wide k-steps ahead.
 // The k index of MFMA step m of k-step J on lane group q is 32J + 8q + m for
 // both operands, a permutation of k, so the dot products are unchanged.
-template <typename E, int TG, int NT, int G, bool DIRECT>
+// PRE: the logits were computed by route_partial_kernel as partial sums over
+// pre_splits slices of d; the block sums the slices in slice order instead
+// of running the GEMM itself (few-token batches, see launch_route).
+template <typename E, int TG, int NT, int G, bool DIRECT, bool PRE = false>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   constexpr int NWV = 4;               // waves per block
   constexpr int TOK = 16 * TG;
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   float* sU = smem;                     // [TOK][kLd]
   float* sW = smem + TOK * kLd;         // [NP][kLd]; reused as logits [TOK][NP+1]
-  float* sL = DIRECT ? smem : sW;
+  float* sL = (DIRECT || PRE) ? smem : sW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,6 +122,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int t0 = blockIdx.x * TOK;
   const int T = a.T, d = a.d, N = a.N;
 
+  constexpr int LdL = NP + 1;
+  if constexpr (PRE) {
+    static_assert(!DIRECT, "partial logits replace the GEMM");
+    for (int i = tid; i < TOK * NP; i += kThreads) {
+      const int lt = i / NP, e = i - lt * NP;
+      const int t = t0 + lt;
+      float v = 0.0f;
+      if (t < T && e < N)
+        for (int s = 0; s < a.pre_splits; ++s) v += a.pre[((size_t)s * T + t) * N + e];
+      sL[lt * LdL + e] = v;
+    }
+    __syncthreads();
+  } else {
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -263,7 +281,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
 
   // ---- sum the k-split partial logits into sL[TOK][NP+1] (fixed order)
-  constexpr int LdL = NP + 1;
   for (int s = 0; s < KS; ++s) {
     if (ks == s) {
 #pragma unroll
@@ -276,6 +293,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     }
     __syncthreads();
   }
+  }  // !PRE
 
   // ---- softmax statistics, top-K and gates: each wave takes TOK/4 tokens
   constexpr int TPW = TOK / NWV;            // tokens per wave
@@ -391,6 +409,98 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
 }
 
+// Split-k logits for few-token batches: block (token tile, slice s, expert
+// group) computes 16 tokens x 16*NTB experts over d-slice s on the fp32
+// 16x16x4 MFMA, register-direct as in the narrow router (k permuted within
+// each 32-wide step), the 4 waves on interleaved 32-wide steps, summed over
+// the waves in wave order through LDS:  pre[s][t][e] = sum_{k in slice s}.
+template <typename E, int NTB>
+__global__ __launch_bounds__(kThreads) void route_partial_kernel(const void* u, const float* w, int T,
+                                                                 int d, int N, int dk, float* pre) {
+  __shared__ float red[4][16][16 * NTB + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, s = blockIdx.y, e0 = blockIdx.z * 16 * NTB;
+  const int q = lane >> 4;
+  const int t = t0 + (lane & 15);
+  const bool t_ok = t < T;
+  const E* urow = static_cast<const E*>(u) + (size_t)(t_ok ? t : 0) * d + 8 * q;
+  const float* wrow[NTB];
+  bool w_ok[NTB];
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const int e = e0 + 16 * j + (lane & 15);
+    w_ok[j] = e < N;
+    wrow[j] = w + (size_t)(w_ok[j] ? e : 0) * d + 8 * q;
+  }
+  f32x4 acc[NTB];
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int J0 = s * dk / 32, J1 = J0 + dk / 32;
+  for (int J = J0 + wave; J < J1; J += 4) {
+    float uv[8];
+    if constexpr (sizeof(E) == 2) {
+      const u32x4 qu = t_ok ? *reinterpret_cast<const u32x4*>(urow + 32 * J) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        uv[m] = __uint_as_float((m & 1) ? (qu[m >> 1] & 0xffff0000u) : (qu[m >> 1] << 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 qu = t_ok ? *reinterpret_cast<const u32x4*>(urow + 32 * J + 4 * i)
+                              : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) uv[4 * i + m] = __uint_as_float(qu[m]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      float wv[8];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4 v = w_ok[j] ? *reinterpret_cast<const float4*>(wrow[j] + 32 * J + 4 * i)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        wv[4 * i] = v.x;
+        wv[4 * i + 1] = v.y;
+        wv[4 * i + 2] = v.z;
+        wv[4 * i + 3] = v.w;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(uv[m], wv[m], acc[j], 0, 0, 0);
+    }
+  }
+  // lane holds tokens 4*(lane/16) + v, expert 16*j + lane%16
+#pragma unroll
+  for (int j = 0; j < NTB; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][16 * j + (lane & 15)] = acc[j][v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * 16 * NTB; i += kThreads) {
+    const int tt = i / (16 * NTB), ee = i - tt * 16 * NTB;
+    const int tok = t0 + tt, e = e0 + ee;
+    if (tok >= T || e >= N) continue;
+    const float v = ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
+    pre[((size_t)s * T + tok) * N + e] = v;
+  }
+}
+
+// The slices summed in slice order, one thread per (token, expert), eight
+// loads in flight: out[t][e] = sum_s pre[s][t][e].
+__global__ __launch_bounds__(256) void route_pre_reduce_kernel(const float* pre, int S, long long TN,
+                                                               float* out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= TN) return;
+  float acc = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = s0 + j < S ? pre[(size_t)(s0 + j) * TN + i] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+  }
+  out[i] = acc;
+}
+
 // mean_prob[i] = (sum of the per-block sums part[i][*]) / T: one block per
 // expert; thread t sums blocks t, t+256, ... in order, then a fixed tree.
 __global__ __launch_bounds__(256) void route_finalize_kernel(const float* part, int blocks, int N,
@@ -460,28 +570,37 @@ int pow2_at_least(int x) {
   return p;
 }
 
-template <typename E, int TG, int NT, int G>
+template <typename E, int TG, int NT, int G, bool PRE>
 hipError_t launch_g(const RouteArgs& a, int blocks, hipStream_t s) {
-  constexpr bool DIRECT = TG == 1 && NT <= 2;
+  constexpr bool DIRECT = !PRE && TG == 1 && NT <= 2;
   constexpr int TOK = 16 * TG, NP = 16 * NT;
   constexpr int kLd = chunk_k<TG, NT>() + 4;
   constexpr size_t stage = (size_t)(TOK + NP) * kLd * sizeof(float);
   constexpr size_t logits = (size_t)TOK * kLd * sizeof(float) + (size_t)TOK * (NP + 1) * sizeof(float);
   constexpr size_t direct = (size_t)(TOK * (NP + 1) > 4 * NP ? TOK * (NP + 1) : 4 * NP) * sizeof(float);
-  constexpr size_t lds = DIRECT ? direct : (stage > logits ? stage : logits);
+  constexpr size_t lds = (DIRECT || PRE) ? direct : (stage > logits ? stage : logits);
   static_assert(lds <= 160 * 1024, "router tile exceeds the LDS of a CU");
   if constexpr (lds > 64 * 1024) {
     static bool attr_set = false;   // once per instantiation (idempotent)
     if (!attr_set) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&route_kernel<E, TG, NT, G, DIRECT>),
+          reinterpret_cast<const void*>(&route_kernel<E, TG, NT, G, DIRECT, PRE>),
           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL((route_kernel<E, TG, NT, G, DIRECT>), dim3(blocks), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((route_kernel<E, TG, NT, G, DIRECT, PRE>), dim3(blocks), dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+
+template <typename E, int TG, int NT, int G>
+hipError_t launch_gp(const RouteArgs& a, int blocks, hipStream_t s) {
+  if (a.pre != nullptr) {
+    if constexpr (TG == 1) return launch_g<E, TG, NT, G, true>(a, blocks, s);
+    else return hipErrorInvalidValue;
+  }
+  return launch_g<E, TG, NT, G, false>(a, blocks, s);
 }
 
 // Lanes per token G: the smallest power of two >= N (at least 4, at most
@@ -489,11 +608,11 @@ hipError_t launch_g(const RouteArgs& a, int blocks, hipStream_t s) {
 template <typename E, int TG, int NT>
 hipError_t launch_gsel(const moe_problem_t& p, const RouteArgs& a, int blocks, hipStream_t s) {
   if constexpr (NT == 1) {
-    if (p.N <= 4) return launch_g<E, TG, 1, 4>(a, blocks, s);
-    if (p.N <= 8) return launch_g<E, TG, 1, 8>(a, blocks, s);
-    return launch_g<E, TG, 1, 16>(a, blocks, s);
+    if (p.N <= 4) return launch_gp<E, TG, 1, 4>(a, blocks, s);
+    if (p.N <= 8) return launch_gp<E, TG, 1, 8>(a, blocks, s);
+    return launch_gp<E, TG, 1, 16>(a, blocks, s);
   } else {
-    return launch_g<E, TG, NT, (16 * NT < 64 ? 16 * NT : 64)>(a, blocks, s);
+    return launch_gp<E, TG, NT, (16 * NT < 64 ? 16 * NT : 64)>(a, blocks, s);
   }
 }
 
@@ -522,9 +641,29 @@ hipError_t launch_tg(const moe_problem_t& p, const RouteArgs& a, int blocks, hip
 
 }  // namespace
 
+// Few-token batches (fewer than 256 tiles of 16 tokens) would leave most of
+// the chip idle with one block per 16 tokens: their logits are computed in
+// pre_splits slices of d by route_partial_kernel first (at least ~512
+// blocks), then summed by the routing blocks.  0: the fused path.
+int route_pre_splits(const moe_problem_t& p) {
+  const int tiles = (p.T + 15) / 16;
+  if (tiles >= 256 || p.T == 0) return 0;
+  const int groups = (p.N + 63) / 64;
+  int S = 1;
+  while (S < 32 && S * 2 * 32 <= p.d / 4 && p.d % (S * 2 * 32) == 0 && tiles * groups * S < 512)
+    S *= 2;
+  return S;
+}
+
+size_t route_pre_bytes(const moe_problem_t& p) {
+  const int S = route_pre_splits(p);
+  return S > 0 ? (size_t)(S + 1) * p.T * p.N * sizeof(float) : 0;
+}
+
 // Small expert counts keep the router HBM-bound: few tokens per block, many
 // blocks.  Wide routers reuse the staged router weights over more tokens.
 int route_tokens_per_block(const moe_problem_t& p) {
+  if (route_pre_splits(p) > 0) return 16;
   if (p.N <= 32) return 16;
   if ((long long)p.T >= 64LL * 256) return 64;
   if ((long long)p.T >= 32LL * 256) return 32;
@@ -534,7 +673,8 @@ int route_tokens_per_block(const moe_problem_t& p) {
 hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_router,
                         const float* b_router, const float* noise, float* scores,
                         int32_t* topk_idx, float* topk_gate, float* mean_prob,
-                        float* lse_sq, float* part, int route_blocks, hipStream_t s) {
+                        float* lse_sq, float* part, int route_blocks, float* pre,
+                        hipStream_t s) {
   RouteArgs a;
   a.u = u;
   a.w = w_router;
@@ -551,6 +691,33 @@ hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_ro
   a.N = p.N;
   a.K = p.K;
   a.gating = p.gating;
+  a.pre = nullptr;
+  a.pre_splits = route_pre_splits(p);
+  if (a.pre_splits > 0) {
+    const int S = a.pre_splits, dk = p.d / S;
+    const int nt = pow2_at_least((p.N + 15) / 16);
+    const dim3 grid((p.T + 15) / 16, S, (p.N + 63) / 64);
+    if (p.dtype == MOE_BF16) {
+      if (nt == 1) hipLaunchKernelGGL((route_partial_kernel<uint16_t, 1>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+      else if (nt == 2) hipLaunchKernelGGL((route_partial_kernel<uint16_t, 2>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+      else hipLaunchKernelGGL((route_partial_kernel<uint16_t, 4>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+    } else {
+      if (nt == 1) hipLaunchKernelGGL((route_partial_kernel<float, 1>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+      else if (nt == 2) hipLaunchKernelGGL((route_partial_kernel<float, 2>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+      else hipLaunchKernelGGL((route_partial_kernel<float, 4>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+    }
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    // the slices summed into slice S, which the routing blocks then read
+    const long long TN = (long long)p.T * p.N;
+    float* summed = pre + (size_t)S * TN;
+    hipLaunchKernelGGL(route_pre_reduce_kernel, dim3((unsigned)((TN + 255) / 256)), dim3(256), 0, s,
+                       (const float*)pre, S, TN, summed);
+    e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    a.pre = summed;
+    a.pre_splits = 1;
+  }
   hipError_t e = p.dtype == MOE_BF16 ? launch_tg<uint16_t>(p, a, route_blocks, s)
                                      : launch_tg<float>(p, a, route_blocks, s);
   if (e != hipSuccess) return e;
