@@ -241,32 +241,44 @@ void oracle_dispatch(const oracle_problem* p, const int32_t* topk_idx,
                      int32_t* kept_counts, int32_t* offsets, int32_t* row_of,
                      int32_t* token_of_row) {
   const int N = p->N, K = p->K, T = p->T;
-  int32_t* rank = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+  const size_t TK = (size_t)T * K;
+  int32_t* prio = (int32_t*)malloc(sizeof(int32_t) * (TK + 1));
+  int32_t* fill = (int32_t*)calloc((size_t)N, sizeof(int32_t));
   for (int e = 0; e < N; ++e) expert_counts[e] = 0;
-  /* first come, first served in ascending token order */
-  for (int t = 0; t < T; ++t)
-    for (int k = 0; k < K; ++k) {
-      int e = topk_idx[(size_t)t * K + k];
-      rank[(size_t)t * K + k] = expert_counts[e]++;
-    }
+  /* priority rank of each assignment within its expert: first come, first
+   * served in ascending token order, or by (choice rank, token) */
+  if (p->drop_order == OR_DROP_CHOICE_RANK) {
+    for (int k = 0; k < K; ++k)
+      for (int t = 0; t < T; ++t) {
+        int e = topk_idx[(size_t)t * K + k];
+        prio[(size_t)t * K + k] = expert_counts[e]++;
+      }
+  } else {
+    for (int t = 0; t < T; ++t)
+      for (int k = 0; k < K; ++k) {
+        int e = topk_idx[(size_t)t * K + k];
+        prio[(size_t)t * K + k] = expert_counts[e]++;
+      }
+  }
   for (int e = 0; e < N; ++e)
     kept_counts[e] = (capacity >= 0 && expert_counts[e] > capacity) ? capacity : expert_counts[e];
   offsets[0] = 0;
   for (int e = 0; e < N; ++e) offsets[e + 1] = offsets[e] + kept_counts[e];
-  for (size_t r = 0; r < (size_t)T * K; ++r) token_of_row[r] = -1;
+  for (size_t r = 0; r < TK; ++r) token_of_row[r] = -1;
+  /* the kept assignments take the expert's rows in ascending token order */
   for (int t = 0; t < T; ++t)
     for (int k = 0; k < K; ++k) {
       int e = topk_idx[(size_t)t * K + k];
-      int32_t rk = rank[(size_t)t * K + k];
-      if (capacity >= 0 && rk >= capacity) {
+      if (capacity >= 0 && prio[(size_t)t * K + k] >= capacity) {
         row_of[(size_t)t * K + k] = -1;          /* overflow: dropped */
       } else {
-        int32_t row = offsets[e] + rk;
+        int32_t row = offsets[e] + fill[e]++;
         row_of[(size_t)t * K + k] = row;
         token_of_row[row] = t;
       }
     }
-  free(rank);
+  free(prio);
+  free(fill);
 }
 
 /* ------------------------------------------------------------------ */

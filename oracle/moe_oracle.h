@@ -36,6 +36,7 @@ extern "C" {
 enum { OR_F32 = 0, OR_BF16 = 1 };                        /* storage type */
 enum { OR_GATE_SOFTMAX_TOPK = 0, OR_GATE_TOPK_SOFTMAX = 1 };
 enum { OR_ACT_SWIGLU = 0, OR_ACT_RELU = 1 };
+enum { OR_DROP_TOKEN_ORDER = 0, OR_DROP_CHOICE_RANK = 1 };   /* capacity priority */
 
 typedef struct {
   int32_t T, d, N, K, d_ff;     /* tokens, hidden width, experts, top-K, expert width */
@@ -45,6 +46,7 @@ typedef struct {
   int32_t gating;               /* OR_GATE_*                                    */
   int32_t act;                  /* OR_ACT_*                                     */
   int32_t dtype;                /* OR_F32 / OR_BF16 for u and expert weights    */
+  int32_t drop_order;           /* OR_DROP_*: which assignments a full expert keeps */
 } oracle_problem;
 
 /* All weights row-major.  Element type of u and of the expert weights is
@@ -91,11 +93,17 @@ void oracle_route(const oracle_problem* p, const float* H, int32_t* topk_idx,
  * can hold each token at most once); -1 when cf <= 0 (no limit). */
 int32_t oracle_capacity(int32_t T, int32_t K, int32_t N, float cf);
 
-/* Dispatch maps by one sequential walk over (t ascending, k ascending).
+/* Dispatch maps.  Which assignments an expert keeps when more than C choose
+ * it (p->drop_order):
+ *   OR_DROP_TOKEN_ORDER  the first C in ascending token order
+ *   OR_DROP_CHOICE_RANK  the first C in order of (choice rank k, token):
+ *                        every token's first choice before any second
+ *                        choice, and so on
+ * Kept assignments occupy the expert's rows in ascending token order.
  *   expert_counts[N]   assignments per expert before capacity
  *   kept_counts[N]     min(count, C)
  *   offsets[N+1]       exclusive prefix sum of kept_counts
- *   row_of[T][K]       offsets[e] + rank, or -1 if dropped
+ *   row_of[T][K]       offsets[e] + position among the kept, or -1 if dropped
  *   token_of_row[T*K]  inverse map; -1 past offsets[N]                   */
 void oracle_dispatch(const oracle_problem* p, const int32_t* topk_idx,
                      int32_t capacity, int32_t* expert_counts,

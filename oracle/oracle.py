@@ -17,6 +17,7 @@ from . import build as _build
 F32, BF16 = 0, 1
 GATE_SOFTMAX_TOPK, GATE_TOPK_SOFTMAX = 0, 1
 ACT_SWIGLU, ACT_RELU = 0, 1
+DROP_TOKEN_ORDER, DROP_CHOICE_RANK = 0, 1
 
 _lib = None
 
@@ -26,7 +27,8 @@ class _Problem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_float), ("noise_weight", ctypes.c_float),
-                ("gating", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("gating", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("drop_order", ctypes.c_int32)]
 
 
 class _Inputs(ctypes.Structure):
@@ -49,11 +51,12 @@ class Problem:
     gating: int = GATE_TOPK_SOFTMAX
     act: int = ACT_SWIGLU
     dtype: int = F32
+    drop_order: int = DROP_TOKEN_ORDER
 
     def c(self) -> _Problem:
         return _Problem(self.T, self.d, self.N, self.K, self.d_ff, self.n_shared,
                         self.d_ff_shared, self.capacity_factor, self.noise_weight,
-                        self.gating, self.act, self.dtype)
+                        self.gating, self.act, self.dtype, self.drop_order)
 
 
 def nthreads_default() -> int:

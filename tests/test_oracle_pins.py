@@ -643,3 +643,55 @@ def test_ec_equal_affinities_pick_lowest_tokens():
     p = O.Problem(T=T, d=64, N=N, K=1, d_ff=64)
     o = O.ec_select(p, np.full((T, N), 1.0 / N), C)
     assert (o["expert_tokens"] == np.arange(C)).all()
+
+
+# ------------------------------------------- capacity by choice rank (K > 1)
+
+def _choice_problem(T, N, K, order):
+    return O.Problem(T=T, d=64, N=N, K=K, d_ff=64, drop_order=order)
+
+
+def test_choice_rank_keeps_first_choices_worked_case():
+    """Two tokens put expert 0 second, two later tokens put it first; with
+    capacity 2, token order keeps the early second choices and drops the late
+    first choices, choice rank does the opposite; rows stay in token order."""
+    idx = np.array([[1, 0], [1, 0], [0, 1], [0, 1]], np.int32)
+    tok = O.dispatch(_choice_problem(4, 2, 2, O.DROP_TOKEN_ORDER), idx, C=2)
+    rank = O.dispatch(_choice_problem(4, 2, 2, O.DROP_CHOICE_RANK), idx, C=2)
+    # expert 0 rows 0..1, expert 1 rows 2..3
+    assert tok["row_of"].tolist() == [[2, 0], [3, 1], [-1, -1], [-1, -1]]
+    assert rank["row_of"].tolist() == [[2, -1], [3, -1], [0, -1], [1, -1]]
+    assert rank["token_of_row"][:4].tolist() == [2, 3, 0, 1]
+    assert tok["kept_counts"].tolist() == rank["kept_counts"].tolist() == [2, 2]
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.integers(1, 40), st.integers(1, 6), st.data())
+def test_choice_rank_matches_sorting(T, N, data):
+    """Each expert keeps the first C of its assignments sorted by (choice
+    rank, token); its rows hold the kept tokens in ascending order."""
+    K = data.draw(st.integers(1, N))
+    C = data.draw(st.integers(0, T))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
+    idx = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+    o = O.dispatch(_choice_problem(T, N, K, O.DROP_CHOICE_RANK), idx, C=C)
+    for e in range(N):
+        pairs = sorted((k, t) for t in range(T) for k in range(K) if idx[t, k] == e)
+        kept = sorted(t for k, t in pairs[:C])
+        assert o["kept_counts"][e] == len(kept)
+        lo = o["offsets"][e]
+        assert o["token_of_row"][lo:lo + len(kept)].tolist() == kept
+        for k, t in pairs:
+            want = lo + kept.index(t) if t in kept else -1
+            assert o["row_of"][t, k] == want
+
+
+def test_choice_rank_reduces_to_token_order():
+    """K = 1, or a capacity no expert reaches: both orders agree exactly."""
+    rng = np.random.default_rng(7)
+    for T, N, K, C in ((50, 4, 1, 5), (50, 6, 3, 50), (30, 5, 2, -1)):
+        idx = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+        a = O.dispatch(_choice_problem(T, N, K, O.DROP_TOKEN_ORDER), idx, C=C)
+        b = O.dispatch(_choice_problem(T, N, K, O.DROP_CHOICE_RANK), idx, C=C)
+        for key in ("expert_counts", "kept_counts", "offsets", "row_of", "token_of_row"):
+            assert np.array_equal(a[key], b[key]), (T, N, K, C, key)
