@@ -75,6 +75,16 @@ enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 };
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
+/* Which assignments an expert keeps when more than C choose it.
+ * MOE_DROP_TOKEN_ORDER: the first C in ascending token order (first come,
+ *   first served; "Switch Transformers explained", "Making it work").
+ * MOE_DROP_CHOICE_RANK: the first C in order of (choice rank k, token):
+ *   every token's first choice before any second choice, and so on, the
+ *   priority of top-2 gating at scale (the GShard entry of the "Mixture of
+ *   Experts (MoE)" glossary).
+ * In both, the kept assignments take the expert's rows in token order. */
+enum { MOE_DROP_TOKEN_ORDER = 0, MOE_DROP_CHOICE_RANK = 1 };
+
 typedef struct moe_problem {
   int32_t T;            /* tokens (rows of u), >= 0                           */
   int32_t d;            /* hidden width, multiple of 64                       */
@@ -88,6 +98,7 @@ typedef struct moe_problem {
   int32_t gating;       /* MOE_GATE_*                                         */
   int32_t act;          /* MOE_ACT_*                                          */
   int32_t dtype;        /* MOE_F32 or MOE_BF16                                */
+  int32_t drop_order;   /* MOE_DROP_*: priority under capacity                */
 } moe_problem_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -111,6 +111,37 @@ constexpr int kVecPerLane = 8;              // 16-byte vectors in flight per lan
 constexpr int kScanInBlock = 4096;          // chunk counts one block scans itself (16 KB)
 static_assert(kTok % kRowTok == 0, "blocks tile the mask chunks");
 
+// Copy each token row of the block (read once, 16-byte vectors, kVecPerLane
+// per lane in flight) to every kept row srow[j*16 + k]; wave w takes tokens
+// w, w+4, ... of the block.
+__device__ __forceinline__ void copy_rows(int t0, int T, int K, const int32_t* srow,
+                                          const u32x4* u, u32x4* x_perm, int vec_per_row) {
+  const int lane = threadIdx.x & 63;
+  for (int j = threadIdx.x >> 6; j < kRowTok; j += 4) {
+    const int t = t0 + j;
+    if (t >= T) break;
+    const u32x4* src = u + (size_t)t * vec_per_row;
+    for (int v0 = 0; v0 < vec_per_row; v0 += 64 * kVecPerLane) {
+      u32x4 q[kVecPerLane];
+#pragma unroll
+      for (int i = 0; i < kVecPerLane; ++i) {
+        const int v = v0 + i * 64 + lane;
+        if (v < vec_per_row) q[i] = src[v];
+      }
+      for (int k = 0; k < K; ++k) {
+        const int row = srow[j * 16 + k];
+        if (row < 0) continue;
+        u32x4* dst = x_perm + (size_t)row * vec_per_row;
+#pragma unroll
+        for (int i = 0; i < kVecPerLane; ++i) {
+          const int v = v0 + i * 64 + lane;
+          if (v < vec_per_row) dst[v] = q[i];
+        }
+      }
+    }
+  }
+}
+
 template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int32_t* topk_idx, const int32_t* blk_count, int chunks, const int32_t* blk_base,
@@ -199,31 +230,154 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     token_of_row[r] = -1;
   __syncthreads();
 
-  // copy: wave w takes tokens w, w+4, ... of the block
-  const int lane = tid & 63;
-  for (int j = tid >> 6; j < kRowTok; j += 4) {
-    const int t = t0 + j;
-    if (t >= T) break;
-    const u32x4* src = u + (size_t)t * vec_per_row;
-    for (int v0 = 0; v0 < vec_per_row; v0 += 64 * kVecPerLane) {
-      u32x4 q[kVecPerLane];
+  copy_rows(t0, T, K, srow, u, x_perm, vec_per_row);
+}
+
+// ---------------------------------------------------------------------
+// Capacity by choice rank: a full expert keeps the first C of its
+// assignments in order of (choice rank k, token), and the kept ones take its
+// rows in token order.  With q[k][e] = min(max(C - sum_{k'<k} n[k'][e], 0),
+// n[k][e]) kept at level k (n = level-k assignments to e), the kept level-k
+// assignments are the first q[k][e] of that level in token order, and the
+// row of a kept (t, k) is offsets[e] + sum_k' min(q[k'][e], rank_k'(t, e)),
+// rank_k'(t, e) = level-k' assignments to e of tokens before t.  Per-chunk
+// level masks give those ranks with the same popcounts as above.
+
+// level-k masks of a chunk: bit t of mask[e] set iff topk_idx[t][k] == e
+__device__ __forceinline__ void build_level_mask(uint32_t* mask, const int32_t* topk_idx, int T,
+                                                 int N, int K, int k, int t_local, int t) {
+  for (int i = threadIdx.x; i < N * kWords; i += kTok) mask[i] = 0u;
+  __syncthreads();
+  if (t < T) {
+    const int e = topk_idx[(size_t)t * K + k];
+    if (e >= 0 && e < N) atomicOr(&mask[e * kWords + (t_local >> 5)], 1u << (t_local & 31));
+  }
+  __syncthreads();
+}
+
+// cnt[chunk][k][e]: level-k assignments to e in the chunk
+__global__ __launch_bounds__(kTok) void dispatch_count_levels_kernel(const int32_t* topk_idx, int T,
+                                                                     int N, int K, int32_t* cnt) {
+  __shared__ uint32_t mask[256 * kWords];
+  const int tl = threadIdx.x;
+  const int t = blockIdx.x * kTok + tl;
+  for (int k = 0; k < K; ++k) {
+    build_level_mask(mask, topk_idx, T, N, K, k, tl, t);
+    for (int e = tl; e < N; e += kTok) {
+      int c = 0;
 #pragma unroll
-      for (int i = 0; i < kVecPerLane; ++i) {
-        const int v = v0 + i * 64 + lane;
-        if (v < vec_per_row) q[i] = src[v];
-      }
-      for (int k = 0; k < K; ++k) {
-        const int row = srow[j * 16 + k];
-        if (row < 0) continue;
-        u32x4* dst = x_perm + (size_t)row * vec_per_row;
+      for (int w = 0; w < kWords; ++w) c += __popc(mask[e * kWords + w]);
+      cnt[((size_t)blockIdx.x * K + k) * N + e] = c;
+    }
+    __syncthreads();
+  }
+}
+
+// One block: per (level, expert) running sums over the chunks, the kept
+// counts per level q, and the expert offsets.
+__global__ __launch_bounds__(256) void dispatch_scan_levels_kernel(
+    const int32_t* cnt, int32_t* base, int32_t* q, int chunks, int N, int K, int32_t capacity,
+    int32_t* expert_counts, int32_t* kept_counts, int32_t* offsets) {
+  __shared__ int32_t tot[16 * 256];
+  __shared__ int32_t sc[256];
+  const int tid = threadIdx.x;
+  for (int pk = tid; pk < K * N; pk += 256) {
+    int run = 0;
+    for (int c = 0; c < chunks; ++c) {
+      const size_t at = (size_t)c * K * N + pk;
+      const int v = cnt[at];
+      base[at] = run;
+      run += v;
+    }
+    tot[pk] = run;
+  }
+  __syncthreads();
+  int kept = 0;
+  if (tid < N) {
+    int cum = 0;
+    for (int k = 0; k < K; ++k) {
+      const int n = tot[k * N + tid];
+      int room = capacity - cum;
+      room = room < 0 ? 0 : room;
+      const int qk = n < room ? n : room;
+      q[k * N + tid] = qk;
+      kept += qk;
+      cum += n;
+    }
+    expert_counts[tid] = cum;
+    kept_counts[tid] = kept;
+  }
+  sc[tid] = kept;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < N) offsets[tid + 1] = sc[tid];
+  if (tid == 0) offsets[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void dispatch_permute_levels_kernel(
+    const int32_t* topk_idx, const int32_t* base, const int32_t* q, const int32_t* offsets, int T,
+    int N, int K, int32_t* row_of, int32_t* token_of_row, const u32x4* u, u32x4* x_perm,
+    int vec_per_row) {
+  __shared__ uint32_t mask[256 * kWords];
+  __shared__ int32_t srow[kRowTok * 16];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRowTok;
+  const int chunk = t0 / kTok;
+  const int t = t0 + tid;                       // token of thread tid < kRowTok
+  const bool mine = tid < kRowTok && t < T;
+  const int tl = mine ? t - chunk * kTok : 0;
+  int e_of[16], pos[16];
+  bool kept[16];
 #pragma unroll
-        for (int i = 0; i < kVecPerLane; ++i) {
-          const int v = v0 + i * 64 + lane;
-          if (v < vec_per_row) dst[v] = q[i];
-        }
+  for (int k = 0; k < 16; ++k) {
+    e_of[k] = (mine && k < K) ? topk_idx[(size_t)t * K + k] : 0;
+    pos[k] = 0;
+    kept[k] = false;
+  }
+  for (int lvl = 0; lvl < K; ++lvl) {
+    build_level_mask(mask, topk_idx, T, N, K, lvl, tid, chunk * kTok + tid);
+    if (mine) {
+      const int w0 = tl >> 5;
+      const uint32_t below = (1u << (tl & 31)) - 1u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k >= K) break;
+        const int e = e_of[k];
+        if (e < 0 || e >= N) continue;           // no such expert: never kept
+        int r = __popc(mask[e * kWords + w0] & below);
+        for (int w = 0; w < w0; ++w) r += __popc(mask[e * kWords + w]);
+        r += base[((size_t)chunk * K + lvl) * N + e];
+        const int qv = q[lvl * N + e];
+        pos[k] += r < qv ? r : qv;
+        if (k == lvl) kept[k] = r < qv;
       }
     }
+    __syncthreads();
   }
+  if (mine) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k >= K) break;
+      int32_t row = -1;
+      if (kept[k]) {
+        row = offsets[e_of[k]] + pos[k];
+        token_of_row[row] = t;
+      }
+      row_of[(size_t)t * K + k] = row;
+      srow[tid * 16 + k] = row;
+    }
+  }
+  const int64_t total = (int64_t)T * K;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t r = offsets[N] + (int64_t)blockIdx.x * 256 + tid; r < total; r += stride)
+    token_of_row[r] = -1;
+  __syncthreads();
+  copy_rows(t0, T, K, srow, u, x_perm, vec_per_row);
 }
 
 }  // namespace
@@ -232,7 +386,27 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                            int32_t capacity, int32_t* expert_counts, int32_t* kept_counts,
                            int32_t* offsets, int32_t* row_of, int32_t* token_of_row,
                            void* x_perm, int32_t* blk_count, int32_t* blk_base,
-                           int disp_blocks, hipStream_t s) {
+                           int32_t* level_q, int disp_blocks, hipStream_t s) {
+  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
+  const int vec_per_row = (int)((size_t)p.d * es / 16);
+  const unsigned blocks = (unsigned)((p.T + kRowTok - 1) / kRowTok);
+  if (p.drop_order == MOE_DROP_CHOICE_RANK && capacity >= 0 && p.K > 1) {
+    // (K = 1 or no capacity: both orders keep the same assignments)
+    hipLaunchKernelGGL(dispatch_count_levels_kernel, dim3(disp_blocks), dim3(kTok), 0, s, topk_idx,
+                       p.T, p.N, p.K, blk_count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_scan_levels_kernel, dim3(1), dim3(256), 0, s,
+                       (const int32_t*)blk_count, blk_base, level_q, disp_blocks, p.N, p.K,
+                       capacity, expert_counts, kept_counts, offsets);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_permute_levels_kernel, dim3(blocks), dim3(256), 0, s, topk_idx,
+                       (const int32_t*)blk_base, (const int32_t*)level_q, (const int32_t*)offsets,
+                       p.T, p.N, p.K, row_of, token_of_row, static_cast<const u32x4*>(u),
+                       static_cast<u32x4*>(x_perm), vec_per_row);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(disp_blocks), dim3(kTok), 0, s, topk_idx, p.T,
                      p.N, p.K, blk_count);
   hipError_t e = hipGetLastError();
@@ -244,9 +418,6 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
-  const int vec_per_row = (int)((size_t)p.d * es / 16);
-  const unsigned blocks = (unsigned)((p.T + kRowTok - 1) / kRowTok);
   if (scan_in_block)
     hipLaunchKernelGGL(dispatch_permute_kernel<true>, dim3(blocks), dim3(256), 0, s, topk_idx,
                        (const int32_t*)blk_count, disp_blocks, (const int32_t*)blk_base, offsets,

@@ -20,9 +20,11 @@ Workspace workspace_layout(const moe_problem_t& p) {
   w.route_pre = off;
   off = align_up(off + route_pre_bytes(p), kAlign);
   w.disp_count = off;
-  off = align_up(off + (size_t)w.disp_blocks * N * 4, kAlign);
+  off = align_up(off + (size_t)w.disp_blocks * K * N * 4, kAlign);
   w.disp_base = off;
-  off = align_up(off + (size_t)w.disp_blocks * N * 4, kAlign);
+  off = align_up(off + (size_t)w.disp_blocks * K * N * 4, kAlign);
+  w.disp_q = off;
+  off = align_up(off + K * N * 4, kAlign);
   w.tiles = off;
   off = align_up(off + 2 * (N + 2) * 4, kAlign);
   w.act = off;
@@ -120,6 +122,8 @@ int check_problem(const moe_problem_t* p) {
   if (p->act != MOE_ACT_SWIGLU && p->act != MOE_ACT_RELU) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (isnan(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (p->drop_order != MOE_DROP_TOKEN_ORDER && p->drop_order != MOE_DROP_CHOICE_RANK)
+    return MOE_ERR_INVALID_ARG;
   // valid, but outside what the kernels implement
   if (p->N > 256 || p->K > 16) return MOE_ERR_UNSUPPORTED;
   if (p->d % 64 != 0 || p->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -279,7 +283,8 @@ int moe_dispatch(const moe_problem_t* p, const void* u, const int32_t* topk_idx,
   return hip_status(moe::launch_dispatch(
       *p, u, topk_idx, C, expert_counts, kept_counts, offsets, row_of, token_of_row, x_perm,
       reinterpret_cast<int32_t*>(ws_at(ws, w.disp_count)),
-      reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)), w.disp_blocks,
+      reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)),
+      reinterpret_cast<int32_t*>(ws_at(ws, w.disp_q)), w.disp_blocks,
       static_cast<hipStream_t>(stream)));
 }
 
@@ -350,7 +355,8 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
   e = moe::launch_dispatch(*p, u, o->topk_idx, C, o->expert_counts, o->kept_counts, o->offsets,
                            o->row_of, o->token_of_row, o->x_perm,
                            reinterpret_cast<int32_t*>(ws_at(ws, w.disp_count)),
-                           reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)), w.disp_blocks, s);
+                           reinterpret_cast<int32_t*>(ws_at(ws, w.disp_base)),
+                           reinterpret_cast<int32_t*>(ws_at(ws, w.disp_q)), w.disp_blocks, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   void* ysh = p->n_shared > 0 ? o->y_shared : nullptr;
   e = moe::launch_grouped_ffn(*p, p->T * p->K, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u,

@@ -44,8 +44,9 @@ constexpr int kDispatchTok = 256;   // tokens per dispatch block
 struct Workspace {
   size_t route_part;   // fp32 [route_blocks][N]   per-block softmax sums
   size_t route_pre;    // fp32 [slices][T][N]       split-k logits (few tokens)
-  size_t disp_count;   // int32 [disp_blocks][N]  per-block expert counts
-  size_t disp_base;    // int32 [disp_blocks][N]  per-block rank base
+  size_t disp_count;   // int32 [disp_blocks][K][N]  per-block expert counts (per choice rank)
+  size_t disp_base;    // int32 [disp_blocks][K][N]  per-block rank base
+  size_t disp_q;       // int32 [K][N]               kept per choice rank
   size_t tiles;        // int32 [2][N+2]          grouped-GEMM full and tail tile prefixes
   size_t act;          // elem [T*K][d_ff]        gated activations
   size_t act_shared;   // elem [T][n_shared*d_ff_shared]
@@ -71,7 +72,7 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                            int32_t capacity, int32_t* expert_counts, int32_t* kept_counts,
                            int32_t* offsets, int32_t* row_of, int32_t* token_of_row,
                            void* x_perm, int32_t* blk_count, int32_t* blk_base,
-                           int disp_blocks, hipStream_t s);
+                           int32_t* level_q, int disp_blocks, hipStream_t s);
 
 // rows_alloc: rows of x_perm / y_perm / act (T*K for token choice).
 hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void* x_perm,

@@ -19,10 +19,12 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_RELU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
+MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_RANK = 0, 1
 
 GATING = {"softmax_topk": MOE_GATE_SOFTMAX_TOPK, "topk_softmax": MOE_GATE_TOPK_SOFTMAX}
 ACT = {"swiglu": MOE_ACT_SWIGLU, "relu": MOE_ACT_RELU}
 DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16}
+DROP = {"token": MOE_DROP_TOKEN_ORDER, "choice": MOE_DROP_CHOICE_RANK}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 
@@ -31,7 +33,7 @@ class MoeProblem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
                 ("noise_weight", ctypes.c_float), ("gating", ctypes.c_int32),
-                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32), ("drop_order", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -122,19 +124,22 @@ def lib() -> ctypes.CDLL:
 
 
 def problem(T, d, N, K, d_ff, n_shared=0, d_ff_shared=0, capacity_factor=0.0, noise_weight=0.0,
-            gating=MOE_GATE_TOPK_SOFTMAX, act=MOE_ACT_SWIGLU, dtype=MOE_BF16) -> MoeProblem:
+            gating=MOE_GATE_TOPK_SOFTMAX, act=MOE_ACT_SWIGLU, dtype=MOE_BF16,
+            drop_order=MOE_DROP_TOKEN_ORDER) -> MoeProblem:
     gating = GATING.get(gating, gating)
     act = ACT.get(act, act)
     dtype = DTYPE.get(dtype, dtype)
+    drop_order = DROP.get(drop_order, drop_order)
     return MoeProblem(T, d, N, K, d_ff, n_shared, d_ff_shared, capacity_factor, noise_weight,
-                      gating, act, dtype)
+                      gating, act, dtype, drop_order)
 
 
 def problem_of(w, **over) -> MoeProblem:
     """Problem descriptor of a workload description (workloads.Workload)."""
     kw = dict(T=w.T, d=w.d, N=w.N, K=w.K, d_ff=w.d_ff, n_shared=w.n_shared,
               d_ff_shared=w.d_ff_shared, capacity_factor=w.capacity_factor,
-              noise_weight=w.noise_weight, gating=w.gating, act=w.act, dtype=w.dtype)
+              noise_weight=w.noise_weight, gating=w.gating, act=w.act, dtype=w.dtype,
+              drop_order=w.drop_order)
     kw.update(over)
     return problem(**kw)
 

@@ -46,6 +46,7 @@ class Workload:
     hot_bias: float = 0.70              # hot2: bias added to two seeded experts
     zipf_s: float = 1.2                 # zipf: exponent of the load ranking
     noise: bool = False
+    drop_order: str = "token"           # token | choice: priority under capacity
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)

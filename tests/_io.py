@@ -8,6 +8,7 @@ from oracle import oracle as O
 GATING = {"softmax_topk": O.GATE_SOFTMAX_TOPK, "topk_softmax": O.GATE_TOPK_SOFTMAX}
 ACT = {"swiglu": O.ACT_SWIGLU, "relu": O.ACT_RELU}
 DT = {"f32": O.F32, "bf16": O.BF16}
+DROP = {"token": O.DROP_TOKEN_ORDER, "choice": O.DROP_CHOICE_RANK}
 
 
 def to_np(t):
@@ -31,7 +32,7 @@ def problem(w, **over):
     kw = dict(T=w.T, d=w.d, N=w.N, K=w.K, d_ff=w.d_ff, n_shared=w.n_shared,
               d_ff_shared=w.d_ff_shared, capacity_factor=w.capacity_factor,
               noise_weight=w.noise_weight, gating=GATING[w.gating], act=ACT[w.act],
-              dtype=DT[w.dtype])
+              dtype=DT[w.dtype], drop_order=DROP[w.drop_order])
     kw.update(over)
     return O.Problem(**kw)
 

@@ -95,6 +95,7 @@ def test_workspace_size():
     (dict(dtype=3), M.MOE_ERR_INVALID_ARG),
     (dict(n_shared=1, d_ff_shared=0), M.MOE_ERR_INVALID_ARG),
     (dict(capacity_factor=float("nan")), M.MOE_ERR_INVALID_ARG),
+    (dict(drop_order=2), M.MOE_ERR_INVALID_ARG),
     (dict(N=300, K=2), M.MOE_ERR_UNSUPPORTED),
     (dict(N=32, K=17), M.MOE_ERR_UNSUPPORTED),
     (dict(d=96), M.MOE_ERR_UNSUPPORTED),

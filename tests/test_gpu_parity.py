@@ -113,9 +113,10 @@ def test_route_ties_and_noise_off():
 
 # --------------------------------------------------------------- dispatch
 
-def _dispatch_case(T, N, K, d, dtype, cf, seed, skew=0.0):
-    w = W.Workload("disp", T=T, d=d, N=N, K=K, d_ff=64, dtype=dtype, capacity_factor=cf, seed=seed)
-    say(f"dispatch T={T} N={N} K={K} d={d} {dtype} cf={cf} skew={skew}")
+def _dispatch_case(T, N, K, d, dtype, cf, seed, skew=0.0, drop_order="token"):
+    w = W.Workload("disp", T=T, d=d, N=N, K=K, d_ff=64, dtype=dtype, capacity_factor=cf, seed=seed,
+                   drop_order=drop_order)
+    say(f"dispatch T={T} N={N} K={K} d={d} {dtype} cf={cf} skew={skew} {drop_order}")
     u = W.generate(w, only=("u",))["u"]
     idx = W.random_topk(T, N, K, seed, skew)
     p = M.problem_of(w)
@@ -150,6 +151,20 @@ def test_dispatch_edges(T, N, K, cf, skew):
     ref = _dispatch_case(T, N, K, 64, "bf16", cf, 17 + T, skew)
     if cf > 0:
         assert (ref["expert_counts"] - ref["kept_counts"]).sum() > 0   # drops happen
+
+
+@pytest.mark.parametrize("T,N,K,cf,skew", [(300, 7, 3, 0.5, 2.0), (2049, 8, 2, 1.0, 1.5),
+                                           (777, 256, 16, 0.3, 1.2), (5000, 64, 6, 0.8, 0.5),
+                                           (1000, 16, 2, 0.0, 0.0), (16385, 64, 6, 1.1, 1.0)])
+def test_dispatch_choice_rank(T, N, K, cf, skew):
+    """Capacity by choice rank: every first choice before any second choice;
+    bit-exact maps and rows against the oracle."""
+    ref = _dispatch_case(T, N, K, 64, "bf16", cf, 31 + T, skew, drop_order="choice")
+    if cf > 0:
+        tok = O.dispatch(_io.problem(W.Workload("d", T=T, d=64, N=N, K=K, d_ff=64,
+                                                capacity_factor=cf)),
+                         W.random_topk(T, N, K, 31 + T, skew).numpy())
+        assert not np.array_equal(tok["row_of"], ref["row_of"])   # the orders differ here
 
 
 def test_dispatch_figure3():
@@ -360,11 +375,14 @@ def test_layer_full_size(name):
     (200, 8, 3, "softmax_topk", "swiglu", 0.0, 2, "bf16"),
     (150, 1, 1, "topk_softmax", "swiglu", 0.0, 0, "bf16"),
     (100, 5, 2, "softmax_topk", "relu", 0.0, 1, "f32"),
-    (333, 16, 16, "softmax_topk", "swiglu", 0.0, 0, "bf16")])
+    (333, 16, 16, "softmax_topk", "swiglu", 0.0, 0, "bf16"),
+    (400, 6, 3, "topk_softmax", "swiglu", 0.4, 1, "bf16-choice")])
 def test_layer_small_shapes(T, N, K, gating, act, cf, shared, dtype):
+    dtype, _, drop = dtype.partition("-")
     w = W.Workload("small", T=T, d=128, N=N, K=K, d_ff=192, gating=gating, act=act,
                    capacity_factor=cf, n_shared=shared, d_ff_shared=64 if shared else 0,
-                   dtype=dtype, seed=T * 31 + N, noise=True, noise_weight=0.5)
+                   dtype=dtype, seed=T * 31 + N, noise=True, noise_weight=0.5,
+                   drop_order=drop or "token")
     x = W.generate(w)
     p = M.problem_of(w)
     say(f"layer small T={T} N={N} K={K} {gating} {act} cf={cf} shared={shared} {dtype}")
