@@ -570,15 +570,19 @@ struct WgradArgs {
 };
 
 __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
-  __shared__ u32x4 sA[2][256 * 8];
-  __shared__ u32x4 sB[2][256 * 8];
+  // operand stages, then the output tile: 128 KB in one array
+  __shared__ u32x4 smem[4][256 * 8];
+  u32x4 (&sA)[2][256 * 8] = *reinterpret_cast<u32x4 (*)[2][256 * 8]>(&smem[0]);
+  u32x4 (&sB)[2][256 * 8] = *reinterpret_cast<u32x4 (*)[2][256 * 8]>(&smem[2]);
   constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2, PER = 32 / NW;
   const int mtn = (a.M + 255) / 256, ntn = (a.N + 255) / 256;
   const int per_g = mtn * ntn, total = a.G * per_g;
-  const int h = blockIdx.x;
-  if (h >= total) return;
-  // XCD-contiguous runs of tiles (consecutive blocks go to different XCDs)
+  // Persistent: block b takes tiles b, b + gridDim, ...; a tile's output
+  // stores then drain while the block already streams the next tile's
+  // operands.  XCD-contiguous runs of tiles (consecutive blocks go to
+  // different XCDs; gridDim is a multiple of 8, so a block stays on one).
   const int full = total - total % 8;
+  for (int h = blockIdx.x; h < total; h += gridDim.x) {
   const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
   const int g = __builtin_amdgcn_readfirstlane(L / per_g);
   const int rem = L - g * per_g;
@@ -657,31 +661,42 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
     __syncthreads();
   }
 
-  // epilogue: lane holds column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4
+  // epilogue: the tile goes through LDS as bf16 [256][256] (the operand
+  // stages are free after the loop's last barrier) and out in 16-byte
+  // stores.  Lane holds column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4;
+  // neighbouring lanes swap one value so that each writes a 4-byte pair of
+  // columns: the even lane row r, the odd lane row r+1.
+  uint32_t* stile = reinterpret_cast<uint32_t*>(&smem[0][0]);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * WTN + 32 * j + (lane & 31);
-    if (n >= a.N) continue;
-    const size_t ncol = (size_t)(n / a.nseg) * a.nseg_stride + (size_t)(n % a.nseg);
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
+        const bool odd = (lane & 1) != 0;
+        const float give = odd ? acc[i][j][v] : acc[i][j][v + 1];
+        const float got = __shfl_xor(give, 1);
         f32x2 pr;
-        pr[0] = acc[i][j][v];
-        pr[1] = acc[i][j][v + 1];
-        const uint32_t packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int m = m0 + wm * WTM + 32 * i + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
-          if (m >= a.M) continue;
-          uint16_t* out = static_cast<uint16_t*>(m < a.msplit ? a.C : a.C2) + (size_t)g * a.c_group_stride;
-          const int mr = m < a.msplit ? m : m - a.msplit;
-          out[(size_t)mr * a.ldc + ncol] = (uint16_t)(q ? packed >> 16 : packed & 0xffffu);
-        }
+        pr[0] = odd ? got : acc[i][j][v];
+        pr[1] = odd ? acc[i][j][v + 1] : got;
+        const int r = wm * WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3) + (odd ? 1 : 0);
+        const int c = wn * WTN + 32 * j + (lane & 31) - (odd ? 1 : 0);
+        stile[r * 128 + (c >> 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
       }
-    }
+  __syncthreads();
+  const u32x4* vt = &smem[0][0];
+#pragma unroll 4
+  for (int id = tid; id < 256 * 32; id += 512) {
+    const int r = id >> 5, cv = id & 31;
+    const int m = m0 + r, n = n0 + 8 * cv;
+    if (m >= a.M || n >= a.N) continue;
+    uint16_t* out = static_cast<uint16_t*>(m < a.msplit ? a.C : a.C2) + (size_t)g * a.c_group_stride;
+    const int mr = m < a.msplit ? m : m - a.msplit;
+    const size_t ncol = (size_t)(n / a.nseg) * a.nseg_stride + (size_t)(n % a.nseg);
+    *reinterpret_cast<u32x4*>(out + (size_t)mr * a.ldc + ncol) = vt[id];
   }
+  __syncthreads();                 // the tile's LDS reads are done
+  }  // tiles
 }
 
 // --------------------------------------------------------------- fp32
@@ -929,9 +944,28 @@ WgradArgs wgrad_args(const void* A, int lda, const void* B, int ldb, const int32
   return w;
 }
 
+// compute units of the current device (cached per device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t run_wgrad(const WgradArgs& w, hipStream_t s) {
-  const long long blocks = (long long)w.G * ((w.M + 255) / 256) * ((w.N + 255) / 256);
-  if (blocks == 0) return hipSuccess;
+  const long long tiles = (long long)w.G * ((w.M + 255) / 256) * ((w.N + 255) / 256);
+  if (tiles == 0) return hipSuccess;
+  // one 512-thread block per compute unit (128 KB of LDS each), rounded
+  // down to a multiple of 8 XCDs
+  long long blocks = cu_count() / 8 * 8;
+  if (blocks < 8) blocks = 8;
+  if (blocks > tiles) blocks = tiles;
   hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)blocks), dim3(512), 0, s, w);
   return hipGetLastError();
 }
