@@ -264,12 +264,14 @@ __device__ __forceinline__ bf16x8 read_kmajor(const char* tile, int kk, int col0
   return __builtin_bit_cast(bf16x8, both);
 }
 
+
 // One BM x BN output tile of group g (rows [row0, row0+rows), n-tile by),
 // staged through the caller's LDS arrays (at least BM and BN rows a stage).
 //
 // BT: B is k-major (B[k][n] row-major, n contiguous; see above) instead of
-// [n][k]; only with EPI_NONE and BN = 256.
-template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN, bool BT = false>
+// [n][k]; only with EPI_NONE and BN = 256.  PIPE: the software-pipelined
+// main loop (256-column tiles); otherwise a plain double-buffered loop.
+template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN, bool BT = false, bool PIPE = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, int rows, int by,
                                           u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN]) {
   constexpr int NW = WGM * WGN;                   // waves
@@ -382,6 +384,159 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   };
 
   const int nk = a.Kdim / BK;
+  if constexpr (PIPE) {
+    static_assert(BN == 256, "pipelined tile: 256 columns");
+    // Software pipeline with a fixed instruction order.  Fragments of
+    // k-step kk+1 are read between the matrix instructions of k-step kk, in
+    // the order the matrix instructions consume them.  The stage barrier
+    // sits in the middle of k-step 3: the first half of its matrix
+    // instructions runs before it, the second half after it, while the next
+    // stage's first fragments are read.  From that barrier on, the buffer of
+    // the stage just finished is free, so the loads of the stage after next
+    // start at once and continue through k-steps 0 and 1, one per two matrix
+    // instructions per wave: a burst of them would stall the wave's issue
+    // (the load path takes about one 1-KB load per 16 cycles per CU).
+    // Every K-segment length is a multiple of BK, so the segment of a stage
+    // advances without a division.  The loads issued during the last stage
+    // get an empty buffer range: they read nothing, and their LDS buffer is
+    // never read.
+    constexpr int NL = AI + BI;                       // loads per wave per stage
+    const uint32_t a_bytes = (uint32_t)rows * a.lda * 2;
+    const void* a_base = static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda;
+    int seg_n = 0, koff_n = 0;                        // segment and offset of the stage to load
+    auto issue_part = [&](int kt_n, bool live, int buf, int lo, int hi) {
+      const __amdgpu_buffer_rsrc_t rAx = make_rsrc(a_base, live ? a_bytes : 0u);
+      const uint32_t ka = (uint32_t)kt_n * BK * 2;
+#pragma unroll
+      for (int i = 0; i < AI; ++i) {
+        if (i < lo || i >= hi) continue;
+        const bool odd = ((wave * AI + i) & 1) != 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rAx, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
+                                                 (odd ? a_voff_o : a_voff_e) + i * a_step + ka, 0, 0, 0);
+      }
+      if constexpr (BT) {
+        const uint16_t* base = static_cast<const uint16_t*>(seg_n == 0 ? a.B0 : a.B1) +
+                               (size_t)g * a.b_group_stride + n0;
+        const __amdgpu_buffer_rsrc_t rBT =
+            make_rsrc(base, live ? (uint32_t)((size_t)a.kseg * a.ldb - n0) * 2u : 0u);
+        const uint32_t krow = (uint32_t)koff_n * (uint32_t)a.ldb * 2u;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+          if (AI + i < lo || AI + i >= hi) continue;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rBT, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
+                                                   kmajor_voff(wave * BI + i, lane, a.ldb) + krow,
+                                                   0, 0, 0);
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rBx =
+            make_rsrc(Bsrc + (size_t)seg_n * a.kseg_stride, live ? b_bytes : 0u);
+        const uint32_t kbb = (uint32_t)koff_n * 2;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+          if (AI + i < lo || AI + i >= hi) continue;
+          const bool odd = ((wave * BI + i) & 1) != 0;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rBx, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
+                                                   (odd ? b_voff_o : b_voff_e) + i * b_step + kbb, 0, 0, 0);
+        }
+      }
+    };
+    auto advance = [&]() {
+      koff_n += BK;
+      if (koff_n == a.kseg) { koff_n = 0; ++seg_n; }
+    };
+    auto read_frags = [&](bf16x8 (&fa_)[TM], bf16x8 (&fb_)[TN], int buf, int kk) {
+      const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa_[i] = __builtin_bit_cast(bf16x8, sA[buf][swz(wm * WTM + i * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BT) fb_[j] = read_kmajor((const char*)&sB[buf][0], kk, brow(j), lane);
+        else fb_[j] = __builtin_bit_cast(bf16x8, sB[buf][swz(brow(j) + (lane & 31), c)]);
+      }
+    };
+    // Fragment r of a k-step, in the order the matrix instructions of row
+    // 0 need them first: A row 0, the B columns, then A rows 1.. .
+    auto read_one = [&](bf16x8 (&ra)[TM], bf16x8 (&rb)[TN], int rbuf, int rkk, int r) {
+      const int c = rkk * 2 + (lane >> 5);
+      const int ia = r == 0 ? 0 : (r <= TN ? -1 : r - TN);
+      if (ia >= 0) {
+        ra[ia] = __builtin_bit_cast(bf16x8, sA[rbuf][swz(wm * WTM + ia * 32 + (lane & 31), c)]);
+      } else {
+        const int jj = r - 1;
+        if constexpr (BT) rb[jj] = read_kmajor((const char*)&sB[rbuf][0], rkk, brow(jj), lane);
+        else rb[jj] = __builtin_bit_cast(bf16x8, sB[rbuf][swz(brow(jj) + (lane & 31), c)]);
+      }
+    };
+    // One k-step in a fixed order: matrix instruction s is followed by
+    // fragment read s / RS of the next k-step when s % RS == 0, and by load
+    // l0 + s / 2 of the next stage when s is odd; each step is fenced so the
+    // compiler keeps the order.
+    auto kstep = [&](const bf16x8 (&fa_)[TM], const bf16x8 (&fb_)[TN], int i0, int i1,
+                     bf16x8 (&ra)[TM], bf16x8 (&rb)[TN], int rbuf, int rkk, bool rd, int RS,
+                     int kt_n, bool live, int lbuf, int l0, int l1) {
+      int s = 0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i < i0 || i >= i1) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
+          if (rd && s % RS == 0 && s / RS < TM + TN) read_one(ra, rb, rbuf, rkk, s / RS);
+          if ((s & 1) && l0 + s / 2 < l1) issue_part(kt_n, live, lbuf, l0 + s / 2, l0 + s / 2 + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          ++s;
+        }
+      }
+      // reads or loads left over when the k-step has fewer instructions
+#pragma unroll
+      for (int t = 0; t < TM + TN; ++t)
+        if (rd && t * RS >= s) read_one(ra, rb, rbuf, rkk, t);
+#pragma unroll
+      for (int t = 0; t < NL; ++t)
+        if (l0 + t < l1 && 2 * t + 1 >= s) issue_part(kt_n, live, lbuf, l0 + t, l0 + t + 1);
+    };
+    constexpr int H = TM / 2;
+    bf16x8 fa[2][TM], fb[2][TN];
+    issue_part(0, true, 0, 0, NL);
+    advance();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    read_frags(fa[0], fb[0], 0, 0);
+    // k-steps 0, 1, 2 and the first half of 3 of stage kt; loads l0.. of
+    // stage kt+1 are issued during k-steps 0 and 1 (the first ones already
+    // went out after the previous barrier)
+    auto body = [&](int kt, int l0) {
+      const int buf = kt & 1;
+      const bool live = kt + 1 < nk;
+      const int lm = l0 + TM * TN / 2 < NL ? l0 + TM * TN / 2 : NL;
+      kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], buf, 1, true, 2, kt + 1, live, buf ^ 1, l0, lm);
+      kstep(fa[1], fb[1], 0, TM, fa[0], fb[0], buf, 2, true, 2, kt + 1, live, buf ^ 1, lm, NL);
+      kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], buf, 3, true, 2, 0, false, 0, 0, 0);
+      kstep(fa[1], fb[1], 0, H, fa[0], fb[0], 0, 0, false, 1, 0, false, 0, 0, 0);
+      advance();
+    };
+    // loads issued during the second half of k-step 3 (one per two matrix
+    // instructions)
+    constexpr int LB = (TM - H) * TN / 2 < NL ? (TM - H) * TN / 2 : NL;
+    body(0, 0);
+    // The loop starts at the stage barrier, where every wait has drained,
+    // so the waits on the fragment reads after it stay exact.  The buffer
+    // of stage kt-1 is free from here on, so the loads of stage kt+1 start
+    // at once.
+    for (int kt = 1; kt < nk; ++kt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // second half of k-step 3 of stage kt-1, reading the first
+      // fragments of stage kt
+      kstep(fa[1], fb[1], H, TM, fa[0], fb[0], kt & 1, 0, true, 1, kt + 1, kt + 1 < nk, (kt + 1) & 1, 0, LB);
+      body(kt, LB);
+    }
+    kstep(fa[1], fb[1], H, TM, fa[0], fb[0], 0, 0, false, 1, 0, false, 0, 0, 0);
+    // the empty loads of the last stage still write the LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -421,6 +576,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  }
+
   }
 
   // epilogue: lane holds column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4
@@ -522,10 +679,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
   int g, row0, rows, by;
   if (h < real) {
     find_tile_2d(a, 256, ntiles, h, real, g, row0, rows, by);
-    if (rows > 256) gemm_tile<EPI, 256 + kExtRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
-    else gemm_tile<EPI, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
+    if (rows > 256) gemm_tile<EPI, 256 + kExtRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
+    else gemm_tile<EPI, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
   } else if (find_tail(a, 256, ntiles, h - real, g, row0, rows, by)) {
-    gemm_tile<EPI, kTailRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
+    gemm_tile<EPI, kTailRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
   }
 }
 
