@@ -122,6 +122,10 @@ __host__ __device__ inline int full_tiles_total(const GemmArgs& a, int BM) {
 // n-tiles, so the activation and weight panels of a patch are fetched into
 // one L2 once and shared by the blocks of the patch.  rows is at most BM,
 // except for a group's last tile, which may run up to ext_rows further.
+// The row tiles of patch nb are taken in an order rotated by nb: a block at
+// a given position of successive patches tends to land on the same CU (the
+// CUs finish their tiles in the same order), and without the rotation the
+// same few CUs would draw every group's taller last tile.
 __host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntiles, int h, int real,
                                              int& g, int& row0, int& rows, int& nt) {
   int mt_g, base;
@@ -146,7 +150,7 @@ __host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntil
   const int nb = l / (mt_g * kPatchN);
   const int rem = l - nb * mt_g * kPatchN;
   const int nbe = ntiles - nb * kPatchN < kPatchN ? ntiles - nb * kPatchN : kPatchN;
-  const int mt = rem / nbe;
+  const int mt = (rem / nbe + nb) % mt_g;
   nt = nb * kPatchN + rem % nbe;
   row0 = (a.offsets == nullptr ? 0 : a.offsets[g]) + mt * BM;
   const int end = a.offsets == nullptr ? a.M : a.offsets[g + 1];
