@@ -588,6 +588,108 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   uint16_t* C = static_cast<uint16_t*>(a.C);
   constexpr int OUT_TN = GATED ? TN / 2 : TN;
   const int col_base = n0 + (GATED ? wn * (WTN / 2) : wn * WTN) + (lane & 31);
+  if constexpr (PIPE && EPI == EPI_SWIGLU_BWD) {
+    // Backward epilogue through LDS.  The dA tile is staged as bf16
+    // [BM][128] with 16-byte loads.  Neighbouring lanes swap one value of
+    // each accumulator pair in place, so that each lane holds two adjacent
+    // columns of one row (the even lane row r, the odd lane row r+1), and
+    // read the matching dA pair as one 4-byte word.  a, dG and dU are then
+    // produced one at a time, each packed as bf16 pairs into the same LDS
+    // region and written out in 16-byte row pieces.  16-byte chunk c of
+    // staged row r sits at slot c ^ 4*(r%2 + 2*(r/4 %2)), which keeps the
+    // pair accesses of one instruction (rows r, r+1, r+4, r+5) on disjoint
+    // banks.
+    static_assert(BM * 256 <= 2 * SAN * 16, "staged tile fits the A stages");
+    static_assert(OUT_TN == 1, "one 32-column output block per wave");
+    uint32_t* st = reinterpret_cast<uint32_t*>(&sA[0][0]);
+    u32x4* stv = &sA[0][0];
+    auto slot = [](int r, int c) { return c ^ (((r & 1) | ((r >> 1) & 2)) << 2); };
+    const uint16_t* D = static_cast<const uint16_t*>(a.D);
+    uint16_t* C2 = static_cast<uint16_t*>(a.C2);
+    const int wcol = wn * (WTN / 2);                    // first output column of the wave
+    const bool odd = (lane & 1) != 0;
+    auto pair_row = [&](int i, int v) { return wm * WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3) + (odd ? 1 : 0); };
+    const int pc = wcol + (lane & 31) - (odd ? 1 : 0);  // the lane's (even) first column
+    __syncthreads();               // the loop's LDS reads are done
+    {
+      // direct loads of the dA tile: load q of the wave fills staged rows
+      // 4q' .. 4q'+3 (q' = wave*DQ + q), lane l row 4q' + l/16 at slot l%16,
+      // which holds chunk (l%16) ^ slot-XOR of that row; rows past the
+      // group read 0 through the descriptor's size
+      constexpr int DQ = BM / 4 / NW;
+      static_assert(DQ * 4 * NW == BM, "whole rows per wave");
+      const __amdgpu_buffer_rsrc_t rD = make_rsrc(D + (size_t)row0 * a.ldd, (uint32_t)rows * a.ldd * 2u);
+#pragma unroll
+      for (int q = 0; q < DQ; ++q) {
+        const int r = (wave * DQ + q) * 4 + (lane >> 4);
+        const int ch = slot(r, lane & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_t*)&stv[(wave * DQ + q) * 64], 16,
+                                                 (uint32_t)(r * a.ldd + n0 + 8 * ch) * 2u, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const int j = jj * (TN / 2);                   // gate block, then up block
+          const float got = __shfl_xor(odd ? acc[i][j][v] : acc[i][j][v + 1], 1);
+          const float x0 = acc[i][j][v], x1 = acc[i][j][v + 1];
+          acc[i][j][v] = odd ? got : x0;
+          acc[i][j][v + 1] = odd ? x1 : got;
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t dap[TM * 8];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const int r = pair_row(i, v);
+        dap[i * 8 + v / 2] = st[r * 64 + slot(r, pc >> 3) * 4 + ((pc >> 1) & 3)];
+      }
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {
+      __syncthreads();             // the staged dA / the last output is fully read
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const uint32_t dp = dap[i * 8 + v / 2];
+          f32x2 pr;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            float gv = acc[i][0][v + q];
+            const float uv = acc[i][TN / 2][v + q];
+            // recompute the gate terms in each round rather than keep them
+            // live across all three (an empty asm hides gv's value)
+            asm volatile("" : "+v"(gv));
+            const float sg = sigmoid_fast(gv);
+            const float sl = gv * sg;
+            const float da = __builtin_bit_cast(float, q ? (dp & 0xffff0000u) : (dp << 16));
+            if (o == 0) pr[q] = sl * uv;
+            else if (o == 1) pr[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
+            else pr[q] = da * sl;
+          }
+          const int r = pair_row(i, v);
+          st[r * 64 + slot(r, pc >> 3) * 4 + ((pc >> 1) & 3)] =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        }
+      __syncthreads();
+      uint16_t* dst = o == 0 ? C : C2;
+      const int ld = o == 0 ? a.ldc : a.ldc2;
+      const int cofs = o == 2 ? a.Ndim : 0;           // dU follows dG in each row of C2
+#pragma unroll 2
+      for (int id = tid; id < BM * 16; id += NW * 64) {
+        const int r = id >> 4, ch = id & 15;
+        const int col = n0 + 8 * ch;
+        if (r < rows && col < a.Ndim)
+          *reinterpret_cast<u32x4*>(dst + (size_t)(row0 + r) * ld + cofs + col) = stv[r * 16 + slot(r, ch)];
+      }
+    }
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) {
     // a = act(g[, v]) to C; dG (and dU) from dA to C2
     const uint16_t* D = static_cast<const uint16_t*>(a.D);
