@@ -73,9 +73,8 @@ def main():
                          "known size, to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the layer shards over tokens with no communication; see DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the multi-GPU (expert-parallel, all-to-all) "
+              "path of the layer is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

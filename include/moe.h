@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size or enum, misaligned pointer */
-  MOE_ERR_UNSUPPORTED = 2,  /* valid problem outside what this build implements */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid problem outside what the library implements */
   MOE_ERR_WORKSPACE = 3,    /* ws NULL or ws_bytes below moe_workspace_size() */
   MOE_ERR_HIP = 4           /* a HIP launch failed (hipGetLastError) */
 } moe_status_t;
