@@ -56,6 +56,39 @@ def stored_traffic(workload):
     return e.get("bytes_per_call")
 
 
+def mfma_reference(stream):
+    """Attainable bf16 MFMA rate: back-to-back matrix instructions on register
+    operands, eight waves per CU, from libmoe_ref.so (a reference measurement,
+    not part of the layer).  None when that library is absent."""
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "sparse_mixture_experts_42_amd", "libmoe_ref.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.moe_ref_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_ref_mfma.restype = ctypes.c_int
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    iters = 60000
+    assert lib.moe_ref_mfma(blocks, 1000, ctypes.c_void_p(out.data_ptr()), sp) == 0
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert lib.moe_ref_mfma(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    flops = blocks * 8 * iters * 8 * 32768.0
+    tf = flops / (float(np.median(times)) * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "note": "independent v_mfma_f32_32x32x16_bf16 on register operands, 8 waves per CU, no "
+                    "memory traffic: the matrix-core rate at the clock the chip sustains under that load"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +247,9 @@ def main():
     del flush, src, dst
     log("stages, cold caches (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_cold_ms.items()))
     log(f"copy of 128 MiB: warm {copy_warm_ms:.4f} ms, cold {copy_cold_ms:.4f} ms")
+    mfma_ref = mfma_reference(stream)
+    if mfma_ref is not None:
+        log(f"matrix cores alone (reference): {mfma_ref['tflops']} TFLOP/s")
 
     # ---- expert-choice pass on the same workload (same inputs and weights)
     ec = None
@@ -296,6 +332,8 @@ def main():
     flops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * mults
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (stages_ms["grouped_ffn"] * 1e-3) / 1e12
+    if mfma_ref is not None and w.dtype == "bf16":
+        mfma_ref["grouped_gemm_frac_of_this"] = round(achieved / mfma_ref["tflops"], 4)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name),
                 "kernel": "grouped expert GEMMs (moe_grouped_ffn: gate/up GEMM + down GEMM)",
@@ -367,6 +405,7 @@ def main():
                            "cold_frac": round(copy_bytes / (copy_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "note": "device-to-device copy of 128 MiB, the attainable HBM fraction "
                                    "for a transfer of the combine stage's size"},
+        "mfma_reference": mfma_ref,
         "cpu_baseline": cpu,
         "expert_choice": ec,
         "backward": bwd,

@@ -15,6 +15,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
+# reference measurements (not part of the layer): csrc_ref/ -> libmoe_ref.so
+CSRC_REF = os.path.join(HERE, "csrc_ref")
+LIB_REF = os.path.join(HERE, "libmoe_ref.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -45,17 +48,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    refs = sorted(os.path.join(CSRC_REF, f) for f in os.listdir(CSRC_REF) if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(refs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + refs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], LIB_REF, verbose)
     return LIB
 
 

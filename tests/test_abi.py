@@ -39,6 +39,13 @@ def test_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_reference_library_exports_its_probe():
+    # the matrix-core reference the benchmark times (not part of the layer's ABI)
+    path = os.path.join(ROOT, "sparse_mixture_experts_42_amd", "libmoe_ref.so")
+    L = ctypes.CDLL(path)
+    assert hasattr(L, "moe_ref_mfma")
+
+
 def test_status_strings():
     for s in range(5):
         assert M.moe_status_string(s).startswith("MOE_")
