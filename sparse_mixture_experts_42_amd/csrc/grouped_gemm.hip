@@ -962,6 +962,122 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
   }  // tiles
 }
 
+// ------------------------------------- weight gradients, transposed form
+// For groups of many rows the weight gradients run as forward-style GEMMs:
+// dW_g = A_g^T B_g with A_g^T stored explicitly (each A column a row,
+// reduction index contiguous) and B_g read k-major, the form of the dA and
+// dX GEMMs.  The transposed operand holds group g's rows as columns
+// kpad[g] .. kpad[g] + K_g, zero up to the next multiple of BK.
+
+// kpad[g]: first column of group g in the transposed operands (a multiple
+// of BK); kpad[G]: the padded total.
+__global__ void kpad_kernel(const int32_t* offsets, int G, int32_t* kpad) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  int acc = 0;
+  for (int g = 0; g < G; ++g) {
+    kpad[g] = acc;
+    acc += (offsets[g + 1] - offsets[g] + BK - 1) / BK * BK;
+  }
+  kpad[G] = acc;
+}
+
+// S [rows][C] (leading dimension lds) -> T [C][ldt] (bf16): row r of group
+// g becomes column kpad[g] + r - offsets[g]; each group's padding columns
+// are zero.  One block per 64 x 64 tile of T; blocks past kpad[G] exit.
+__global__ __launch_bounds__(256) void transpose_groups_kernel(const uint16_t* S, int lds, int C,
+                                                               const int32_t* offsets,
+                                                               const int32_t* kpad, int G,
+                                                               uint16_t* T, int ldt) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][64 + 8];   // 144-byte rows
+  const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (p0 >= kpad[G]) return;
+  int lo = 0, hi = G;                      // kpad[lo] <= p0 < kpad[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (kpad[mid] <= p0) lo = mid;
+    else hi = mid;
+  }
+  const int r0 = offsets[lo] + (p0 - kpad[lo]);
+  const int nrows = offsets[lo + 1] - r0;  // source rows left in the group (> 0)
+#pragma unroll
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int r = q >> 3, cc = (q & 7) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < nrows && c0 + cc < C) v = *reinterpret_cast<const u32x4*>(S + (size_t)(r0 + r) * lds + c0 + cc);
+    *reinterpret_cast<u32x4*>(&tile[r][cc]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int c = q >> 3, pc = (q & 7) * 8;
+    if (c0 + c >= C) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = (uint32_t)tile[pc + 2 * k][c] | ((uint32_t)tile[pc + 2 * k + 1][c] << 16);
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(T + (size_t)(c0 + c) * ldt + p0 + pc) = v;
+  }
+}
+
+struct KGemmArgs {
+  const void* AT;          // [M][ldat]: the transposed operand
+  int ldat;
+  const void* B;           // [rows][ldb]: rows offsets[g] .. of group g, k-major
+  int ldb;
+  const int32_t* offsets;  // [G+1] group rows
+  const int32_t* kpad;     // [G+1] group columns in AT
+  int G, M, N;
+  void* C;                 // group g: [M][ldc] at C + g * c_group_stride
+  int ldc;
+  size_t c_group_stride;
+};
+
+// One block per (group, 256 x 256 output tile), in the XCD-contiguous,
+// patch-rotated order of the forward GEMMs.  A group without rows writes
+// zeros.
+__global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
+  __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
+  __shared__ u32x4 sB[2][256 * 8];
+  const int mtn = (k.M + 255) / 256, ntn = (k.N + 255) / 256;
+  const int per = mtn * ntn, total = k.G * per;
+  const int h = blockIdx.x;
+  if (h >= total) return;
+  const int full = total - total % 8;
+  const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
+  const int g = L / per, l = L - g * per;
+  const int nb = l / (mtn * kPatchN);
+  const int rem = l - nb * mtn * kPatchN;
+  const int nbe = ntn - nb * kPatchN < kPatchN ? ntn - nb * kPatchN : kPatchN;
+  const int mt = (rem / nbe + nb) % mtn;
+  const int nt = nb * kPatchN + rem % nbe;
+  const int kg = k.offsets[g + 1] - k.offsets[g];
+  const int kp = k.kpad[g + 1] - k.kpad[g];
+  uint16_t* C = static_cast<uint16_t*>(k.C) + (size_t)g * k.c_group_stride;
+  const int row0 = mt * 256, rows = k.M - row0 < 256 ? k.M - row0 : 256, n0 = nt * 256;
+  if (kp == 0) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int id = threadIdx.x; id < 256 * 32; id += 512) {
+      const int r = id >> 5, col = n0 + 8 * (id & 31);
+      if (r < rows && col < k.N) *reinterpret_cast<u32x4*>(C + (size_t)(row0 + r) * k.ldc + col) = z;
+    }
+    return;
+  }
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(k.AT) + k.kpad[g];
+  a.lda = k.ldat;
+  a.B0 = static_cast<const uint16_t*>(k.B) + (size_t)k.offsets[g] * k.ldb;
+  a.B1 = a.B0;
+  a.ldb = k.ldb;
+  a.kseg = kg;             // the group's rows: B rows past them read 0
+  a.Kdim = kp;
+  a.Ndim = k.N;
+  a.C = C;
+  a.ldc = k.ldc;
+  a.G = 1;
+  a.M = k.M;
+  gemm_tile<EPI_NONE, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, true, true>(a, 0, row0, rows, nt, sA, sB);
+}
+
 // --------------------------------------------------------------- fp32
 // Plain fp32 path (one thread per output element), for fp32 problems.
 template <int EPI>
@@ -1233,6 +1349,24 @@ hipError_t run_wgrad(const WgradArgs& w, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t run_kgemm(const void* AT, int ldat, const void* B, int ldb, const int32_t* offsets,
+                     const int32_t* kpad, int G, int M, int N, void* C, int ldc, size_t c_stride,
+                     hipStream_t s) {
+  KGemmArgs k{AT, ldat, B, ldb, offsets, kpad, G, M, N, C, ldc, c_stride};
+  const long long blocks = (long long)G * ((M + 255) / 256) * ((N + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_kgemm_kernel, dim3((unsigned)blocks), dim3(512), 0, s, k);
+  return hipGetLastError();
+}
+
+hipError_t run_transpose(const void* S, int lds, int C, const int32_t* offsets, const int32_t* kpad,
+                         int G, void* T, int ldt, hipStream_t s) {
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ldt / 64));
+  hipLaunchKernelGGL(transpose_groups_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(S),
+                     lds, C, offsets, kpad, G, static_cast<uint16_t*>(T), ldt);
+  return hipGetLastError();
+}
+
 hipError_t run_bwd_epi(const GemmArgs& a, bool swiglu, int bm, int mtiles, hipStream_t s) {
   return swiglu ? launch_bf16<EPI_SWIGLU_BWD>(a, bm, mtiles, s)
                 : launch_bf16<EPI_RELU_BWD>(a, bm, mtiles, s);
@@ -1309,15 +1443,35 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   n2.ldc = d;
   if ((e = launch_bf16<EPI_NONE, true>(n2, bm, mtiles_max, s)) != hipSuccess) return e;
   // weight gradients
-  if ((e = run_wgrad(wgrad_args(b.dy_perm, d, b.act, dff, b.offsets, p.N, 0, d, dff, b.dw_down,
-                                nullptr, d, (size_t)d * dff, dff, dff, 0),
-                     s)) != hipSuccess)
-    return e;
-  if ((e = run_wgrad(wgrad_args(b.dgu, swiglu ? 2 * dff : dff, b.x_perm, d, b.offsets, p.N, 0,
-                                swiglu ? 2 * dff : dff, d, b.dw_gate, b.dw_up, dff,
-                                (size_t)dff * d, d, d, 0),
-                     s)) != hipSuccess)
-    return e;
+  const int gu = swiglu ? 2 : 1;
+  if (b.kpad != nullptr) {
+    // transposed form: dW_down = dY^T a, [dW_gate; dW_up] = [dG dU]^T X
+    hipLaunchKernelGGL(kpad_kernel, dim3(1), dim3(64), 0, s, b.offsets, p.N, b.kpad);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = run_transpose(b.dy_perm, d, d, b.offsets, b.kpad, p.N, b.dyT, b.ldt, s)) != hipSuccess) return e;
+    if ((e = run_kgemm(b.dyT, b.ldt, b.act, dff, b.offsets, b.kpad, p.N, d, dff, b.dw_down, dff,
+                       (size_t)d * dff, s)) != hipSuccess)
+      return e;
+    if ((e = run_transpose(b.dgu, gu * dff, gu * dff, b.offsets, b.kpad, p.N, b.dguT, b.ldt, s)) !=
+        hipSuccess)
+      return e;
+    if ((e = run_kgemm(b.dguT, b.ldt, b.x_perm, d, b.offsets, b.kpad, p.N, dff, d, b.dw_gate, d,
+                       (size_t)dff * d, s)) != hipSuccess)
+      return e;
+    if (swiglu &&
+        (e = run_kgemm(static_cast<const uint16_t*>(b.dguT) + (size_t)dff * b.ldt, b.ldt, b.x_perm, d,
+                       b.offsets, b.kpad, p.N, dff, d, b.dw_up, d, (size_t)dff * d, s)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = run_wgrad(wgrad_args(b.dy_perm, d, b.act, dff, b.offsets, p.N, 0, d, dff, b.dw_down,
+                                  nullptr, d, (size_t)d * dff, dff, dff, 0),
+                       s)) != hipSuccess)
+      return e;
+    if ((e = run_wgrad(wgrad_args(b.dgu, gu * dff, b.x_perm, d, b.offsets, p.N, 0, gu * dff, d,
+                                  b.dw_gate, b.dw_up, dff, (size_t)dff * d, d, d, 0),
+                       s)) != hipSuccess)
+      return e;
+  }
 
   if (p.n_shared == 0) return hipSuccess;
   // shared experts over all T tokens, dY = d_out

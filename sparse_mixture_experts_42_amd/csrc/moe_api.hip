@@ -97,8 +97,23 @@ BwdWorkspace bwd_workspace_layout(const moe_problem_t& p) {
     w.dgu_s = take(T * gu * wsw * es);
     w.dx_shared = take(T * d * es);
   }
+  w.ldt = wgrad_transposed_ld(p);
+  if (w.ldt > 0) {
+    w.kpad = take((N + 1) * 4);
+    w.dyT = take(d * (size_t)w.ldt * es);
+    w.dguT = take(gu * dff * (size_t)w.ldt * es);
+  }
   w.total = off;
   return w;
+}
+
+int wgrad_transposed_ld(const moe_problem_t& p) {
+  const long long rows = (long long)p.T * p.K;
+  if (rows < 512LL * p.N) return 0;            // short groups: the direct kernel
+  const long long ld = (rows + 63LL * p.N + 63) / 64 * 64;
+  // a 256-row tile of the transposed operand is addressed through one buffer
+  // descriptor, whose size is 32-bit: 256 * ld * 2 bytes stays below 2 GiB
+  return ld <= (1LL << 22) ? (int)ld : 0;
 }
 
 }  // namespace moe
@@ -465,6 +480,12 @@ int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_
   b.dw_gate = g->dw_gate;
   b.dw_up = g->dw_up;
   b.dw_down = g->dw_down;
+  if (L.ldt > 0) {
+    b.kpad = reinterpret_cast<int32_t*>(ws_at(ws, L.kpad));
+    b.dyT = ws_at(ws, L.dyT);
+    b.dguT = ws_at(ws, L.dguT);
+    b.ldt = L.ldt;
+  }
   if (shared) {
     b.u = u;
     b.d_out = d_out;

@@ -99,6 +99,11 @@ struct FfnBwdBuffers {
   void* dgu;                // [rows][2*d_ff] workspace (ReLU: [rows][d_ff])
   void* dx_perm;            // [rows][d]     gradients of the rows
   void *dw_gate, *dw_up, *dw_down;
+  // weight gradients in transposed form (null kpad: the direct k-major kernel)
+  int32_t* kpad;            // [N+1] workspace
+  void* dyT;                // [d][ldt] workspace
+  void* dguT;               // [2*d_ff][ldt] workspace (ReLU: [d_ff][ldt])
+  int ldt;
   // shared experts (n_shared > 0)
   const void* u;            // [T][d]
   const void* d_out;        // [T][d]
@@ -140,9 +145,17 @@ struct BwdWorkspace {
   size_t dA_s, act_s;  // elem [T][n_shared*d_ff_shared]
   size_t dgu_s;        // elem [T][2*n_shared*d_ff_shared]
   size_t dx_shared;    // elem [T][d]
+  size_t kpad;         // int32 [N+1]         (transposed weight gradients only)
+  size_t dyT;          // elem [d][ldt]
+  size_t dguT;         // elem [2*d_ff][ldt]  (ReLU: d_ff)
+  int ldt;             // 0: weight gradients by the direct k-major kernel
   size_t total;
 };
 BwdWorkspace bwd_workspace_layout(const moe_problem_t& p);
+// Leading dimension of the transposed weight-gradient operands (rows padded
+// per expert to a multiple of 64), or 0 when the experts' groups are too
+// short on average for the transposed form to pay.
+int wgrad_transposed_ld(const moe_problem_t& p);
 
 // expert choice (expert_choice.hip)
 hipError_t launch_ec_select(const moe_problem_t& p, const float* scores, int32_t C,
