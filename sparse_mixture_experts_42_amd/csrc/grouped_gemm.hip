@@ -589,16 +589,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   constexpr int OUT_TN = GATED ? TN / 2 : TN;
   const int col_base = n0 + (GATED ? wn * (WTN / 2) : wn * WTN) + (lane & 31);
   if constexpr (PIPE && EPI == EPI_SWIGLU_BWD) {
-    // Backward epilogue through LDS.  The dA tile is staged as bf16
-    // [BM][128] with 16-byte loads.  Neighbouring lanes swap one value of
-    // each accumulator pair in place, so that each lane holds two adjacent
-    // columns of one row (the even lane row r, the odd lane row r+1), and
-    // read the matching dA pair as one 4-byte word.  a, dG and dU are then
-    // produced one at a time, each packed as bf16 pairs into the same LDS
-    // region and written out in 16-byte row pieces.  16-byte chunk c of
-    // staged row r sits at slot c ^ 4*(r%2 + 2*(r/4 %2)), which keeps the
-    // pair accesses of one instruction (rows r, r+1, r+4, r+5) on disjoint
-    // banks.
+    // Backward epilogue.  The dA tile is staged in LDS as bf16 [BM][128] by
+    // direct loads.  Neighbouring lanes swap one value of each accumulator
+    // pair in place, so that each lane holds two adjacent columns of one
+    // row (the even lane row r, the odd lane row r+1), and read the matching
+    // dA pair as one 4-byte word.  a, dG and dU then go out as bf16 pairs.
+    // 16-byte chunk c of staged row r sits at slot c ^ 4*(r%2 + 2*(r/4 %2)),
+    // which keeps the pair reads of one instruction (rows r, r+1, r+4, r+5)
+    // on disjoint banks.
     static_assert(BM * 256 <= 2 * SAN * 16, "staged tile fits the A stages");
     static_assert(OUT_TN == 1, "one 32-column output block per wave");
     uint32_t* st = reinterpret_cast<uint32_t*>(&sA[0][0]);
@@ -649,45 +647,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
         const int r = pair_row(i, v);
         dap[i * 8 + v / 2] = st[r * 64 + slot(r, pc >> 3) * 4 + ((pc >> 1) & 3)];
       }
+    // a, dG and dU straight to global memory as bf16 pairs (4 bytes a lane),
+    // through buffer descriptors over the tile's rows: stores to rows past
+    // the group fall outside them and are dropped
+    const uint32_t lane_row = (uint32_t)(wm * WTM + 4 * (lane >> 5) + (odd ? 1 : 0));
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(C + (size_t)row0 * a.ldc + n0, (uint32_t)((size_t)rows * a.ldc * 2 - (size_t)n0 * 2));
+    const __amdgpu_buffer_rsrc_t rG =
+        make_rsrc(C2 + (size_t)row0 * a.ldc2 + n0, (uint32_t)((size_t)rows * a.ldc2 * 2 - (size_t)n0 * 2));
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(C2 + (size_t)row0 * a.ldc2 + a.Ndim + n0,
+                                                (uint32_t)((size_t)rows * a.ldc2 * 2 - (size_t)(a.Ndim + n0) * 2));
+    const bool col_ok = n0 + pc < a.Ndim;
+    const uint32_t vC = (lane_row * a.ldc + pc) * 2u, vG = (lane_row * a.ldc2 + pc) * 2u;
 #pragma unroll
-    for (int o = 0; o < 3; ++o) {
-      __syncthreads();             // the staged dA / the last output is fully read
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int v = 0; v < 16; v += 2) {
+        const uint32_t dp = dap[i * 8 + v / 2];
+        f32x2 pa, pg, pu;
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const uint32_t dp = dap[i * 8 + v / 2];
-          f32x2 pr;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            float gv = acc[i][0][v + q];
-            const float uv = acc[i][TN / 2][v + q];
-            // recompute the gate terms in each round rather than keep them
-            // live across all three (an empty asm hides gv's value)
-            asm volatile("" : "+v"(gv));
-            const float sg = sigmoid_fast(gv);
-            const float sl = gv * sg;
-            const float da = __builtin_bit_cast(float, q ? (dp & 0xffff0000u) : (dp << 16));
-            if (o == 0) pr[q] = sl * uv;
-            else if (o == 1) pr[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
-            else pr[q] = da * sl;
-          }
-          const int r = pair_row(i, v);
-          st[r * 64 + slot(r, pc >> 3) * 4 + ((pc >> 1) & 3)] =
-              __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        for (int q = 0; q < 2; ++q) {
+          const float gv = acc[i][0][v + q], uv = acc[i][TN / 2][v + q];
+          const float sg = sigmoid_fast(gv);
+          const float sl = gv * sg;
+          const float da = __builtin_bit_cast(float, q ? (dp & 0xffff0000u) : (dp << 16));
+          pa[q] = sl * uv;
+          pg[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
+          pu[q] = da * sl;
         }
-      __syncthreads();
-      uint16_t* dst = o == 0 ? C : C2;
-      const int ld = o == 0 ? a.ldc : a.ldc2;
-      const int cofs = o == 2 ? a.Ndim : 0;           // dU follows dG in each row of C2
-#pragma unroll 2
-      for (int id = tid; id < BM * 16; id += NW * 64) {
-        const int r = id >> 4, ch = id & 15;
-        const int col = n0 + 8 * ch;
-        if (r < rows && col < a.Ndim)
-          *reinterpret_cast<u32x4*>(dst + (size_t)(row0 + r) * ld + cofs + col) = stv[r * 16 + slot(r, ch)];
+        if (!col_ok) continue;
+        const int rr = 32 * i + 8 * (v >> 2) + (v & 3);   // uniform part of the row
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, __builtin_convertvector(pa, bf16x2)),
+                                              rC, vC, rr * a.ldc * 2, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, __builtin_convertvector(pg, bf16x2)),
+                                              rG, vG, rr * a.ldc2 * 2, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, __builtin_convertvector(pu, bf16x2)),
+                                              rU, vG, rr * a.ldc2 * 2, 0);
       }
-    }
     return;
   }
   if constexpr (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) {
