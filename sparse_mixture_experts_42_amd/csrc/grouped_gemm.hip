@@ -1075,28 +1075,79 @@ __global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
 }
 
 // --------------------------------------------------------------- fp32
-// Plain fp32 path (one thread per output element), for fp32 problems.
+// fp32 problems (the small fp32 configuration): a plain LDS-tiled kernel on
+// the vector ALUs.  One 256-thread block per 32-row x 64-column output tile
+// of one group; K advances 32 at a time through LDS, loaded along k
+// (contiguous in both operands).  Thread (ty, tx) accumulates rows ty and
+// ty+16, columns tx + 16j, for gate (and up) weights.
+constexpr int kF32Rows = 32;
+
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs a, int BMr) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  __shared__ float sa[kF32Rows][33];
+  __shared__ float sg[64][33];
+  __shared__ float su[GATED ? 64 : 1][33];
   int g, row0, rows;
   if (!find_tile(a, blockIdx.x, BMr, g, row0, rows)) return;
-  const int col = blockIdx.y * 256 + threadIdx.x;
-  if (col >= a.Ndim) return;
+  const int n0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const float* A = static_cast<const float*>(a.A);
   const float* Bg = static_cast<const float*>(a.B0) + (size_t)g * a.b_group_stride;
-  const float* Bu = EPI == EPI_SWIGLU ? static_cast<const float*>(a.B1) + (size_t)g * a.b_group_stride
-                                      : nullptr;
-  float* C = static_cast<float*>(a.C);
-  for (int r = 0; r < rows; ++r) {
-    const float* x = A + (size_t)(row0 + r) * a.lda;
-    float s0 = 0.0f, s1 = 0.0f;
-    for (int k = 0; k < a.Kdim; ++k) {
-      const int seg = k / a.kseg;
-      const size_t off = (size_t)seg * a.kseg_stride + (size_t)col * a.ldb + (k - seg * a.kseg);
-      s0 = fmaf(x[k], Bg[off], s0);
-      if (EPI == EPI_SWIGLU) s1 = fmaf(x[k], Bu[off], s1);
+  const float* Bu = GATED ? static_cast<const float*>(a.B1) + (size_t)g * a.b_group_stride : nullptr;
+  float acc[2][4], accu[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = accu[i][j] = 0.0f;
+  for (int k0 = 0; k0 < a.Kdim; k0 += 32) {
+    // A: 32 rows x 32 k (4 a thread); B: 64 columns x 32 k (8 a thread)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q, r = e >> 5, kk = e & 31, k = k0 + kk;
+      sa[r][kk] = r < rows && k < a.Kdim ? A[(size_t)(row0 + r) * a.lda + k] : 0.0f;
     }
-    C[(size_t)(row0 + r) * a.ldc + col] = epilogue<EPI>(s0, s1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = tid + 256 * q, c = e >> 5, kk = e & 31, k = k0 + kk, col = n0 + c;
+      float vg = 0.0f, vu = 0.0f;
+      if (col < a.Ndim && k < a.Kdim) {
+        const int seg = k / a.kseg;
+        const size_t off = (size_t)seg * a.kseg_stride + (size_t)col * a.ldb + (k - seg * a.kseg);
+        vg = Bg[off];
+        if constexpr (GATED) vu = Bu[off];
+      }
+      sg[c][kk] = vg;
+      if constexpr (GATED) su[c][kk] = vu;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      const float x0 = sa[ty][kk], x1 = sa[ty + 16][kk];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = sg[tx + 16 * j][kk];
+        acc[0][j] = fmaf(x0, w, acc[0][j]);
+        acc[1][j] = fmaf(x1, w, acc[1][j]);
+        if constexpr (GATED) {
+          const float wu = su[tx + 16 * j][kk];
+          accu[0][j] = fmaf(x0, wu, accu[0][j]);
+          accu[1][j] = fmaf(x1, wu, accu[1][j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* C = static_cast<float*>(a.C);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = ty + 16 * i;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx + 16 * j;
+      if (col < a.Ndim) C[(size_t)(row0 + r) * a.ldc + col] = epilogue<EPI>(acc[i][j], accu[i][j]);
+    }
   }
 }
 
@@ -1156,7 +1207,7 @@ hipError_t run_gemm(const GemmArgs& a, int epi, bool bf16, int bm, int mtiles, h
       default: return launch_bf16<EPI_NONE>(a, bm, mtiles, s);
     }
   }
-  dim3 grid(mtiles, (a.Ndim + 255) / 256);
+  dim3 grid(mtiles, (a.Ndim + 63) / 64);
   switch (epi) {
     case EPI_SWIGLU:
       hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, a, bm);
@@ -1181,9 +1232,9 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
                               hipStream_t s) {
   const bool bf16 = p.dtype == MOE_BF16;
   const int epi1 = p.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
-  // fp32 problems: one block per 128 rows; bf16: tiles sized to the mean
+  // fp32 problems: one block per 32 rows; bf16: tiles sized to the mean
   // group (all groups share one tile height so the plan is one prefix sum)
-  const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : 128;
+  const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : kF32Rows;
   const int tail_rows = bf16 && bm == 256 ? kTailRows : 0;
   const int ext_rows = bf16 && bm == 256 ? kExtRows : 0;
   // grid bound: at most rows/bm + 1 full tiles and one tail tile per group
@@ -1237,7 +1288,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     // gate/up rows of consecutive experts are contiguous; the down
     // projection is K-segmented, one segment per shared expert
     const int ws_w = p.n_shared * p.d_ff_shared;
-    const int sbm = bf16 ? pick_tiles(p.T).bm : 128;
+    const int sbm = bf16 ? pick_tiles(p.T).bm : kF32Rows;
     const int s_tail = bf16 && sbm == 256 ? kTailRows : 0;
     const int s_ext = bf16 && sbm == 256 ? kExtRows : 0;
     int mt = (p.T + sbm - 1) / sbm;
