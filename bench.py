@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
-PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (256 CUs x 128 FMA lanes x 2 x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec + grouped-GEMM % of bf16 MFMA peak (Mixtral-shaped)"
 
@@ -334,7 +334,8 @@ def main():
     achieved = flops / (stages_ms["grouped_ffn"] * 1e-3) / 1e12
     if mfma_ref is not None and w.dtype == "bf16":
         mfma_ref["grouped_gemm_frac_of_this"] = round(achieved / mfma_ref["tflops"], 4)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+    # the fp32 experts run on the vector ALUs (LDS-tiled FMA), not the matrix cores
+    roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name),
                 "kernel": "grouped expert GEMMs (moe_grouped_ffn: gate/up GEMM + down GEMM)",
                 "flops_per_call": flops, "rows": R}

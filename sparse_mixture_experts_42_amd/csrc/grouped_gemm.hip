@@ -803,6 +803,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_small_kernel(GemmArgs a
   gemm_tile<EPI, 32, 256, 1, 4, 32 * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
 }
 
+// Groups of a few hundred rows (e.g. a Switch-shaped layer with capacity
+// 640): 128x256 tiles on 8 waves of 64x64, so a narrow output (few column
+// tiles) still spreads over more CUs than 256-row tiles would.
+template <int EPI, bool BT = false>
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_mid_kernel(GemmArgs a) {
+  __shared__ u32x4 sA[2][128 * 8];
+  __shared__ u32x4 sB[2][256 * 8];
+  constexpr int BNH = gated<EPI>() ? 128 : 256;
+  const int ntiles = (a.Ndim + BNH - 1) / BNH;
+  const int real = full_tiles_total(a, 128) * ntiles;
+  const int h = blockIdx.x;
+  if (h >= real) return;
+  int g, row0, rows, by;
+  find_tile_2d(a, 128, ntiles, h, real, g, row0, rows, by);
+  gemm_tile<EPI, 128, 256, 2, 4, 128 * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
+}
+
 // ------------------------------------------------------ weight gradients
 // dW = A^T B per group, reducing over the group's rows: A [rows][lda]
 // supplies the output rows m (its columns), B [rows][ldb] the output
@@ -1182,11 +1199,12 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, 
 }
 
 // Tile shape per problem: large groups use 256x256 tiles (8 waves of
-// 128x64); groups of a few rows (decode-sized batches) use 32-row tiles so the
-// matrix cores do not multiply mostly-empty rows.
+// 128x64); groups of a few hundred rows use 128-row tiles, which double the
+// number of blocks; groups of a few rows (decode-sized batches) use 32-row
+// tiles so the matrix cores do not multiply mostly-empty rows.
 struct TileShape { int bm; };
 
-TileShape pick_tiles(int rows_per_group) { return TileShape{rows_per_group >= 128 ? 256 : 32}; }
+TileShape pick_tiles(int rows_per_group) { return TileShape{rows_per_group >= 1024 ? 256 : rows_per_group >= 128 ? 128 : 32}; }
 
 template <int EPI, bool BT = false>
 hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
@@ -1194,6 +1212,8 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
   dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
   if (bm == 256)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
+  else if (bm == 128)
+    hipLaunchKernelGGL((grouped_gemm_bf16_mid_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_small_kernel<EPI, BT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
