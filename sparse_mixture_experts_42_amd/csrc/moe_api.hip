@@ -90,7 +90,7 @@ BwdWorkspace bwd_workspace_layout(const moe_problem_t& p) {
   w.dx_perm = take(rows * d * es);
   w.d_gate = take(T * K * 4);
   w.dH = take(T * N * 4);
-  w.partial = take((size_t)router_grad_slices(p.T) * N * (d + 1) * 4);
+  w.partial = take((size_t)router_grad_slices(p.T, N) * N * (d + 1) * 4);
   if (p.n_shared > 0) {
     w.dA_s = take(T * wsw * es);
     w.act_s = take(T * wsw * es);

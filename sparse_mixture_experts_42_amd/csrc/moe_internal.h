@@ -118,7 +118,7 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc,
                                        const FfnBwdBuffers& b, hipStream_t s);
 
 // backward, apart from the expert GEMMs (backward.hip)
-int router_grad_slices(int T);
+int router_grad_slices(int T, int N);
 hipError_t launch_combine_backward(const moe_problem_t& p, const void* d_out, const void* y_perm,
                                    const int32_t* row_of, const float* gate, void* dy_perm,
                                    float* d_gate, hipStream_t s);

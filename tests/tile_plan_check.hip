@@ -62,6 +62,7 @@ int main() {
     for (auto& x : s) { int k = rng() % 4; x = k == 0 ? rng() % 70 : k == 1 ? 256 * (rng() % 9) + rng() % 80 : rng() % 3000; }
     int nt = 1 + rng() % 40;
     fails += check(s, nt, false, 256, 64, 64); ++n;
+    fails += check(s, nt, false, 128, 0, 0); ++n;
     fails += check(s, nt, false, 32, 0, 0); ++n;
   }
   printf("%d cases, %d failures\n", n, fails);
