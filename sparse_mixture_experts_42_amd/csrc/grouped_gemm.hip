@@ -820,6 +820,22 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_mid_kernel(GemmArgs a) 
   gemm_tile<EPI, 128, 256, 2, 4, 128 * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
 }
 
+// The plain down projection of mid-sized groups: 128x128 tiles on 8 waves of
+// 32x64 (the unpipelined tile body), twice the blocks of 128x256 tiles for an
+// output with few column tiles (d = 768 has three of 256).
+template <int EPI>
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_mid_narrow_kernel(GemmArgs a) {
+  __shared__ u32x4 sA[2][128 * 8];
+  __shared__ u32x4 sB[2][128 * 8];
+  const int ntiles = (a.Ndim + 127) / 128;
+  const int real = full_tiles_total(a, 128) * ntiles;
+  const int h = blockIdx.x;
+  if (h >= real) return;
+  int g, row0, rows, by;
+  find_tile_2d(a, 128, ntiles, h, real, g, row0, rows, by);
+  gemm_tile<EPI, 128, 128, 4, 2, 128 * 8, 128 * 8>(a, g, row0, rows, by, sA, sB);
+}
+
 // ------------------------------------------------------ weight gradients
 // dW = A^T B per group, reducing over the group's rows: A [rows][lda]
 // supplies the output rows m (its columns), B [rows][ldb] the output
@@ -1212,8 +1228,13 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
   dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
   if (bm == 256)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
-  else if (bm == 128)
-    hipLaunchKernelGGL((grouped_gemm_bf16_mid_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
+  else if (bm == 128) {
+    if constexpr (EPI == EPI_NONE && !BT)
+      hipLaunchKernelGGL((grouped_gemm_bf16_mid_narrow_kernel<EPI>),
+                         dim3(mtiles * ((a.Ndim + 127) / 128)), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((grouped_gemm_bf16_mid_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
+  }
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_small_kernel<EPI, BT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
