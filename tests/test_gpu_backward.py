@@ -117,7 +117,10 @@ def _check_weight_grads(w, po, xi, x, t, ro, dsp, dO, experts, f_of, shared_f=No
     (129, 16, 4, "topk_softmax", "relu", 0.0, 1),
     (560, 2, 2, "topk_softmax", "swiglu", 0.0, 0),
     (64, 32, 2, "softmax_topk", "swiglu", 0.0, 1),
-    (1, 4, 2, "softmax_topk", "swiglu", 0.0, 1)])
+    (1, 4, 2, "softmax_topk", "swiglu", 0.0, 1),
+    # router weight gradient over 256-token slices (wide router, long
+    # batch), the last slice ragged
+    (1100, 12, 2, "softmax_topk", "swiglu", 0.0, 0)])
 def test_backward_small_shapes(T, N, K, gating, act, cf, shared):
     """Every gradient and intermediate against the oracle: 560 rows over two
     experts run 320-row tiles; 64 tokens over 32 experts run 32-row tiles."""
