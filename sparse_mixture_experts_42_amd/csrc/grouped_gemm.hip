@@ -869,46 +869,61 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
   constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2, PER = 32 / NW;
   const int mtn = (a.M + 255) / 256, ntn = (a.N + 255) / 256;
   const int per_g = mtn * ntn, total = a.G * per_g;
-  // Persistent: block b takes tiles b, b + gridDim, ...; a tile's output
-  // stores then drain while the block already streams the next tile's
-  // operands.  XCD-contiguous runs of tiles (consecutive blocks go to
-  // different XCDs; gridDim is a multiple of 8, so a block stays on one).
+  // XCD-contiguous runs of tiles (consecutive blocks go to different XCDs;
+  // gridDim is a multiple of 8, so a block stays on one).
   const int full = total - total % 8;
-  for (int h = blockIdx.x; h < total; h += gridDim.x) {
-  const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
-  const int g = __builtin_amdgcn_readfirstlane(L / per_g);
-  const int rem = L - g * per_g;
-  const int mt = __builtin_amdgcn_readfirstlane(rem / ntn);
-  const int nt = __builtin_amdgcn_readfirstlane(rem - mt * ntn);
-  const int r0 = __builtin_amdgcn_readfirstlane(a.offsets ? a.offsets[g] : 0);
-  const int rows = __builtin_amdgcn_readfirstlane(a.offsets ? a.offsets[g + 1] - r0 : a.Krows);
-  const int m0 = mt * 256, n0 = nt * 256;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  const long long abytes = ((long long)rows * a.lda - m0) * 2;
-  const long long bbytes = ((long long)rows * a.ldb - n0) * 2;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-      static_cast<const uint16_t*>(a.A) + (size_t)r0 * a.lda + m0, (uint32_t)(abytes > 0 ? abytes : 0));
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(
-      static_cast<const uint16_t*>(a.B) + (size_t)r0 * a.ldb + n0, (uint32_t)(bbytes > 0 ? bbytes : 0));
   lds_t* ldsA[2] = {(lds_t*)&sA[0][wave * PER * 64], (lds_t*)&sA[1][wave * PER * 64]};
   lds_t* ldsB[2] = {(lds_t*)&sB[0][wave * PER * 64], (lds_t*)&sB[1][wave * PER * 64]};
 
-  auto issue = [&](int kt, int buf) {
+  // tile h: group, output tile origin, the group's rows and operand descriptors
+  struct Tile {
+    int g, m0, n0, rows;
+    __amdgpu_buffer_rsrc_t rA, rB;
+  };
+  auto setup = [&](int h) __attribute__((always_inline)) {
+    Tile t;
+    const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
+    t.g = __builtin_amdgcn_readfirstlane(L / per_g);
+    const int rem = L - t.g * per_g;
+    const int mt = __builtin_amdgcn_readfirstlane(rem / ntn);
+    const int nt = __builtin_amdgcn_readfirstlane(rem - mt * ntn);
+    const int r0 = __builtin_amdgcn_readfirstlane(a.offsets ? a.offsets[t.g] : 0);
+    t.rows = __builtin_amdgcn_readfirstlane(a.offsets ? a.offsets[t.g + 1] - r0 : a.Krows);
+    t.m0 = mt * 256;
+    t.n0 = nt * 256;
+    const long long abytes = ((long long)t.rows * a.lda - t.m0) * 2;
+    const long long bbytes = ((long long)t.rows * a.ldb - t.n0) * 2;
+    t.rA = make_rsrc(static_cast<const uint16_t*>(a.A) + (size_t)r0 * a.lda + t.m0,
+                     (uint32_t)(abytes > 0 ? abytes : 0));
+    t.rB = make_rsrc(static_cast<const uint16_t*>(a.B) + (size_t)r0 * a.ldb + t.n0,
+                     (uint32_t)(bbytes > 0 ? bbytes : 0));
+    return t;
+  };
+  auto issue = [&](const Tile& t, int kt, int buf) __attribute__((always_inline)) {
     const uint32_t ka = (uint32_t)kt * BK * (uint32_t)a.lda * 2u;
     const uint32_t kb = (uint32_t)kt * BK * (uint32_t)a.ldb * 2u;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rA, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
                                                kmajor_voff(wave * PER + i, lane, a.lda) + ka, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rB, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
                                                kmajor_voff(wave * PER + i, lane, a.ldb) + kb, 0, 0, 0);
   };
 
+  // Persistent: block b takes tiles b, b + gridDim, ...  A tile's first
+  // operand stage is issued during the previous tile's epilogue, before
+  // that tile's output stores, so the load latency and the store drain
+  // overlap (one counter covers both on this target).
+  int h = blockIdx.x;
+  if (h >= total) return;
+  Tile t = setup(h);
+  if (t.rows > 0) issue(t, 0, 0);
+  for (; h < total; h += gridDim.x) {
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -917,15 +932,12 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = (rows + BK - 1) / BK;
-  if (nk > 0) {
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  const int nk = (t.rows + BK - 1) / BK;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+    if (kt + 1 < nk) issue(t, kt + 1, buf ^ 1);
     const char* tA = (const char*)&sA[buf][0];
     const char* tB = (const char*)&sB[buf][0];
     bf16x8 fa[2][TM], fb[2][TN];
@@ -976,18 +988,31 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
         stile[r * 128 + (c >> 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
       }
   __syncthreads();
+  constexpr int kOut = 256 * 32 / 512;        // 16-byte pieces per thread
+  u32x4 outv[kOut];
   const u32x4* vt = &smem[0][0];
-#pragma unroll 4
-  for (int id = tid; id < 256 * 32; id += 512) {
+#pragma unroll
+  for (int it = 0; it < kOut; ++it) outv[it] = vt[tid + 512 * it];
+  __syncthreads();                 // the tile's LDS reads are done
+  const Tile cur = t;
+  if (h + (int)gridDim.x < total) {
+    t = setup(h + gridDim.x);
+    if (t.rows > 0) issue(t, 0, 0);
+  }
+  uint16_t* out0 = static_cast<uint16_t*>(a.C) + (size_t)cur.g * a.c_group_stride;
+  uint16_t* out1 =
+      a.C2 != nullptr ? static_cast<uint16_t*>(a.C2) + (size_t)cur.g * a.c_group_stride : nullptr;
+#pragma unroll
+  for (int it = 0; it < kOut; ++it) {
+    const int id = tid + 512 * it;
     const int r = id >> 5, cv = id & 31;
-    const int m = m0 + r, n = n0 + 8 * cv;
+    const int m = cur.m0 + r, n = cur.n0 + 8 * cv;
     if (m >= a.M || n >= a.N) continue;
-    uint16_t* out = static_cast<uint16_t*>(m < a.msplit ? a.C : a.C2) + (size_t)g * a.c_group_stride;
+    uint16_t* out = m < a.msplit ? out0 : out1;
     const int mr = m < a.msplit ? m : m - a.msplit;
     const size_t ncol = (size_t)(n / a.nseg) * a.nseg_stride + (size_t)(n % a.nseg);
-    *reinterpret_cast<u32x4*>(out + (size_t)mr * a.ldc + ncol) = vt[id];
+    *reinterpret_cast<u32x4*>(out + (size_t)mr * a.ldc + ncol) = outv[it];
   }
-  __syncthreads();                 // the tile's LDS reads are done
   }  // tiles
 }
 
