@@ -820,20 +820,32 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_mid_kernel(GemmArgs a) 
   gemm_tile<EPI, 128, 256, 2, 4, 128 * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
 }
 
-// The plain down projection of mid-sized groups: 128x128 tiles on 8 waves of
-// 32x64 (the unpipelined tile body), twice the blocks of 128x256 tiles for an
-// output with few column tiles (d = 768 has three of 256).
+// The plain down projection of mid-sized groups: the 128-row tiles of the
+// plan, 128 columns wide, each split into two 64-row blocks on 8 waves of
+// 32x32 (the unpipelined tile body).  An output with few column tiles
+// (d = 768 has three of 256) then still spreads over every CU, and the
+// 48 KB of LDS per block lets three blocks share a CU.
 template <int EPI>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_mid_narrow_kernel(GemmArgs a) {
-  __shared__ u32x4 sA[2][128 * 8];
+  __shared__ u32x4 sA[2][64 * 8];
   __shared__ u32x4 sB[2][128 * 8];
   const int ntiles = (a.Ndim + 127) / 128;
   const int real = full_tiles_total(a, 128) * ntiles;
-  const int h = blockIdx.x;
+  // blocks [0, real) take the upper 64 rows of each 128-row tile, blocks
+  // [real, 2 real) the lower 64
+  int h = blockIdx.x, half = 0;
+  if (h >= real) {
+    h -= real;
+    half = 1;
+  }
   if (h >= real) return;
   int g, row0, rows, by;
   find_tile_2d(a, 128, ntiles, h, real, g, row0, rows, by);
-  gemm_tile<EPI, 128, 128, 4, 2, 128 * 8, 128 * 8>(a, g, row0, rows, by, sA, sB);
+  row0 += 64 * half;
+  rows -= 64 * half;
+  if (rows <= 0) return;
+  if (rows > 64) rows = 64;
+  gemm_tile<EPI, 64, 128, 2, 4, 64 * 8, 128 * 8>(a, g, row0, rows, by, sA, sB);
 }
 
 // ------------------------------------------------------ weight gradients
@@ -1256,7 +1268,7 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
   else if (bm == 128) {
     if constexpr (EPI == EPI_NONE && !BT)
       hipLaunchKernelGGL((grouped_gemm_bf16_mid_narrow_kernel<EPI>),
-                         dim3(mtiles * ((a.Ndim + 127) / 128)), dim3(512), 0, s, a);
+                         dim3(2 * mtiles * ((a.Ndim + 127) / 128)), dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL((grouped_gemm_bf16_mid_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
   }
