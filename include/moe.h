@@ -115,6 +115,18 @@ size_t moe_workspace_size(const moe_problem_t* p);
  * entry; the K factor counts each (token, expert) assignment. */
 int32_t moe_capacity(int32_t T, int32_t K, int32_t N, float cf);
 
+/* Row-tile height of the grouped expert GEMMs (moe_grouped_ffn, the
+ * forward and backward passes) over `rows` rows of x_perm split into
+ * `groups` expert groups: rows = T*K and groups = N for the routed experts of
+ * token choice, rows = N*C for expert choice, rows = T and groups = 1 for the
+ * shared experts.  bf16 problems: 256 when the mean group has at least 1024
+ * rows (a group's last tile then grows to 320 rows when the group ends at
+ * most 64 rows past a multiple of 256, and a group of at most 64 rows gets a
+ * 64-row tile), 128 from 128 rows, else 32; fp32 problems: 32.  A planning
+ * query with no device work: callers and tests use it to know which kernel
+ * a shape reaches.  Returns -1 for rows < 0, groups <= 0 or an unknown dtype. */
+int32_t moe_ffn_row_tile(int32_t rows, int32_t groups, int32_t dtype);
+
 /* Stage 1 -- router.
  * scores H[t][i] = fp32(sum_j u[t][j] w_router[i][j] + b_router[i]) then
  *   H = fmaf(W_noise, noise[t][i], H) if noise != NULL ("Noise Top-k

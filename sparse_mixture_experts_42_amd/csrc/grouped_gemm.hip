@@ -1302,6 +1302,10 @@ hipError_t run_gemm(const GemmArgs& a, int epi, bool bf16, int bm, int mtiles, h
 
 }  // namespace
 
+int ffn_row_tile(int rows, int groups, bool bf16) {
+  return bf16 ? pick_tiles(rows / groups).bm : kF32Rows;
+}
+
 hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void* x_perm,
                               const int32_t* offsets, const void* w_gate, const void* w_up,
                               const void* w_down, const void* u, const void* ws_gate,
@@ -1312,7 +1316,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   const int epi1 = p.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
   // fp32 problems: one block per 32 rows; bf16: tiles sized to the mean
   // group (all groups share one tile height so the plan is one prefix sum)
-  const int bm = bf16 ? pick_tiles(rows_alloc / p.N).bm : kF32Rows;
+  const int bm = ffn_row_tile(rows_alloc, p.N, bf16);
   const int tail_rows = bf16 && bm == 256 ? kTailRows : 0;
   const int ext_rows = bf16 && bm == 256 ? kExtRows : 0;
   // grid bound: at most rows/bm + 1 full tiles and one tail tile per group
@@ -1366,7 +1370,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     // gate/up rows of consecutive experts are contiguous; the down
     // projection is K-segmented, one segment per shared expert
     const int ws_w = p.n_shared * p.d_ff_shared;
-    const int sbm = bf16 ? pick_tiles(p.T).bm : kF32Rows;
+    const int sbm = ffn_row_tile(p.T, 1, bf16);
     const int s_tail = bf16 && sbm == 256 ? kTailRows : 0;
     const int s_ext = bf16 && sbm == 256 ? kExtRows : 0;
     int mt = (p.T + sbm - 1) / sbm;
@@ -1503,7 +1507,7 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
                                        hipStream_t s) {
   const bool swiglu = p.act == MOE_ACT_SWIGLU;
   const int dff = p.d_ff, d = p.d;
-  const int bm = pick_tiles(rows_alloc / p.N).bm;
+  const int bm = ffn_row_tile(rows_alloc, p.N, true);
   const int tail_rows = bm == 256 ? kTailRows : 0;
   const int ext_rows = bm == 256 ? kExtRows : 0;
   const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N + (tail_rows > 0 ? p.N : 0);
@@ -1601,7 +1605,7 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   if (p.n_shared == 0) return hipSuccess;
   // shared experts over all T tokens, dY = d_out
   const int dffs = p.d_ff_shared, wsw = p.n_shared * dffs;
-  const int sbm = pick_tiles(p.T).bm;
+  const int sbm = ffn_row_tile(p.T, 1, true);
   const int s_tail = sbm == 256 ? kTailRows : 0;
   const int s_ext = sbm == 256 ? kExtRows : 0;
   int mt = (p.T + sbm - 1) / sbm;

@@ -147,6 +147,13 @@ int check_problem(const moe_problem_t* p) {
   if (rows > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if ((long long)p->n_shared * p->d_ff_shared > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if ((long long)p->d * p->d_ff > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  // the grouped GEMMs address a row tile (at most 320 rows) of an operand
+  // through a buffer descriptor whose size field is 32 bits
+  long long ld = p->d;
+  const long long gu = p->act == MOE_ACT_SWIGLU ? 2 : 1;
+  if (gu * p->d_ff > ld) ld = gu * p->d_ff;
+  if (gu * p->n_shared * (long long)p->d_ff_shared > ld) ld = gu * p->n_shared * (long long)p->d_ff_shared;
+  if (320LL * ld * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -265,6 +272,11 @@ int32_t moe_capacity(int32_t T, int32_t K, int32_t N, float cf) {
   double c = ceil((double)cf * (double)((int64_t)T * K) / (double)N);
   if (c > (double)T) c = (double)T;
   return (int32_t)c;
+}
+
+int32_t moe_ffn_row_tile(int32_t rows, int32_t groups, int32_t dtype) {
+  if (rows < 0 || groups <= 0 || (dtype != MOE_F32 && dtype != MOE_BF16)) return -1;
+  return moe::ffn_row_tile(rows, groups, dtype == MOE_BF16);
 }
 
 int moe_route(const moe_problem_t* p, const void* u, const float* w_router,

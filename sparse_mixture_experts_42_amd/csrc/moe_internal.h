@@ -74,6 +74,10 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                            void* x_perm, int32_t* blk_count, int32_t* blk_base,
                            int32_t* level_q, int disp_blocks, hipStream_t s);
 
+// Row-tile height of the grouped GEMMs over `rows` rows in `groups` groups
+// (the mean group size picks the kernel family).
+int ffn_row_tile(int rows, int groups, bool bf16);
+
 // rows_alloc: rows of x_perm / y_perm / act (T*K for token choice).
 hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void* x_perm,
                               const int32_t* offsets, const void* w_gate, const void* w_up,

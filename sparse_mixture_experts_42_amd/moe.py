@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
             L.moe_workspace_size.restype = sz
             L.moe_capacity.argtypes = [i32, i32, i32, ctypes.c_float]
             L.moe_capacity.restype = i32
+            L.moe_ffn_row_tile.argtypes = [i32, i32, i32]
+            L.moe_ffn_row_tile.restype = i32
             L.moe_route.argtypes = [P] + [vp] * 10 + [sz, vp]
             L.moe_dispatch.argtypes = [P] + [vp] * 9 + [sz, vp]
             L.moe_grouped_ffn.argtypes = [P] + [vp] * 12 + [sz, vp]
@@ -154,6 +156,11 @@ def moe_workspace_size(p: MoeProblem) -> int:
 
 def moe_capacity(T: int, K: int, N: int, cf: float) -> int:
     return int(lib().moe_capacity(int(T), int(K), int(N), float(cf)))
+
+
+def moe_ffn_row_tile(rows: int, groups: int, dtype="bf16") -> int:
+    """Row-tile height of the grouped GEMMs over `rows` rows in `groups` groups."""
+    return int(lib().moe_ffn_row_tile(int(rows), int(groups), int(DTYPE.get(dtype, dtype))))
 
 
 # ------------------------------------------------------------------ helpers
@@ -350,6 +357,7 @@ def moe_layer_forward(p: MoeProblem, u, noise, weights: MoeWeights, bufs: LayerB
     _call("moe_layer_forward", ctypes.byref(p), _ptr(u), _ptr(noise), ctypes.byref(weights),
           ctypes.byref(bufs.c), _ptr(bufs.t["out"]), _ptr(ws), ws.numel(), _stream(dev))
     return bufs.t["out"]
+
 
 
 def layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], want_scores=True) -> Dict[str, torch.Tensor]:

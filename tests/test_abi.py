@@ -108,9 +108,34 @@ def test_workspace_size():
     (dict(d=96), M.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=100), M.MOE_ERR_UNSUPPORTED),
     (dict(n_shared=1, d_ff_shared=100), M.MOE_ERR_UNSUPPORTED),
+    # a 320-row tile of the widest GEMM operand must stay below 2^32 bytes
+    # (the buffer descriptors' size field): 320 * 2 * d_ff * 2 bytes here
+    (dict(d_ff=3355456), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=3355456, act="relu"), M.MOE_ERR_WORKSPACE),
+    (dict(d=6710912, d_ff=64), M.MOE_ERR_UNSUPPORTED),
+    (dict(d=6710848, d_ff=64), M.MOE_ERR_WORKSPACE),
+    (dict(n_shared=2, d_ff_shared=1677728), M.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_checks(over, status):
     assert route_call(good(**over)) == status
+
+
+def test_ffn_row_tile():
+    """The tile-height query: the mean group size picks 256-, 128- or
+    32-row tiles for bf16, 32-row blocks for fp32; bad arguments give -1."""
+    assert M.moe_ffn_row_tile(8192 * 2, 8) == 256        # Mixtral-shaped
+    assert M.moe_ffn_row_tile(16384 * 6, 64) == 256      # DeepSeekMoE-shaped
+    assert M.moe_ffn_row_tile(4096, 8) == 128            # Switch-shaped
+    assert M.moe_ffn_row_tile(128 * 8, 128) == 32        # decode-sized
+    assert M.moe_ffn_row_tile(1024 * 12, 12) == 256
+    assert M.moe_ffn_row_tile(1024 * 12 - 1, 12) == 128
+    assert M.moe_ffn_row_tile(128 * 5, 5) == 128
+    assert M.moe_ffn_row_tile(128 * 5 - 1, 5) == 32
+    assert M.moe_ffn_row_tile(3100, 1) == 256            # shared experts over 3100 tokens
+    assert M.moe_ffn_row_tile(256 * 2, 4, "f32") == 32
+    assert M.moe_ffn_row_tile(-1, 4) == -1
+    assert M.moe_ffn_row_tile(10, 0) == -1
+    assert M.moe_ffn_row_tile(10, 1, 7) == -1
 
 
 def test_route_argument_checks():
@@ -278,3 +303,4 @@ def test_backward_checks_before_launch():
     g.dws_down = None     # shared experts need their gradients
     assert call(q, W_, S_, G_, 1 << 40) == M.MOE_ERR_INVALID_ARG
     assert call(good(T=0), W_, S_, G_, 0) == M.MOE_OK
+

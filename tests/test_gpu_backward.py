@@ -117,16 +117,22 @@ def _check_weight_grads(w, po, xi, x, t, ro, dsp, dO, experts, f_of, shared_f=No
     (129, 16, 4, "topk_softmax", "relu", 0.0, 1),
     (560, 2, 2, "topk_softmax", "swiglu", 0.0, 0),
     (64, 32, 2, "softmax_topk", "swiglu", 0.0, 1),
+    (1300, 2, 2, "topk_softmax", "swiglu", 0.0, 0),
     (1, 4, 2, "softmax_topk", "swiglu", 0.0, 1),
     # router weight gradient over 256-token slices (wide router, long
     # batch), the last slice ragged
     (1100, 12, 2, "softmax_topk", "swiglu", 0.0, 0)])
 def test_backward_small_shapes(T, N, K, gating, act, cf, shared):
-    """Every gradient and intermediate against the oracle: 560 rows over two
-    experts run 320-row tiles; 64 tokens over 32 experts run 32-row tiles."""
+    """Every gradient and intermediate against the oracle.  The mean group
+    T*K/N picks the GEMM tiles: 1300 tokens on both of two experts give two
+    groups of 1300 rows (256-row tiles, each group's last tile extended by
+    20 rows); 560 rows over two experts and 300 over six run 128-row tiles;
+    64 tokens over 32 experts run 32-row tiles."""
     w = W.Workload("bwd", T=T, d=128, N=N, K=K, d_ff=192, gating=gating, act=act,
                    capacity_factor=cf, n_shared=shared, d_ff_shared=64 if shared else 0,
                    seed=T * 17 + N, noise=True, noise_weight=0.5, bias="zipf")
+    want = 256 if T * K >= 1024 * N else 128 if T * K >= 128 * N else 32
+    assert M.moe_ffn_row_tile(T * K, N) == want
     say(f"backward T={T} N={N} K={K} {gating} {act} cf={cf} shared={shared}")
     x = W.generate(w)
     p, po, xg, fwd, t, H, ro, dsp, dO = _run(w, x, seed=T)
@@ -220,20 +226,42 @@ def test_backward_is_deterministic_and_fp32_is_refused():
         M.layer_backward(pf, xf, ff, torch.zeros_like(xf["u"]))
 
 
-@pytest.mark.parametrize("T,shared,empty", [(300, 0, False), (300, 1, False), (2100, 0, True)])
-def test_backward_integer_data_is_exact(T, shared, empty):
+def _cold_bias(w, x, lo, hi):
+    """Router bias that leaves expert N-1 with between lo and hi tokens: 0 for
+    the others, and for N-1 minus the midpoint of a wide gap in the sorted
+    margins H[N-1] - max_{i<N-1} H[i] of the unbiased scores (wide enough that
+    the GPU's fp32 scores, within 1e-4 of the oracle's, choose the same
+    tokens)."""
+    N = w.N
+    b = torch.zeros(N, dtype=torch.float32)
+    x["b_router"] = b
+    po = _io.problem(w, noise_weight=0.0)
+    H = O.router_logits(po, _io.inputs(po, x)).astype(np.float64)
+    srt = np.sort(H[:, N - 1] - H[:, :N - 1].max(axis=1))[::-1]
+    m = max(range(lo, hi + 1), key=lambda m: srt[m - 1] - srt[m])
+    assert srt[m - 1] - srt[m] > 1e-3
+    b[N - 1] = -float(srt[m - 1] + srt[m]) / 2
+    return m
+
+
+@pytest.mark.parametrize("T,shared,cold", [(300, 0, None), (300, 1, None), (2100, 0, "empty"),
+                                           (4200, 0, "short")])
+def test_backward_integer_data_is_exact(T, shared, cold):
     """ReLU experts, top-1 with softmax over the one selected score (gate 1,
     so no gradient reaches the router), sparse weights and inputs in
     {-1, 0, 1}: every product, sum and stored bf16 value is a small integer,
     so every gradient must equal the oracle's bit for bit.  With 2100 tokens
     the experts average over 512 rows, so the weight gradients take the
     transposed form; the last expert's bias keeps it empty, and its weight
-    gradients must come out zero."""
+    gradients must come out zero.  With 4200 tokens the groups average 1050
+    rows, so the GEMMs run 256-row tiles; the last expert's bias leaves it
+    24 to 56 rows, which run as a 64-row tail tile."""
     N, d, dff = 4, 128, 192
     w = W.Workload("bwdint", T=T, d=d, N=N, K=1, d_ff=dff, gating="topk_softmax", act="relu",
                    n_shared=shared, d_ff_shared=64 if shared else 0, seed=5)
+    assert M.moe_ffn_row_tile(T, N) == (256 if T >= 1024 * N else 128 if T >= 128 * N else 32)
     x = W.generate(w)
-    if empty:
+    if cold == "empty":
         x["b_router"] = torch.zeros(N, dtype=torch.float32)
         x["b_router"][N - 1] = -1.0e4
     g = torch.Generator().manual_seed(11)
@@ -241,7 +269,7 @@ def test_backward_integer_data_is_exact(T, shared, empty):
                                (torch.rand(s, generator=g) < p)).to(torch.bfloat16)
     # sparser inputs for the longer groups keep every sum within bf16's
     # exact integers (|v| <= 256)
-    dens = 0.5 if T < 1000 else 0.15
+    dens = 0.5 if T < 1000 else 0.15 if T < 3000 else 0.1
     x["u"] = tern(T, d, p=dens)
     x["w_gate"] = tern(N, dff, d)
     x["w_down"] = tern(N, d, dff)
@@ -250,6 +278,9 @@ def test_backward_integer_data_is_exact(T, shared, empty):
         x["ws_down"] = tern(1, d, 64)
     x["noise"] = None
     d_out = tern(T, d, p=dens)
+    if cold == "short":
+        m = _cold_bias(w, x, 24, 56)
+        say(f"integer backward: expert {N - 1} biased to {m} tokens")
     p = M.problem_of(w, noise_weight=0.0)
     xg = gpu(x)
     fwd = M.layer_forward(p, xg["u"], xg)
@@ -269,9 +300,12 @@ def test_backward_integer_data_is_exact(T, shared, empty):
     assert np.array_equal(host(t["d_gate"]), lb["d_gate"]), "d_gate"
     assert not host(t["dw_router"]).any() and not host(t["d_scores"]).any()
     u = _io.to_np(x["u"])
-    if empty:
-        assert np.diff(dsp["offsets"])[N - 1] == 0
+    sizes = np.diff(dsp["offsets"])
+    if cold == "empty":
+        assert sizes[N - 1] == 0
         assert not host(t["dw_gate"][N - 1]).any() and not host(t["dw_down"][N - 1]).any()
+    if cold == "short":
+        assert sizes[N - 1] == m and 1 <= m <= 64 and sizes.mean() >= 1024
     for e in range(N):
         toks, gates = _expert_rows(dsp, ro, e)
         ref = O.ffn_weight_grads(po, xi, e, u[toks], dO[toks], np.arange(dff, dtype=np.int32))

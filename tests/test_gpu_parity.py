@@ -241,18 +241,21 @@ def test_grouped_ffn_ragged(T, N, K, d, dff, act, shared):
     _ffn_case(w, W.generate(w))
 
 
-@pytest.mark.parametrize("act", ["swiglu", "relu"])
-def test_grouped_ffn_group_sizes_around_tile_multiples(act):
-    """Groups of 0 .. 600 rows around multiples of the 256-row tile: a last
-    tile extended by 1, 44, 64 rows (257, 300, 320, 576), not extended (321,
-    600: a partly filled third tile), exact multiples (512), short groups
-    with a 64-row tail tile (1, 64) or one partly filled tile (65, 255), and
-    a shared expert over 1050 tokens (its fourth tile extended by 26 rows):
-    every row checked."""
-    sizes = [257, 320, 321, 300, 0, 255, 1, 600, 64, 65, 576, 512]
-    T, K, d, dff = 1050, 4, 128, 192
+# Groups of 0 .. 600 rows around multiples of 256: a group ending 1, 44 or
+# 64 rows past a multiple (257, 300, 320, 576), 65 or 88 rows past (321,
+# 600), an exact multiple (512), short groups (1, 64, 65, 255) and an empty
+# one.
+TILE_SIZES = [257, 320, 321, 300, 0, 255, 1, 600, 64, 65, 576, 512]
+
+
+def _tile_case(act, T, want_tile, want_shared_tile):
+    K, d, dff = 4, 128, 192
+    sizes = TILE_SIZES
     w = W.Workload("tails", T=T, d=d, N=len(sizes), K=K, d_ff=dff, act=act, n_shared=1,
                    d_ff_shared=128, seed=77, dtype="bf16")
+    # the launch's tile height follows the mean group size T*K/N
+    assert M.moe_ffn_row_tile(T * K, len(sizes)) == want_tile
+    assert M.moe_ffn_row_tile(T, 1) == want_shared_tile
     x = W.generate(w)
     p = M.problem_of(w)
     po = _io.problem(w)
@@ -261,7 +264,7 @@ def test_grouped_ffn_group_sizes_around_tile_multiples(act):
     assert R <= T * K
     g = torch.Generator().manual_seed(5)
     x_perm = torch.randn(T * K, d, generator=g).to(torch.bfloat16)
-    say(f"ffn tails {act}: groups {sizes}, shared over {T} tokens")
+    say(f"ffn tiles {act}: {want_tile}-row tiles, groups {sizes}, shared over {T} tokens")
     xg = gpu(x)
     o = M.moe_grouped_ffn(p, x_perm.to(DEV), torch.from_numpy(offsets).to(DEV), xg["w_gate"],
                           xg["w_up"], xg["w_down"], xg["u"], xg["ws_gate"], xg["ws_up"],
@@ -270,9 +273,31 @@ def test_grouped_ffn_group_sizes_around_tile_multiples(act):
     eor = np.repeat(np.arange(len(sizes), dtype=np.int32), sizes)
     xi = _io.inputs(po, x)
     y_ref = O.ffn_rows(po, xi, elems(x_perm[:R]), eor)
-    assert_close(host(o["y_perm"][:R]), y_ref, "bf16", f"tails {act} y_perm")
+    assert_close(host(o["y_perm"][:R]), y_ref, "bf16", f"tiles {act} y_perm")
     ys_ref = O.ffn_rows(po, xi, elems(x["u"]), np.full(T, -1, np.int32))
-    assert_close(host(o["y_shared"]), ys_ref, "bf16", f"tails {act} y_shared")
+    assert_close(host(o["y_shared"]), ys_ref, "bf16", f"tiles {act} y_shared")
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_grouped_ffn_256_row_tiles(act):
+    """3100 tokens x top-4 over 12 experts: a mean group of 1033 rows, so the
+    256-row kernel runs the routed groups.  Its three tile kinds all occur:
+    last tiles extended by 1, 44 and 64 rows (257, 300, 320, 576), 64-row
+    tail tiles (groups of 1 and 64 rows), partly filled 256-row tiles (65,
+    255, and the third tiles of 321 and 600), an exact multiple (512) and an
+    empty group.  The shared expert over 3100 tokens (12 tiles and 28 rows)
+    has its last tile extended.  Every row is checked."""
+    _tile_case(act, 3100, 256, 256)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_grouped_ffn_128_row_tiles(act):
+    """The same groups at 1050 tokens x top-4 (mean group 350 rows) run the
+    128-row kernels (plain 128-row tiles, partly filled last tiles, no
+    extended or tail tiles); the shared expert over 1050 tokens runs
+    256-row tiles, its fourth tile extended by 26 rows.  Every row is
+    checked."""
+    _tile_case(act, 1050, 128, 256)
 
 
 def test_grouped_ffn_integer_data_exact():

@@ -339,6 +339,60 @@ def test_ffn_rows_vs_torch_float64(dtype, act):
     assert same >= 0.97 * n * d
 
 
+def _swiglu_scalar(dtype, x_vals, g_w, v_w):
+    """One expert with d = 2, d_ff = 1 and W_down = [[1], [0]]: the first
+    output of row r is the expert's activation for gate pre-activation
+    x_r[0]*g_w and up pre-activation x_r[0]*v_w, the second output is 0."""
+    f = bf16_bits if dtype == O.BF16 else (lambda a: np.asarray(a, np.float32))
+    n = len(x_vals)
+    x = f(np.array([[xv, 0.0] for xv in x_vals]))
+    wg = f(np.array([[[g_w, 0.0]]]))
+    wu = f(np.array([[[v_w, 0.0]]]))
+    wd = f(np.array([[[1.0], [0.0]]]))
+    p = O.Problem(T=n, d=2, N=1, K=1, d_ff=1, act=O.ACT_SWIGLU, dtype=dtype)
+    y = O.ffn_rows(p, O.Inputs(p, x, None, None, None, wg, wu, wd), x, np.zeros(n, np.int32))
+    assert np.all(y[:, 1] == 0.0)
+    return y[:, 0]
+
+
+def test_swiglu_closed_forms():
+    """Closed forms of the gated activation act = SiLU(gate)*up with
+    SiLU(z) = z/(1+e^-z) (reading of Figure 1's Gate/Up/Down expert on the
+    LLM-systems page): they fix which operand is gated and that the gate is
+    SiLU, not a plain sigmoid (GLU) or ReLU."""
+    ln3 = math.log(3.0)
+    # gate pre-activation 0: SiLU(0) = 0 whatever the up value (a sigmoid
+    # gate would give up/2)
+    y = _swiglu_scalar(O.F32, [1.0, 1.0], 0.0, 5.0)
+    assert y.tolist() == [0.0, 0.0]
+    # gate ln 3, up 2: sigma(ln 3) = 3/4, so act = 2 * ln3 * 3/4 = 1.5 ln 3.
+    # Gate and up swapped would give 2*sigma(2)*ln 3; a sigmoid gate 1.5;
+    # a ReLU gate 2 ln 3.
+    g_w = float(np.float32(ln3))
+    y = _swiglu_scalar(O.F32, [1.0], g_w, 2.0)
+    want = 1.5 * g_w
+    assert y[0] == pytest.approx(want, rel=2 ** -23)
+    assert abs(want - 2.0 / (1.0 + math.exp(-2.0)) * g_w) > 0.1
+    # gate 1, up 2: 2/(1+e^-1)
+    y = _swiglu_scalar(O.F32, [1.0], 1.0, 2.0)
+    assert y[0] == pytest.approx(2.0 / (1.0 + math.exp(-1.0)), rel=2 ** -23)
+    # SiLU(z) - SiLU(-z) = z, and up is linear in x: act(x) + act(-x) = g*v
+    for g, v in ((0.75, 1.25), (3.0, -0.5), (-2.5, 4.0)):
+        y = _swiglu_scalar(O.F32, [1.0, -1.0], g, v)
+        assert y[0] + y[1] == pytest.approx(g * v, rel=1e-6, abs=1e-7)
+    # far negative gate: SiLU(z) -> z e^z -> 0; far positive: SiLU(z) -> z
+    y = _swiglu_scalar(O.F32, [1.0, 1.0], -40.0, 3.0)
+    assert abs(y[0]) <= 40.0 * math.exp(-40.0) * 3.0 * 1.0001
+    y = _swiglu_scalar(O.F32, [1.0], 40.0, 3.0)
+    assert y[0] == pytest.approx(120.0, rel=1e-7)
+    # bf16 storage: the activation and the output are each rounded once to
+    # bf16 (round to nearest even), so 1.5 ln 3 comes out as its bf16 value
+    y = _swiglu_scalar(O.BF16, [1.0], float(torch.tensor(ln3).to(torch.bfloat16)), 2.0)
+    gb = float(torch.tensor(ln3).to(torch.bfloat16))
+    want_bf = float(torch.tensor(1.5 * gb, dtype=torch.float64).to(torch.float32).to(torch.bfloat16))
+    assert y[0] == want_bf
+
+
 def test_ffn_relu_integer_data_is_exact():
     """Small non-negative integers keep every product and sum exact, in bf16
     storage too, so the FFN equals an integer matrix product."""
