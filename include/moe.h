@@ -260,6 +260,27 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
                       const moe_weights_t* w, moe_layer_outputs_t* o, void* out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * moe_layer_forward; its scratch memory is instead a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from load until
+ * the process ends.  The call allocates and frees nothing.
+ *   - Problems whose moe_workspace_size() exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     return MOE_ERR_UNSUPPORTED (before any HIP call); use
+ *     moe_layer_forward for them.
+ *   - `stream` must belong to the current device (MOE_ERR_INVALID_ARG
+ *     otherwise).  The first call on a device looks up that device's copy of
+ *     the array (MOE_ERR_HIP if the lookup fails).
+ *   - Every call on one GPU shares that GPU's array, and nothing in it needs
+ *     to start cleared: each kernel writes the scratch it reads.  Calls that
+ *     overlap on one GPU (other streams, other host threads) race on it;
+ *     serialise them. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_problem_t* p, const void* u, const float* noise,
+                              const moe_weights_t* w, moe_layer_outputs_t* o, void* out,
+                              void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Backward pass.  The gradient of the layer output h (MoE-layer equation
  * of "Mixture-of-Experts (MoE)", ML notes, through the stages of "From

@@ -3,6 +3,8 @@
 // reaches the device; all work is enqueued on the caller's stream.
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -356,11 +358,13 @@ int moe_router_stats(const moe_problem_t* p, const int32_t* expert_counts,
                                              static_cast<hipStream_t>(stream)));
 }
 
-int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
-                      const moe_weights_t* wt, moe_layer_outputs_t* o, void* out, void* ws,
-                      size_t ws_bytes, void* stream) {
-  MOE_TRY(check_problem(p));
-  if (p->T == 0) return MOE_OK;
+}  // extern "C"
+
+namespace {
+
+// Checks of moe_layer_forward's arguments other than the workspace.
+int check_layer(const moe_problem_t* p, const void* u, const float* noise,
+                const moe_weights_t* wt, const moe_layer_outputs_t* o, const void* out) {
   if (wt == nullptr || o == nullptr) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_route(p, u, wt->w_router, wt->b_router, noise, o->scores, o->topk_idx,
                       o->topk_gate, o->mean_prob, o->lse_sq));
@@ -369,9 +373,13 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
   MOE_TRY(check_ffn(p, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u, wt->ws_gate,
                     wt->ws_up, wt->ws_down, o->y_perm, o->y_shared));
   MOE_TRY(check_combine(p, u, o->y_perm, o->row_of, o->topk_gate, o->y_shared, out));
-  const Workspace w = moe::workspace_layout(*p);
-  MOE_TRY(check_ws(ws, ws_bytes, w.total));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// The four stages of the layer on stream s, scratch in ws (layout w).
+int launch_layer(const moe_problem_t* p, const void* u, const float* noise,
+                 const moe_weights_t* wt, moe_layer_outputs_t* o, void* out, void* ws,
+                 const Workspace& w, hipStream_t s) {
   hipError_t e = moe::launch_route(*p, u, wt->w_router, wt->b_router, noise, o->scores,
                                    o->topk_idx, o->topk_gate, o->mean_prob, o->lse_sq,
                                    reinterpret_cast<float*>(ws_at(ws, w.route_part)),
@@ -393,6 +401,69 @@ int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(*p, u, o->y_perm, o->row_of, o->topk_gate, ysh, out, s);
   return hip_status(e);
+}
+
+// ------------------------------------------- allocation-free layer forward
+// Scratch memory of moe_layer_forward_noalloc: a file-scope device array,
+// one copy per GPU, held from module load until the process ends.  In host
+// code `scratch` names only a host-side handle of the symbol; its device
+// address on each GPU comes from hipGetSymbolAddress with that GPU current,
+// looked up once per device and kept in scratch_dev.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array, for a launch on stream
+// s (which must belong to the current GPU).
+int scratch_for(hipStream_t s, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return MOE_ERR_HIP;
+    if (sdev != dev) return MOE_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return MOE_ERR_HIP;
+    scratch_dev[dev] = a;
+  }
+  *ptr = scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_problem_t* p, const void* u, const float* noise,
+                      const moe_weights_t* wt, moe_layer_outputs_t* o, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_layer(p, u, noise, wt, o, out));
+  const Workspace w = moe::workspace_layout(*p);
+  MOE_TRY(check_ws(ws, ws_bytes, w.total));
+  return launch_layer(p, u, noise, wt, o, out, ws, w, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_forward_noalloc(const moe_problem_t* p, const void* u, const float* noise,
+                              const moe_weights_t* wt, moe_layer_outputs_t* o, void* out,
+                              void* stream) {
+  MOE_TRY(check_problem(p));
+  if (p->T == 0) return MOE_OK;
+  MOE_TRY(check_layer(p, u, noise, wt, o, out));
+  const Workspace w = moe::workspace_layout(*p);
+  if (w.total > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  MOE_TRY(scratch_for(s, &ws));
+  return launch_layer(p, u, noise, wt, o, out, ws, w, s);
 }
 
 // ------------------------------------------------------------ backward

@@ -20,6 +20,7 @@ MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_RELU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_RANK = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # static scratch of moe_layer_forward_noalloc, per GPU
 
 GATING = {"softmax_topk": MOE_GATE_SOFTMAX_TOPK, "topk_softmax": MOE_GATE_TOPK_SOFTMAX}
 ACT = {"swiglu": MOE_ACT_SWIGLU, "relu": MOE_ACT_RELU}
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
             L.moe_combine.argtypes = [P] + [vp] * 7 + [sz, vp]
             L.moe_layer_forward.argtypes = [P, vp, vp, ctypes.POINTER(MoeWeights),
                                             ctypes.POINTER(MoeLayerOutputs), vp, vp, sz, vp]
+            L.moe_layer_forward_noalloc.argtypes = [P, vp, vp, ctypes.POINTER(MoeWeights),
+                                                    ctypes.POINTER(MoeLayerOutputs), vp, vp]
             L.moe_router_stats.argtypes = [P] + [vp] * 5
             L.moe_ec_capacity.argtypes = [i32, i32, i32, ctypes.c_float]
             L.moe_ec_capacity.restype = i32
@@ -117,7 +120,7 @@ def lib() -> ctypes.CDLL:
             L.moe_layer_backward.argtypes = [P, vp, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeSaved),
                                              vp, ctypes.POINTER(MoeGrads), vp, sz, vp]
             for f in ("moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
-                      "moe_layer_forward", "moe_router_stats", "moe_ec_route",
+                      "moe_layer_forward", "moe_layer_forward_noalloc", "moe_router_stats", "moe_ec_route",
                       "moe_ec_dispatch", "moe_ec_combine", "moe_ec_layer_forward",
                       "moe_layer_backward"):
                 getattr(L, f).restype = ctypes.c_int
@@ -358,6 +361,17 @@ def moe_layer_forward(p: MoeProblem, u, noise, weights: MoeWeights, bufs: LayerB
           ctypes.byref(bufs.c), _ptr(bufs.t["out"]), _ptr(ws), ws.numel(), _stream(dev))
     return bufs.t["out"]
 
+
+def moe_layer_forward_noalloc(p: MoeProblem, u, noise, weights: MoeWeights,
+                              bufs: LayerBuffers) -> torch.Tensor:
+    """moe_layer_forward with the library's static scratch instead of a
+    workspace (no allocation in the call); returns bufs.t['out']."""
+    dev = u.device
+    _check(u, "u", (p.T, p.d), TORCH_DTYPE[p.dtype], dev)
+    _check(noise, "noise", (p.T, p.N), torch.float32, dev, optional=True)
+    _call("moe_layer_forward_noalloc", ctypes.byref(p), _ptr(u), _ptr(noise),
+          ctypes.byref(weights), ctypes.byref(bufs.c), _ptr(bufs.t["out"]), _stream(dev))
+    return bufs.t["out"]
 
 
 def layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], want_scores=True) -> Dict[str, torch.Tensor]:

@@ -304,3 +304,25 @@ def test_backward_checks_before_launch():
     assert call(q, W_, S_, G_, 1 << 40) == M.MOE_ERR_INVALID_ARG
     assert call(good(T=0), W_, S_, G_, 0) == M.MOE_OK
 
+
+def test_noalloc_scratch_size_and_refusal():
+    """moe_layer_forward_noalloc: the binding's scratch size matches the
+    header's, and a problem whose workspace exceeds it is refused before any
+    HIP call (the fake pointers are never dereferenced)."""
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.MOE_NOALLOC_SCRATCH_BYTES
+    L = M.lib()
+    wts = M.MoeWeights(*[FAKE + 4096 * (10 + i) for i in range(len(M.MoeWeights._fields_))])
+    outs = M.MoeLayerOutputs(*[FAKE + 4096 * (30 + i) for i in range(len(M.MoeLayerOutputs._fields_))])
+
+    def call(p):
+        return L.moe_layer_forward_noalloc(ctypes.byref(p), fake(1), None, ctypes.byref(wts),
+                                           ctypes.byref(outs), fake(2), None)
+    big = good(T=8192, d=4096, N=8, K=2, d_ff=14336)
+    assert M.moe_workspace_size(big) > M.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == M.MOE_ERR_UNSUPPORTED
+    assert call(good(K=0)) == M.MOE_ERR_INVALID_ARG
+    assert call(good(T=0)) == M.MOE_OK
+    assert L.moe_layer_forward_noalloc(ctypes.byref(good()), fake(1), None, None, ctypes.byref(outs),
+                                       fake(2), None) == M.MOE_ERR_INVALID_ARG
