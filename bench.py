@@ -12,6 +12,13 @@ launch stream), per-stage times, and the CPU oracle timed on a bounded
 sample of the same workload on the host cores.  The expert-choice pass
 (moe_ec_layer_forward, experts selecting their tokens) is timed after it on
 the same batch and weights and reported beside the token-choice line.
+
+`per_config` in the same line repeats the forward measurement (tokens/s,
+per-stage times warm and cold, the grouped GEMMs against their roofline,
+route/dispatch/combine against HBM, a CPU-oracle sample) for every workload:
+the tiny fp32 layer, the Switch-style top-1 layer with capacity, the
+Mixtral-shaped layer, the DeepSeekMoE-shaped layer with shared experts and
+the decode-sized noisy layer.
 """
 import argparse
 import ctypes
@@ -89,13 +96,231 @@ def mfma_reference(stream):
                     "memory traffic: the matrix-core rate at the clock the chip sustains under that load"}
 
 
+# tokens timed on the CPU oracle per workload (about 1-15 s of host work each)
+CPU_SAMPLE = dict(tiny_fp32=256, switch_top1=4096, mixtral=1024, deepseekmoe=2048, decode_noisy=128)
+
+
+def host_threads():
+    """Threads the oracle uses: the host cores this process may run on, at
+    most 16 (the host share of one GPU on the GPU machines)."""
+    from oracle import oracle as O
+    return O.nthreads_default()
+
+
+def measure_forward(w, args, dev, stream, headline):
+    """Forward pass of workload w: whole-pass tokens/s (wall clock around
+    exactly args.steps passes), per-stage HIP-event times warm and with cold
+    caches, the grouped GEMMs against their roofline, the memory-bound stages
+    against HBM, and the CPU oracle on a bounded sample of the same batch."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_42_amd import moe as M
+    from sparse_mixture_experts_42_amd import workloads as W
+
+    p = M.problem_of(w)
+    L = M.lib()
+    log(f"workload {w.name}: T={w.T} d={w.d} N={w.N} K={w.K} d_ff={w.d_ff} "
+        f"shared={w.n_shared}x{w.d_ff_shared} {w.dtype}")
+    t0 = time.time()
+    x = W.generate(w)
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    xg = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    weights = M.make_weights(p, xg["w_router"], xg["b_router"], xg["w_gate"], xg["w_up"],
+                             xg["w_down"], xg["ws_gate"], xg["ws_up"], xg["ws_down"])
+    bufs = M.LayerBuffers(p, dev, want_scores=w.gating == "softmax_topk")
+    ws = M.workspace(p, dev)
+    torch.cuda.synchronize()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.byref(p)
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    layer_args = (P, vp(xg["u"]), vp(xg["noise"]), ctypes.byref(weights), ctypes.byref(bufs.c),
+                  vp(bufs.t["out"]), vp(ws), ws.numel(), sp)
+
+    def step():
+        st = L.moe_layer_forward(*layer_args)
+        if st != 0:
+            raise RuntimeError(M.moe_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` whole passes
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = wall * 1e3 / args.steps
+    log(f"{w.name}: timed {args.steps} steps: {ms_step:.4f} ms/step "
+        f"(events {e0.elapsed_time(e1) / args.steps:.4f})")
+
+    # ---- per-stage live timing on the same stream (same buffers)
+    t = bufs.t
+    R = int(t["offsets"][-1].item())
+    stats = torch.empty(4, dtype=torch.float32, device=dev)
+    stage_args = {
+        "route": ("moe_route", (P, vp(xg["u"]), vp(xg["w_router"]), vp(xg["b_router"]),
+                                vp(xg["noise"]), vp(t["scores"]), vp(t["topk_idx"]), vp(t["topk_gate"]),
+                                vp(t["mean_prob"]), vp(t["lse_sq"]), vp(ws), ws.numel(), sp)),
+        "dispatch": ("moe_dispatch", (P, vp(xg["u"]), vp(t["topk_idx"]), vp(t["expert_counts"]),
+                                      vp(t["kept_counts"]), vp(t["offsets"]), vp(t["row_of"]),
+                                      vp(t["token_of_row"]), vp(t["x_perm"]), vp(ws), ws.numel(), sp)),
+        "grouped_ffn": ("moe_grouped_ffn", (P, vp(t["x_perm"]), vp(t["offsets"]), vp(xg["w_gate"]),
+                                            vp(xg["w_up"]), vp(xg["w_down"]), vp(xg["u"]),
+                                            vp(xg["ws_gate"]), vp(xg["ws_up"]), vp(xg["ws_down"]),
+                                            vp(t["y_perm"]), vp(t["y_shared"]), vp(ws), ws.numel(), sp)),
+        "combine": ("moe_combine", (P, vp(xg["u"]), vp(t["y_perm"]), vp(t["row_of"]),
+                                    vp(t["topk_gate"]), vp(t["y_shared"]), vp(t["out"]), None, 0, sp)),
+        "router_stats": ("moe_router_stats", (P, vp(t["expert_counts"]), vp(t["mean_prob"]),
+                                              vp(t["lse_sq"]), vp(stats), sp)),
+    }
+    n = max(args.steps, 10)
+    stages_ms = {}
+    for name, (fn, a) in stage_args.items():
+        f = getattr(L, fn)
+        for _ in range(2):
+            f(*a)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            st = f(*a)
+            if st != 0:
+                raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stages_ms[name] = e0.elapsed_time(e1) / n
+    log(f"{w.name} stages (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_ms.items()))
+
+    # ---- the same stages with cold caches: a 1 GiB buffer is read before
+    # each timed call, evicting the 256 MB Infinity Cache and the L2s (read,
+    # not written: a written buffer would leave up to 256 MB of dirty lines
+    # whose write-back lands inside the timed call); the median of the
+    # per-call event times
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    stages_cold_ms = {}
+    for name, (fn, a) in stage_args.items():
+        f = getattr(L, fn)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for b, e in ev:
+            flush.sum()
+            b.record(stream)
+            st = f(*a)
+            e.record(stream)
+            if st != 0:
+                raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
+        torch.cuda.synchronize()
+        stages_cold_ms[name] = float(np.median([b.elapsed_time(e) for b, e in ev]))
+    del flush
+    log(f"{w.name} stages, cold caches (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_cold_ms.items()))
+
+    # ---- roofline of the grouped expert GEMMs (algorithmic work per call)
+    mults = 3 if w.act == "swiglu" else 2
+    flops = 2.0 * R * w.d * w.d_ff * mults
+    flops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * mults
+    sizes = np.diff(t["offsets"].cpu().numpy())
+    touched = int((sizes > 0).sum())
+    es = w.es
+    # every byte the FFN must move at least once: the touched experts'
+    # weights, x_perm, the gated activations (written and read), y_perm; and
+    # the same for the shared experts over all tokens
+    ffn_bytes = touched * mults * w.d * w.d_ff * es + R * (2 * w.d + 2 * w.d_ff) * es
+    ffn_bytes += w.n_shared * mults * w.d * w.d_ff_shared * es \
+        + (w.T * (2 * w.d + 2 * w.n_shared * w.d_ff_shared) * es if w.n_shared else 0)
+    ffn_s = stages_ms["grouped_ffn"] * 1e-3
+    achieved = flops / ffn_s / 1e12
+    if w.dtype != "bf16":
+        # the fp32 experts run on the vector ALUs (LDS-tiled FMA), not the matrix cores
+        roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 4)}
+    elif flops / ffn_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        # below the ridge point: the weights bound it (decode-sized batches)
+        gbs = ffn_bytes / ffn_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(achieved, 1)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roofline.update({"traffic": stored_traffic(w.name),
+                     "kernel": "grouped expert GEMMs (moe_grouped_ffn: gate/up GEMM + down GEMM)",
+                     "flops_per_call": flops, "min_bytes_per_call": ffn_bytes, "rows": R,
+                     "experts_with_rows": touched,
+                     "row_tile": M.moe_ffn_row_tile(w.T * w.K, w.N, w.dtype)})
+
+    # ---- HBM fractions of the memory-bound stages (algorithmic bytes)
+    route_bytes = w.T * w.d * es + w.N * w.d * 4 + w.T * (w.K * 8 + 4) \
+        + (w.T * w.N * 4 if w.noise else 0) + (w.T * w.N * 4 if t["scores"] is not None else 0)
+    disp_bytes = w.T * w.d * es + R * w.d * es + w.T * w.K * 4 * 3 + R * 4
+    comb_bytes = w.T * w.d * es * 2 + R * w.d * es + w.T * w.K * 8 \
+        + (w.T * w.d * es if w.n_shared else 0)
+    sb = (("route", route_bytes), ("dispatch", disp_bytes), ("combine", comb_bytes))
+    hbm = {k: round(b / (stages_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k, b in sb}
+    hbm_cold = {k: round(b / (stages_cold_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k, b in sb}
+    # the router's fp32 products (2 T d N flops) bound it once N is large
+    hbm["route_fp32_frac"] = round(2.0 * w.T * w.d * w.N / (stages_ms["route"] * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4)
+
+    # ---- CPU oracle on a bounded sample of the same batch
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        from tests import _io
+        want = args.cpu_sample if (headline and args.cpu_sample) else CPU_SAMPLE.get(w.name, 256)
+        nt = min(want, w.T)
+        ws_ = w.replace(T=nt)
+        xs = dict(x)
+        xs["u"] = x["u"][:nt].contiguous()
+        if x["noise"] is not None:
+            xs["noise"] = x["noise"][:nt].contiguous()
+        po = _io.problem(ws_)
+        xi = _io.inputs(po, xs)
+        nth = host_threads()
+        c0 = time.perf_counter()
+        O.layer_forward(po, xi, nthreads=nth)
+        cs = time.perf_counter() - c0
+        what = "the whole batch" if nt == w.T else f"the first {nt} of {w.T} tokens"
+        cpu = {"value": round(nt / cs, 3), "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "host_cores_visible": len(os.sched_getaffinity(0)),
+               "sample": f"{what} of the {w.name} batch (same weights), whole oracle pass "
+                         f"(router, top-K, dispatch, expert FFNs, combine) in {cs:.2f} s"}
+        log(f"{w.name} cpu oracle: {nt} tokens on {nth} threads in {cs:.2f} s")
+
+    tokens_per_s = w.T * args.steps / wall
+    out = {
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "d_ff": w.d_ff,
+                   "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared, "gating": w.gating,
+                   "act": w.act, "capacity_factor": w.capacity_factor, "noise": w.noise,
+                   "dtype": w.dtype, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(tokens_per_s, 1), "ms_per_step": round(ms_step, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},
+        "stages_ms_cold": {k: round(v, 4) for k, v in stages_cold_ms.items()},
+        "roofline": roofline, "hbm_frac": hbm, "hbm_frac_cold": hbm_cold,
+        "cpu_baseline": cpu,
+        "gpu_over_cpu": round(tokens_per_s / cpu["value"], 1) if cpu else None,
+    }
+    if headline:
+        out.update({"_w": w, "_x": x, "_xg": xg, "_p": p, "_weights": weights, "_bufs": bufs, "_ws": ws})
+    else:
+        del xg, weights, bufs, ws, x
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens timed on the CPU oracle")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens of the headline workload timed on the CPU oracle (0: its default)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure the headline workload only (no per_config object)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-expert-choice", action="store_true",
                     help="skip the expert-choice pass timed after the token-choice one")
@@ -120,111 +345,19 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    w = W.WORKLOADS[args.workload]
-    p = M.problem_of(w)
     L = M.lib()
-    log(f"workload {w.name}: T={w.T} d={w.d} N={w.N} K={w.K} d_ff={w.d_ff} "
-        f"shared={w.n_shared}x{w.d_ff_shared} {w.dtype}")
-    t0 = time.time()
-    x = W.generate(w)
-    log(f"inputs generated in {time.time() - t0:.1f} s")
-    xg = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
-    weights = M.make_weights(p, xg["w_router"], xg["b_router"], xg["w_gate"], xg["w_up"],
-                             xg["w_down"], xg["ws_gate"], xg["ws_up"], xg["ws_down"])
-    bufs = M.LayerBuffers(p, dev, want_scores=w.gating == "softmax_topk")
-    ws = M.workspace(p, dev)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    head = measure_forward(W.WORKLOADS[args.workload], args, dev, stream, headline=True)
+    w, x, xg, p, weights, bufs, ws = (head.pop(k) for k in ("_w", "_x", "_xg", "_p", "_weights",
+                                                              "_bufs", "_ws"))
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = ctypes.byref(p)
     vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    layer_args = (P, vp(xg["u"]), vp(xg["noise"]), ctypes.byref(weights), ctypes.byref(bufs.c),
-                  vp(bufs.t["out"]), vp(ws), ws.numel(), sp)
-
-    def step():
-        st = L.moe_layer_forward(*layer_args)
-        if st != 0:
-            raise RuntimeError(M.moe_status_string(st))
-
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` whole passes
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = wall * 1e3 / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events {e0.elapsed_time(e1) / args.steps:.3f})")
-
-    # ---- per-stage live timing on the same stream (same buffers)
-    t = bufs.t
-    R = int(t["offsets"][-1].item())
-    stats = torch.empty(4, dtype=torch.float32, device=dev)
-    stage_args = {
-        "route": ("moe_route", (P, vp(xg["u"]), vp(xg["w_router"]), vp(xg["b_router"]),
-                                vp(xg["noise"]), None, vp(t["topk_idx"]), vp(t["topk_gate"]),
-                                vp(t["mean_prob"]), vp(t["lse_sq"]), vp(ws), ws.numel(), sp)),
-        "dispatch": ("moe_dispatch", (P, vp(xg["u"]), vp(t["topk_idx"]), vp(t["expert_counts"]),
-                                      vp(t["kept_counts"]), vp(t["offsets"]), vp(t["row_of"]),
-                                      vp(t["token_of_row"]), vp(t["x_perm"]), vp(ws), ws.numel(), sp)),
-        "grouped_ffn": ("moe_grouped_ffn", (P, vp(t["x_perm"]), vp(t["offsets"]), vp(xg["w_gate"]),
-                                            vp(xg["w_up"]), vp(xg["w_down"]), vp(xg["u"]),
-                                            vp(xg["ws_gate"]), vp(xg["ws_up"]), vp(xg["ws_down"]),
-                                            vp(t["y_perm"]), vp(t["y_shared"]), vp(ws), ws.numel(), sp)),
-        "combine": ("moe_combine", (P, vp(xg["u"]), vp(t["y_perm"]), vp(t["row_of"]),
-                                    vp(t["topk_gate"]), vp(t["y_shared"]), vp(t["out"]), None, 0, sp)),
-        "router_stats": ("moe_router_stats", (P, vp(t["expert_counts"]), vp(t["mean_prob"]),
-                                              vp(t["lse_sq"]), vp(stats), sp)),
-    }
-    stages_ms = {}
-    for name, (fn, a) in stage_args.items():
-        f = getattr(L, fn)
-        for _ in range(2):
-            f(*a)
-        n = max(args.steps, 10)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            st = f(*a)
-            if st != 0:
-                raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        stages_ms[name] = e0.elapsed_time(e1) / n
-    log("stages (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_ms.items()))
-
-    # ---- the same stages with cold caches: a 1 GiB buffer is read before
-    # each timed call, evicting the 256 MB Infinity Cache and the L2s (read,
-    # not written: a written buffer would leave up to 256 MB of dirty lines
-    # whose write-back lands inside the timed call); the median of the
-    # per-call event times
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    stages_cold_ms = {}
-    for name, (fn, a) in stage_args.items():
-        f = getattr(L, fn)
-        n = max(args.steps, 10)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        torch.cuda.synchronize()
-        for b, e in ev:
-            flush.sum()
-            b.record(stream)
-            st = f(*a)
-            e.record(stream)
-            if st != 0:
-                raise RuntimeError(f"{fn}: {M.moe_status_string(st)}")
-        torch.cuda.synchronize()
-        stages_cold_ms[name] = float(np.median([b.elapsed_time(e) for b, e in ev]))
+    R = head["roofline"]["rows"]
     # attainable HBM reference: a device-to-device copy of 128 MiB (256 MiB
-    # moved, the size of the combine stage's traffic), warm and cold as above
+    # moved, the size of the combine stage's traffic), warm and cold
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     src = torch.ones(1 << 25, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     n = max(args.steps, 10)
@@ -245,11 +378,11 @@ def main():
     copy_cold_ms = float(np.median([b.elapsed_time(e) for b, e in ev]))
     copy_bytes = 2 * src.numel() * 4
     del flush, src, dst
-    log("stages, cold caches (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in stages_cold_ms.items()))
     log(f"copy of 128 MiB: warm {copy_warm_ms:.4f} ms, cold {copy_cold_ms:.4f} ms")
     mfma_ref = mfma_reference(stream)
     if mfma_ref is not None:
         log(f"matrix cores alone (reference): {mfma_ref['tflops']} TFLOP/s")
+        mfma_ref["grouped_gemm_frac_of_this"] = round(head["roofline"]["achieved"] / mfma_ref["tflops"], 4)
 
     # ---- expert-choice pass on the same workload (same inputs and weights)
     ec = None
@@ -326,55 +459,6 @@ def main():
                "note": "moe_layer_backward (all gradients) on the same batch, HIP-event time per pass"}
         del bb, bws
 
-    # ---- roofline of the grouped expert GEMMs (algorithmic flops per call)
-    mults = 3 if w.act == "swiglu" else 2
-    flops = 2.0 * R * w.d * w.d_ff * mults
-    flops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * mults
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = flops / (stages_ms["grouped_ffn"] * 1e-3) / 1e12
-    if mfma_ref is not None and w.dtype == "bf16":
-        mfma_ref["grouped_gemm_frac_of_this"] = round(achieved / mfma_ref["tflops"], 4)
-    # the fp32 experts run on the vector ALUs (LDS-tiled FMA), not the matrix cores
-    roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": stored_traffic(w.name),
-                "kernel": "grouped expert GEMMs (moe_grouped_ffn: gate/up GEMM + down GEMM)",
-                "flops_per_call": flops, "rows": R}
-
-    # ---- HBM fractions of the memory-bound stages (algorithmic bytes)
-    es = w.es
-    route_bytes = w.T * w.d * es + w.N * w.d * 4 + w.T * (w.K * 8 + 4) \
-        + (w.T * w.N * 4 if w.noise else 0)
-    disp_bytes = w.T * w.d * es + R * w.d * es + w.T * w.K * 4 * 3 + R * 4
-    comb_bytes = w.T * w.d * es * 2 + R * w.d * es + w.T * w.K * 8 \
-        + (w.T * w.d * es if w.n_shared else 0)
-    hbm = {k: round(b / (stages_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-           for k, b in (("route", route_bytes), ("dispatch", disp_bytes), ("combine", comb_bytes))}
-    hbm_cold = {k: round(b / (stages_cold_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-                for k, b in (("route", route_bytes), ("dispatch", disp_bytes), ("combine", comb_bytes))}
-
-    # ---- CPU oracle on a bounded sample of the same workload
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import oracle as O
-        from tests import _io
-        n = min(args.cpu_sample, w.T)
-        ws_ = w.replace(T=n)
-        xs = dict(x)
-        xs["u"] = x["u"][:n].contiguous()
-        if x["noise"] is not None:
-            xs["noise"] = x["noise"][:n].contiguous()
-        po = _io.problem(ws_)
-        xi = _io.inputs(po, xs)
-        nth = O.nthreads_default()
-        log(f"cpu oracle: {n} tokens on {nth} threads")
-        c0 = time.perf_counter()
-        O.layer_forward(po, xi, nthreads=nth)
-        cs = time.perf_counter() - c0
-        cpu = {"value": round(n / cs, 3), "unit": "tokens/s", "cores": nth, "kind": "oracle",
-               "sample": f"first {n} tokens of the {w.name} batch (same weights), whole oracle pass "
-                         f"(router, top-K, dispatch, expert FFNs, combine) in {cs:.1f} s"}
-        log(f"cpu oracle: {cs:.1f} s")
-
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -386,30 +470,43 @@ def main():
         log(f"calibration copies: 3 x {args.calibrate_copy} MiB read + written")
         del src, dst
 
-    value = w.T * args.steps / wall
+    del xg, weights, bufs, ws
+    per_config = {}
+    if not args.no_per_config:
+        for name in W.ORDER:
+            if name == w.name:
+                c = dict(head)
+            else:
+                c = measure_forward(W.WORKLOADS[name], args, dev, stream, headline=False)
+                for k in [k for k in c if k.startswith("_")]:
+                    del c[k]
+                torch.cuda.empty_cache()
+            per_config[name] = {k: c[k] for k in ("config", "tokens_per_s", "ms_per_step", "stages_ms",
+                                                  "stages_ms_cold", "roofline", "hbm_frac", "hbm_frac_cold",
+                                                  "cpu_baseline", "gpu_over_cpu")}
+
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded, random-init weights)",
-        "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "d_ff": w.d_ff,
-                   "n_shared": w.n_shared, "d_ff_shared": w.d_ff_shared, "gating": w.gating,
-                   "act": w.act, "capacity_factor": w.capacity_factor, "parallelism": "none (1 GPU)"},
-        "roofline": roofline,
-        "grouped_gemm_pct_bf16_peak": round(100 * roofline["frac"], 2),
-        "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},
-        "hbm_frac": hbm,
-        "stages_ms_cold": {k: round(v, 4) for k, v in stages_cold_ms.items()},
-        "hbm_frac_cold": hbm_cold,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "grouped_gemm_pct_bf16_peak": round(100 * head["roofline"]["frac"], 2),
+        "stages_ms": head["stages_ms"],
+        "hbm_frac": head["hbm_frac"],
+        "stages_ms_cold": head["stages_ms_cold"],
+        "hbm_frac_cold": head["hbm_frac_cold"],
         "copy_reference": {"bytes": copy_bytes,
                            "warm_frac": round(copy_bytes / (copy_warm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "cold_frac": round(copy_bytes / (copy_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "note": "device-to-device copy of 128 MiB, the attainable HBM fraction "
                                    "for a transfer of the combine stage's size"},
         "mfma_reference": mfma_ref,
-        "cpu_baseline": cpu,
+        "cpu_baseline": head["cpu_baseline"],
         "expert_choice": ec,
         "backward": bwd,
+        "per_config": per_config,
     }
     print(json.dumps(line), flush=True)
 

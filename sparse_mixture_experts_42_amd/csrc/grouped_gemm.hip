@@ -52,6 +52,9 @@ struct GemmArgs {
   int ldd;
   void* C2;
   int ldc2;
+  // persistent launches: work-queue counters (kQueueInts, zero at launch),
+  // or null for one block per tile
+  int32_t* queue;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -275,9 +278,20 @@ __device__ __forceinline__ bf16x8 read_kmajor(const char* tile, int kk, int col0
 // BT: B is k-major (B[k][n] row-major, n contiguous; see above) instead of
 // [n][k]; only with EPI_NONE and BN = 256.  PIPE: the software-pipelined
 // main loop (256-column tiles); otherwise a plain double-buffered loop.
-template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN, bool BT = false, bool PIPE = false>
+struct NoPre {
+  __device__ void operator()(int) const {}
+};
+
+// PIPE tiles may continue a persistent block's previous tile: stage 0 uses
+// LDS buffer b0 (stage k buffer (k + b0) & 1), `issued` says its loads are
+// already in flight, and pre(buf) runs after the main loop, once every wave
+// is past the last stage barrier, with buf the LDS buffer that is free
+// (where the next tile's stage 0 goes).
+template <int EPI, int BM, int BN, int WGM, int WGN, int SAN, int SBN, bool BT = false, bool PIPE = false,
+          typename Pre = NoPre>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, int rows, int by,
-                                          u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN]) {
+                                          u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN], int b0 = 0,
+                                          bool issued = false, const Pre& pre = Pre{}) {
   constexpr int NW = WGM * WGN;                   // waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;     // 32x32 accumulators per wave
@@ -291,7 +305,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   static_assert(!BT || (EPI == EPI_NONE && BN == 256), "k-major B: plain epilogue, 256 columns");
   constexpr int BNH = GATED ? BN / 2 : BN;        // output columns per tile
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // opaque to the compiler, so that a persistent caller's loop recomputes
+  // the per-lane addressing of each tile instead of keeping that of every
+  // tile shape live across the loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   // the tile coordinates are block-uniform; saying so keeps the buffer
   // descriptors built from them in scalar registers
@@ -502,16 +521,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
     };
     constexpr int H = TM / 2;
     bf16x8 fa[2][TM], fb[2][TN];
-    issue_part(0, true, 0, 0, NL);
+    if (!issued) issue_part(0, true, b0, 0, NL);
     advance();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    read_frags(fa[0], fb[0], 0, 0);
+    read_frags(fa[0], fb[0], b0, 0);
     // k-steps 0, 1, 2 and the first half of 3 of stage kt; loads l0.. of
     // stage kt+1 are issued during k-steps 0 and 1 (the first ones already
     // went out after the previous barrier)
     auto body = [&](int kt, int l0) {
-      const int buf = kt & 1;
+      const int buf = (kt + b0) & 1;
       const bool live = kt + 1 < nk;
       const int lm = l0 + TM * TN / 2 < NL ? l0 + TM * TN / 2 : NL;
       kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], buf, 1, true, 2, kt + 1, live, buf ^ 1, l0, lm);
@@ -533,13 +552,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       __syncthreads();
       // second half of k-step 3 of stage kt-1, reading the first
       // fragments of stage kt
-      kstep(fa[1], fb[1], H, TM, fa[0], fb[0], kt & 1, 0, true, 1, kt + 1, kt + 1 < nk, (kt + 1) & 1, 0, LB);
+      kstep(fa[1], fb[1], H, TM, fa[0], fb[0], (kt + b0) & 1, 0, true, 1, kt + 1, kt + 1 < nk,
+            (kt + 1 + b0) & 1, 0, LB);
       body(kt, LB);
     }
     kstep(fa[1], fb[1], H, TM, fa[0], fb[0], 0, 0, false, 1, 0, false, 0, 0, 0);
     // the empty loads of the last stage still write the LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    pre((nk + b0) & 1);
   } else {
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -686,6 +707,49 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       }
     return;
   }
+  if constexpr (PIPE && (EPI == EPI_NONE || EPI == EPI_SWIGLU || EPI == EPI_RELU)) {
+    // Forward epilogue of the pipelined tiles.  Neighbouring lanes (columns
+    // c and c+1) swap one value of each row pair, so that the even lane
+    // holds row r and the odd lane row r+1, both at columns (c, c+1); each
+    // lane then stores one bf16 pair (4 bytes) through a buffer descriptor
+    // over the tile's rows, so stores to rows past the group fall outside
+    // it and are dropped without a branch.
+    const bool odd = (lane & 1) != 0;
+    const int pc = (GATED ? wn * (WTN / 2) : wn * WTN) + (lane & 31) - (odd ? 1 : 0);
+    const uint32_t lane_row = (uint32_t)(wm * WTM + 4 * (lane >> 5) + (odd ? 1 : 0));
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(C + (size_t)row0 * a.ldc + n0, (uint32_t)((size_t)rows * a.ldc * 2 - (size_t)n0 * 2));
+    if (n0 + pc < a.Ndim) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < OUT_TN; ++j) {
+          const uint32_t vC = (lane_row * a.ldc + pc + 32 * j) * 2u;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            float x[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float g = acc[i][j][v + q];
+              if constexpr (EPI == EPI_SWIGLU) x[q] = silu_fast(g) * acc[i][j + TN / 2][v + q];
+              else if constexpr (EPI == EPI_RELU) x[q] = g > 0.0f ? g : 0.0f;
+              else x[q] = g;
+            }
+            // quad_perm [1,0,3,2]: each lane receives its neighbour's value
+            const float send = odd ? x[0] : x[1];
+            const float got = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+            f32x2 pr;
+            pr[0] = odd ? got : x[0];
+            pr[1] = odd ? x[1] : got;
+            const int rr = 32 * i + 8 * (v >> 2) + (v & 3);   // uniform part of the row
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)),
+                                                  rC, vC, rr * a.ldc * 2, 0);
+          }
+        }
+    }
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) {
     // a = act(g[, v]) to C; dG (and dU) from dA to C2
     const uint16_t* D = static_cast<const uint16_t*>(a.D);
@@ -785,6 +849,225 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
     else gemm_tile<EPI, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
   } else if (find_tail(a, 256, ntiles, h - real, g, row0, rows, by)) {
     gemm_tile<EPI, kTailRows, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, BT, true>(a, g, row0, rows, by, sA, sB);
+  }
+}
+
+// Stage 0 of a 256-column tile (rows <= 320, 8 waves, row-major B) into LDS
+// buffer buf: the same loads, lane mapping and LDS slots as the first stage
+// the tile body issues itself, for a tile of BMk = 320, 256 or 64 rows.
+template <int EPI, int SAN, int SBN>
+__device__ __forceinline__ void issue_stage0(const GemmArgs& a, int g, int row0, int rows, int by,
+                                             int BMk, int buf, u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN]) {
+  constexpr int NW = 8, BN = 256, BI = BN / 8 / NW;
+  constexpr bool GATED = gated<EPI>();
+  constexpr int BNH = GATED ? BN / 2 : BN;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  by = __builtin_amdgcn_readfirstlane(by);
+  BMk = __builtin_amdgcn_readfirstlane(BMk);
+  const int AI = BMk / 8 / NW;
+  const int n0 = by * BNH;
+  const int lrow = lane >> 3;
+  const int lchunk_even = (lane & 7) ^ (lrow >> 1);
+  const int lchunk_odd = (lane & 7) ^ (4 + (lrow >> 1));
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda, (uint32_t)rows * a.lda * 2);
+  lds_t* ldsA = (lds_t*)&sA[buf][wave * AI * 64];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    if (i >= AI) break;
+    const bool odd = ((wave * AI + i) & 1) != 0;
+    const uint32_t voff = (uint32_t)(((wave * AI + i) * 8 + lrow) * a.lda + (odd ? lchunk_odd : lchunk_even) * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t*)((char*)ldsA + i * 1024), 16, voff, 0, 0, 0);
+  }
+  const uint16_t* Bsrc = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
+  int b_local0 = wave * (BN / NW);
+  if constexpr (GATED) {
+    if (wave >= NW / 2) {
+      Bsrc = static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride;
+      b_local0 -= BN / 2;
+    }
+  }
+  Bsrc += (size_t)n0 * a.ldb;
+  const int b_valid = a.Ndim - n0 < BNH ? a.Ndim - n0 : BNH;
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bsrc, (uint32_t)b_valid * a.ldb * 2);
+  lds_t* ldsB = (lds_t*)&sB[buf][wave * BI * 64];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const bool odd = ((wave * BI + i) & 1) != 0;
+    const uint32_t voff = (uint32_t)((b_local0 + i * 8 + lrow) * a.ldb + (odd ? lchunk_odd : lchunk_even) * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t*)((char*)ldsB + i * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// Persistent launches split the 1-D tile space [0, total) into 9 queues:
+// queue y < 8 holds the y-th run of q = full/8 tiles of the patch order
+// (full = full tiles rounded down to a multiple of 8), queue 8 the rest.
+// Position t of queue y is tile slot h (find_tile_2d / find_tail), or -1
+// past the queue's end.
+__host__ __device__ inline int queue_slot(int y, int t, int q, int full, int rest) {
+  if (y < 8) return t < q ? 8 * t + y : -1;
+  return t < rest ? full + t : -1;
+}
+
+// Tail tiles of all groups (single-group form: from M).
+__host__ __device__ inline int tail_tiles_total(const GemmArgs& a, int BM) {
+  if (a.offsets != nullptr) return a.tails[a.G];
+  int f, t;
+  split_rows(a.M, BM, a.tail_rows, a.ext_rows, f, t);
+  return t;
+}
+
+// Persistent form of grouped_gemm_bf16_kernel for the forward epilogues:
+// one block per compute unit, each taking tiles from a work queue until it
+// is empty, so the blocks that draw the taller 320-row tiles take fewer of
+// them and no block waits on a second wave of launches.
+//
+// The tiles are the kernel's 1-D tile space (full tiles, then tail tiles).
+// Its first full tiles (a multiple of 8) are split into 8 equal contiguous
+// runs of the patch order, one per XCD: block b sits on XCD b % 8 (blocks
+// are dealt to the XCDs round-robin) and takes tiles from queue[b % 8], so
+// one XCD's compute units work through neighbouring patches and share their
+// panels in that XCD's L2.  A block whose run is used up takes the other
+// runs' remaining tiles, then queue[8]: the leftover full tiles and the tail
+// tiles.  Counters are bumped by one lane with a global atomic; they start
+// at zero (the plan kernel clears them).
+//
+// Each block reserves its next tile one tile ahead and, after the main loop
+// of the current tile, issues that tile's first stage into the free LDS
+// buffer, so those loads are in flight during the current epilogue.
+template <int EPI>
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_persistent_kernel(GemmArgs ga) {
+  __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
+  __shared__ u32x4 sB[2][256 * 8];
+  // the tile plan (group offsets and tile prefixes), copied once so that
+  // locating a tile takes LDS reads instead of dependent global loads
+  __shared__ int32_t s_plan[3][257];
+  __shared__ int s_next, s_cur, s_spec;
+  constexpr int SAN = (256 + kExtRows) * 8, SBN = 256 * 8;
+  constexpr int BNH = gated<EPI>() ? 128 : 256;
+  const int tid = threadIdx.x;
+  GemmArgs a = ga;
+  if (a.offsets != nullptr) {
+    for (int i = tid; i <= a.G; i += blockDim.x) {
+      s_plan[0][i] = a.offsets[i];
+      s_plan[1][i] = a.tiles[i];
+      s_plan[2][i] = a.tails[i];
+    }
+    a.offsets = s_plan[0];
+    a.tiles = s_plan[1];
+    a.tails = s_plan[2];
+  }
+  if (tid == 0) {
+    s_cur = 0;
+    s_spec = -1;
+  }
+  __syncthreads();
+  const int ntiles = (a.Ndim + BNH - 1) / BNH;
+  const int real = full_tiles_total(a, 256) * ntiles;
+  const int total = real + tail_tiles_total(a, 256) * ntiles;
+  const int full = real - real % 8;
+  const int q = full / 8;                    // tiles per XCD run
+  const int rest = total - full;             // queue[8]: leftovers and tails
+  const int xcd = blockIdx.x & 7;
+  int32_t* queue = a.queue;
+
+  // Thread 0 only.  The queue being drained (s_cur 0: own run, 1..7: the
+  // runs of the next XCDs, 8: leftovers and tails, 9: none) and the
+  // position reserved in the own run ahead of time (s_spec, -1: none) live
+  // in LDS.  The reservation for the tile after next is requested here and
+  // its value written to s_spec only after the current tile's epilogue, so
+  // no wave waits on the atomic.
+  int pending = -1;
+  auto claim = [&]() -> int {
+    int cur = s_cur;
+    int spec = s_spec;
+    int h = -1;
+    while (cur < 9) {
+      const int y = cur < 8 ? (xcd + cur) & 7 : 8;
+      const int t = (cur == 0 && spec >= 0) ? spec : atomicAdd(&queue[y], 1);
+      spec = -1;
+      h = queue_slot(y, t, q, full, rest);
+      if (h >= 0) break;
+      ++cur;
+    }
+    s_cur = cur;
+    s_spec = -1;
+    pending = cur == 0 ? atomicAdd(&queue[xcd], 1) : -1;
+    return h;
+  };
+  // a tile of the 1-D space: coordinates and height class (320, 256, 64);
+  // false when it holds no rows
+  // (block-uniform results: kept in scalar registers)
+  auto decode = [&](int h, int& g, int& row0, int& rows, int& by, int& bm) -> bool {
+    bool ok = true;
+    if (h < real) {
+      find_tile_2d(a, 256, ntiles, h, real, g, row0, rows, by);
+      bm = rows > 256 ? 256 + kExtRows : 256;
+    } else {
+      bm = kTailRows;
+      ok = find_tail(a, 256, ntiles, h - real, g, row0, rows, by);
+    }
+    g = __builtin_amdgcn_readfirstlane(g);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    rows = __builtin_amdgcn_readfirstlane(rows);
+    by = __builtin_amdgcn_readfirstlane(by);
+    bm = __builtin_amdgcn_readfirstlane(bm);
+    return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+  };
+
+  if (tid == 0) s_next = claim();
+  __syncthreads();
+  if (tid == 0) s_spec = pending;
+  int h = __builtin_amdgcn_readfirstlane(s_next);
+  int g = 0, row0 = 0, rows = 0, by = 0, bm = 0;
+  bool work = h >= 0 && decode(h, g, row0, rows, by, bm);
+  int b0 = 0;               // LDS buffer of the tile's stage 0
+  bool issued = false;      // its stage 0 already in flight
+  const int nk = a.Kdim / BK;
+  while (h >= 0) {
+    int h_next = -1, g2 = 0, r2 = 0, n2 = 0, y2 = 0, bm2 = 0;
+    bool next_work = false;
+    // after the main loop: publish the reserved tile, request the next
+    // reservation, and start the reserved tile's loads into the free buffer
+    auto pre = [&](int free_buf) {
+      if (tid == 0) s_next = claim();
+      __syncthreads();
+      h_next = __builtin_amdgcn_readfirstlane(s_next);
+      next_work = h_next >= 0 && decode(h_next, g2, r2, n2, y2, bm2);
+      if (next_work) issue_stage0<EPI, SAN, SBN>(a, g2, r2, n2, y2, bm2, free_buf, sA, sB);
+    };
+    if (!work) {
+      // a tile slot without rows: nothing computed, nothing was issued for
+      // it, and buffer b0 stays free (every wave has read s_next before
+      // thread 0 writes it again)
+      __syncthreads();
+      pre(b0);
+    } else {
+      if (bm == 256 + kExtRows)
+        gemm_tile<EPI, 256 + kExtRows, 256, 2, 4, SAN, SBN, false, true>(a, g, row0, rows, by, sA, sB, b0, issued, pre);
+      else if (bm == 256)
+        gemm_tile<EPI, 256, 256, 2, 4, SAN, SBN, false, true>(a, g, row0, rows, by, sA, sB, b0, issued, pre);
+      else
+        gemm_tile<EPI, kTailRows, 256, 2, 4, SAN, SBN, false, true>(a, g, row0, rows, by, sA, sB, b0, issued, pre);
+      b0 = (nk + b0) & 1;
+    }
+    // the reservation has long arrived; the next tile's first barrier
+    // publishes it
+    if (tid == 0) s_spec = pending;
+    issued = next_work;
+    work = next_work;
+    h = h_next;
+    g = g2;
+    row0 = r2;
+    rows = n2;
+    by = y2;
+    bm = bm2;
   }
 }
 
@@ -1225,9 +1508,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs a, int B
 // (split_rows), one block: tiles[g], tails[g] for g = 0..G.
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, int G, int BMr,
                                                         int tail_rows, int ext_rows,
-                                                        int32_t* tiles, int32_t* tails) {
+                                                        int32_t* tiles, int32_t* tails,
+                                                        int32_t* queues) {
   __shared__ int32_t s[256], t[256];
   const int g = threadIdx.x;
+  // the persistent GEMM launches that follow start from empty queues
+  if (queues != nullptr && g < kQueueSets * kQueueInts) queues[g] = 0;
   int f = 0, tl = 0;
   if (g < G) split_rows(offsets[g + 1] - offsets[g], BMr, tail_rows, ext_rows, f, tl);
   s[g] = f;
@@ -1251,6 +1537,20 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, 
   }
 }
 
+// compute units of the current device (cached per device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Tile shape per problem: large groups use 256x256 tiles (8 waves of
 // 128x64); groups of a few hundred rows use 128-row tiles, which double the
 // number of blocks; groups of a few rows (decode-sized batches) use 32-row
@@ -1263,7 +1563,14 @@ template <int EPI, bool BT = false>
 hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
   constexpr int BNH = gated<EPI>() ? 128 : 256;
   dim3 grid(mtiles * ((a.Ndim + BNH - 1) / BNH));
-  if (bm == 256)
+  constexpr bool kFwd = !BT && (EPI == EPI_NONE || EPI == EPI_SWIGLU || EPI == EPI_RELU);
+  if (bm == 256 && kFwd && a.queue != nullptr) {
+    // one block per compute unit, a multiple of the 8 XCDs
+    int blocks = cu_count() / 8 * 8;
+    if (blocks < 8) blocks = 8;
+    hipLaunchKernelGGL((grouped_gemm_bf16_persistent_kernel<kFwd ? EPI : EPI_NONE>), dim3(blocks),
+                       dim3(512), 0, s, a);
+  } else if (bm == 256)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
   else if (bm == 128) {
     if constexpr (EPI == EPI_NONE && !BT)
@@ -1322,9 +1629,10 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   // grid bound: at most rows/bm + 1 full tiles and one tail tile per group
   const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N + (tail_rows > 0 ? p.N : 0);
   int32_t* tails = tiles + (p.N + 2);
+  int32_t* queues = tiles + 2 * (p.N + 2);
 
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, offsets, p.N, bm, tail_rows,
-                     ext_rows, tiles, tails);
+                     ext_rows, tiles, tails, queues);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -1339,6 +1647,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g1.tails = tails;
   g1.tail_rows = tail_rows;
   g1.ext_rows = ext_rows;
+  g1.queue = queues;
   g1.G = p.N;
   g1.rows_alloc = rows_alloc;
   g1.Ndim = p.d_ff;
@@ -1356,6 +1665,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g2.B0 = w_down;
   g2.B1 = nullptr;
   g2.C = y_perm;
+  g2.queue = queues + kQueueInts;
   g2.Ndim = p.d;
   g2.Kdim = p.d_ff;
   g2.lda = p.d_ff;
@@ -1389,6 +1699,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     s1.tails = nullptr;
     s1.tail_rows = s_tail;
     s1.ext_rows = s_ext;
+    s1.queue = queues + 2 * kQueueInts;
     s1.G = 1;
     s1.M = p.T;
     s1.rows_alloc = p.T;
@@ -1403,6 +1714,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     if ((e = run_gemm(s1, epi1, bf16, sbm, mt, s)) != hipSuccess) return e;
     GemmArgs s2 = s1;
     s2.A = act_shared;
+    s2.queue = queues + 3 * kQueueInts;
     s2.B0 = ws_down;
     s2.B1 = nullptr;
     s2.C = y_shared;
@@ -1450,20 +1762,6 @@ WgradArgs wgrad_args(const void* A, int lda, const void* B, int ldb, const int32
   w.nseg = nseg;
   w.nseg_stride = nseg_stride;
   return w;
-}
-
-// compute units of the current device (cached per device)
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 hipError_t run_wgrad(const WgradArgs& w, hipStream_t s) {
@@ -1514,7 +1812,7 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   int32_t* tiles = b.tiles;
   int32_t* tails = tiles + (p.N + 2);
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, b.offsets, p.N, bm, tail_rows,
-                     ext_rows, tiles, tails);
+                     ext_rows, tiles, tails, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

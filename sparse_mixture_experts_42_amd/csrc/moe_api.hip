@@ -28,7 +28,7 @@ Workspace workspace_layout(const moe_problem_t& p) {
   w.disp_q = off;
   off = align_up(off + K * N * 4, kAlign);
   w.tiles = off;
-  off = align_up(off + 2 * (N + 2) * 4, kAlign);
+  off = align_up(off + gemm_plan_bytes(N), kAlign);
   w.act = off;
   off = align_up(off + T * K * (size_t)p.d_ff * es, kAlign);
   w.act_shared = off;
@@ -63,7 +63,7 @@ EcWorkspace ec_workspace_layout(const moe_problem_t& p) {
   w.tk_gate = off;
   off = align_up(off + T * K * 4, kAlign);
   w.tiles = off;
-  off = align_up(off + 2 * (N + 2) * 4, kAlign);
+  off = align_up(off + gemm_plan_bytes(N), kAlign);
   w.act = off;
   off = align_up(off + N * (size_t)w.C * (size_t)p.d_ff * es, kAlign);
   w.act_shared = off;

@@ -41,13 +41,20 @@ int route_pre_splits(const moe_problem_t& p);
 size_t route_pre_bytes(const moe_problem_t& p);
 constexpr int kDispatchTok = 256;   // tokens per dispatch block
 
+// Grouped-GEMM plan: full- and tail-tile prefixes ([2][N+2] int32), then
+// the work-queue counters of the persistent GEMM launches (kQueueSets sets
+// of kQueueInts, zeroed by the plan kernel before each grouped FFN).
+constexpr int kQueueInts = 16;
+constexpr int kQueueSets = 4;
+inline size_t gemm_plan_bytes(size_t N) { return (2 * (N + 2) + kQueueSets * kQueueInts) * 4; }
+
 struct Workspace {
   size_t route_part;   // fp32 [route_blocks][N]   per-block softmax sums
   size_t route_pre;    // fp32 [slices][T][N]       split-k logits (few tokens)
   size_t disp_count;   // int32 [disp_blocks][K][N]  per-block expert counts (per choice rank)
   size_t disp_base;    // int32 [disp_blocks][K][N]  per-block rank base
   size_t disp_q;       // int32 [K][N]               kept per choice rank
-  size_t tiles;        // int32 [2][N+2]          grouped-GEMM full and tail tile prefixes
+  size_t tiles;        // int32 gemm_plan_bytes(N)  grouped-GEMM tile prefixes, queue counters
   size_t act;          // elem [T*K][d_ff]        gated activations
   size_t act_shared;   // elem [T][n_shared*d_ff_shared]
   size_t total;

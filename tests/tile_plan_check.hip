@@ -48,6 +48,50 @@ static int check(const std::vector<int>& sizes, int ntiles, bool single, int BM,
   for (size_t i = 0; i < cover.size(); ++i) if (cover[i] != 1) { printf("row %zu covered %d times\n", i / ntiles, cover[i]); return 1; }
   return 0;
 }
+// The persistent launch's work queues: blocks on 8 XCDs claim positions in
+// random interleavings (own run first, then the other runs, then queue 8,
+// with positions reserved one claim ahead as the kernel does); every tile
+// slot of [0, total) must be handed out exactly once.
+static int check_queues(const std::vector<int>& sizes, int ntiles, int blocks, std::mt19937& rng) {
+  int G = (int)sizes.size();
+  std::vector<int32_t> off(G + 1, 0), tiles(G + 2, 0), tails(G + 2, 0);
+  for (int g = 0; g < G; ++g) off[g + 1] = off[g] + sizes[g];
+  for (int g = 0; g < G; ++g) {
+    int f, t;
+    split_rows(sizes[g], 256, 64, 64, f, t);
+    tiles[g + 1] = tiles[g] + f;
+    tails[g + 1] = tails[g] + t;
+  }
+  GemmArgs a{};
+  a.offsets = off.data(); a.tiles = tiles.data(); a.tails = tails.data();
+  a.tail_rows = 64; a.ext_rows = 64; a.G = G;
+  const int real = full_tiles_total(a, 256) * ntiles;
+  const int total = real + tail_tiles_total(a, 256) * ntiles;
+  const int full = real - real % 8, q = full / 8, rest = total - full;
+  std::vector<int> counter(9, 0), cur(blocks, 0), spec(blocks, -1), seen(total, 0);
+  std::vector<int> live;
+  for (int b = 0; b < blocks; ++b) live.push_back(b);
+  while (!live.empty()) {
+    const size_t k = rng() % live.size();
+    const int b = live[k], xcd = b & 7;
+    int h = -1;
+    while (cur[b] < 9) {
+      const int y = cur[b] < 8 ? (xcd + cur[b]) & 7 : 8;
+      const int t = (cur[b] == 0 && spec[b] >= 0) ? spec[b] : counter[y]++;
+      spec[b] = -1;
+      h = queue_slot(y, t, q, full, rest);
+      if (h >= 0) break;
+      ++cur[b];
+    }
+    spec[b] = cur[b] == 0 ? counter[xcd]++ : -1;
+    if (h < 0) { live.erase(live.begin() + k); continue; }
+    if (h >= total) { printf("slot %d past %d\n", h, total); return 1; }
+    seen[h]++;
+  }
+  for (int h = 0; h < total; ++h) if (seen[h] != 1) { printf("slot %d claimed %d times\n", h, seen[h]); return 1; }
+  return 0;
+}
+
 int main() {
   std::mt19937 rng(1);
   int fails = 0, n = 0;
@@ -64,6 +108,12 @@ int main() {
     fails += check(s, nt, false, 256, 64, 64); ++n;
     fails += check(s, nt, false, 128, 0, 0); ++n;
     fails += check(s, nt, false, 32, 0, 0); ++n;
+  }
+  for (int it = 0; it < 400; ++it) {
+    int G = 1 + rng() % 64;
+    std::vector<int> s(G);
+    for (auto& x : s) { int k = rng() % 3; x = k == 0 ? rng() % 70 : k == 1 ? 256 * (rng() % 9) + rng() % 80 : rng() % 3000; }
+    fails += check_queues(s, 1 + rng() % 120, 8 * (1 + rng() % 32), rng); ++n;
   }
   printf("%d cases, %d failures\n", n, fails);
   return fails != 0;
