@@ -484,6 +484,164 @@ __global__ __launch_bounds__(kThreads) void route_partial_kernel(const void* u, 
   }
 }
 
+// ------------------------------------------------- bf16 token batches
+// The fp32 router weights as three bf16 parts, W = W_hi + W_mid + W_lo:
+// W_hi keeps the top 8 significant bits of W (truncation), W_mid the top 8
+// of the residual W - W_hi and W_lo the rest.  Each residual is exact in
+// fp32 and what is left after W_mid has at most 8 significant bits, so the
+// sum is exactly W for every finite |W| >= 2^-90 (below that the last part
+// falls into the subnormals and loses less than 2^-133).  A bf16 token value
+// times a part is exact in fp32, so the bf16 matrix instruction with fp32
+// accumulation evaluates the fp32 router dot product.
+__host__ __device__ inline uint16_t bf16_trunc_bits(float f) {
+  uint32_t x;
+  __builtin_memcpy(&x, &f, 4);
+  return (uint16_t)(x >> 16);
+}
+__host__ __device__ inline float bf16_bits_to_f32(uint16_t h) {
+  const uint32_t x = (uint32_t)h << 16;
+  float f;
+  __builtin_memcpy(&f, &x, 4);
+  return f;
+}
+__host__ __device__ inline void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = bf16_trunc_bits(w);
+  const float r1 = w - bf16_bits_to_f32(hi);
+  mid = bf16_trunc_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(mid);
+  lo = bf16_trunc_bits(r2);
+}
+
+// wp[part][e][k] for e < Np (rows e >= N are zero), four k per thread.
+__global__ __launch_bounds__(256) void route_split_kernel(const float* w, int N, int Np, int d,
+                                                          uint16_t* wp) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long per_part = (long long)Np * d;
+  if (i * 4 >= per_part) return;
+  const int e = (int)(i * 4 / d), k = (int)(i * 4 - (long long)e * d);
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (e < N) x = *reinterpret_cast<const float4*>(w + (size_t)e * d + k);
+  const float v[4] = {x.x, x.y, x.z, x.w};
+  uint16_t q[3][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) split3(v[j], q[0][j], q[1][j], q[2][j]);
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    uint2 o;
+    o.x = (uint32_t)q[p][0] | ((uint32_t)q[p][1] << 16);
+    o.y = (uint32_t)q[p][2] | ((uint32_t)q[p][3] << 16);
+    *reinterpret_cast<uint2*>(wp + (size_t)p * per_part + (size_t)e * d + k) = o;
+  }
+}
+
+// Router logits of bf16 tokens on the bf16 matrix cores:
+//   pre[s][t][e] = sum over k in d-slice s of u[t][k] * (W_hi + W_mid + W_lo)[e][k]
+// Block (token tile, expert tile, slice s): 32*EXP_T experts x TOKB tokens,
+// four waves of 32 experts x 32 tokens (v_mfma_f32_32x32x16_bf16, experts as
+// the A rows, tokens as the B columns, three instructions per 16-wide k-step,
+// one per weight part).  Token rows and weight parts go through LDS in
+// 64-wide k chunks, loaded straight from global memory into a ring of three
+// stages (1-KB buffer loads, 8 rows of 128 bytes each, so every load reads
+// whole cache lines); two chunks are in flight while one is multiplied.
+// Rows past the batch or past the experts read zero through the buffer
+// descriptors' sizes.  LDS rows hold 8 chunks of 16 bytes, chunk c of row r
+// at slot c ^ ((r >> 1) & 7), so the operand reads of 16 lanes hit 16
+// different 16-byte bank groups.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int EXP_T, int NW, int NS>
+__global__ __launch_bounds__(64 * NW) void route_logits_kernel(const uint16_t* u, const uint16_t* wp, int T,
+                                                               int d, int N, int Np, int dk, float* pre) {
+  constexpr int NE = 32 * EXP_T;              // experts per block
+  constexpr int TOKB = 32 * NW / EXP_T;       // tokens per block
+  constexpr int PD = NS - 1;                  // chunks in flight
+  constexpr int UQ = TOKB / 8 / NW;           // 1-KB token loads per wave per chunk
+  constexpr int WQ = 3 * NE / 8 / NW;         // 1-KB weight loads per wave per chunk
+  constexpr int LPW = UQ + WQ;
+  static_assert(UQ * 8 * NW == TOKB && WQ * 8 * NW == 3 * NE, "whole loads per wave");
+  __shared__ u32x4 sU[NS][TOKB * 8];
+  __shared__ u32x4 sW[NS][3 * NE * 8];        // [part][row][8 slots]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int et = wave % EXP_T, tt = wave / EXP_T;
+  const int t0 = blockIdx.x * TOKB, e0 = blockIdx.y * NE, s = blockIdx.z;
+  const int kbeg = s * dk, nch = dk / 64;
+  const size_t per_part = (size_t)Np * d;
+
+  // buffer descriptors: the block's token rows, each part's expert rows
+  const int trows = T - t0 < TOKB ? T - t0 : TOKB;
+  const int erows = N - e0 < NE ? N - e0 : NE;
+  const __amdgpu_buffer_rsrc_t rU = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(u + (size_t)t0 * d + kbeg), (short)0, (int)((uint32_t)trows * d * 2), 0x00020000);
+  __amdgpu_buffer_rsrc_t rW[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    rW[p] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wp + p * per_part + (size_t)e0 * d + kbeg),
+                                              (short)0, (int)((uint32_t)erows * d * 2), 0x00020000);
+  // load q of a chunk fills rows 8q .. 8q+7; lane l row 8q + l/8, slot l%8,
+  // which holds chunk (l%8) ^ ((8q + l/8) >> 1 & 7)
+  const int lrow = lane >> 3;
+  const int ch_even = (lane & 7) ^ (lrow >> 1), ch_odd = (lane & 7) ^ (4 + (lrow >> 1));
+  auto issue = [&](int c, int buf) {
+    const uint32_t kb = (uint32_t)c * 128u;   // bytes into the slice
+#pragma unroll
+    for (int i = 0; i < UQ; ++i) {
+      const int q = wave * UQ + i;
+      const uint32_t voff = (uint32_t)((8 * q + lrow) * d) * 2u + kb + (uint32_t)((q & 1) ? ch_odd : ch_even) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rU, (lds_void*)&sU[buf][q * 64], 16, voff, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
+      const int q = wave * WQ + i;            // over 3 parts x NE/8 row groups
+      const int p = q / (NE / 8), qr = q - p * (NE / 8);
+      const uint32_t voff = (uint32_t)((8 * qr + lrow) * d) * 2u + kb + (uint32_t)((qr & 1) ? ch_odd : ch_even) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW[p], (lds_void*)&sW[buf][q * 64], 16, voff, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  const int arow = et * 32 + (lane & 31), brow = tt * 32 + (lane & 31);
+#pragma unroll
+  for (int c = 0; c < PD; ++c)
+    if (c < nch) issue(c, c);
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c % NS;
+    // chunk c has landed once at most the loads of the chunks after it
+    // (up to PD - 1 of them) are pending
+    const int later = nch - 1 - c < PD - 1 ? nch - 1 - c : PD - 1;
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPW) : "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // every wave is past chunk c-1, whose buffer takes chunk c + PD
+    if (c + PD < nch) issue(c + PD, (c + PD) % NS);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 2 * kk + (lane >> 5);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, sU[buf][brow * 8 + (ch ^ ((brow >> 1) & 7))]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, sW[buf][(p * NE + arow) * 8 + (ch ^ ((arow >> 1) & 7))]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+  }
+  // lane: token t0 + brow, experts e0 + et*32 + 8*(v/4) + 4*(lane/32) + v%4
+  const int t = t0 + brow;
+  if (t >= T) return;
+  float* out = pre + ((size_t)s * T + t) * N;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int e = e0 + et * 32 + 8 * g + 4 * (lane >> 5);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (e + v < N) out[e + v] = acc[4 * g + v];
+  }
+}
+
 // The slices summed in slice order, one thread per (token, expert), eight
 // loads in flight: out[t][e] = sum_s pre[s][t][e].
 __global__ __launch_bounds__(256) void route_pre_reduce_kernel(const float* pre, int S, long long TN,
@@ -603,8 +761,10 @@ hipError_t launch_gp(const RouteArgs& a, int blocks, hipStream_t s) {
   return launch_g<E, TG, NT, G, false>(a, blocks, s);
 }
 
-// Lanes per token G: the smallest power of two >= N (at least 4, at most
-// 64); that fixes G for every padded width above 16 experts.
+// Lanes per token G: up to 16 experts, the smallest power of two >= N (at
+// least 4), one expert per lane; wider routers use 16 lanes per token, each
+// holding NT experts, so a wave selects for four tokens at once with
+// four-step butterflies.
 template <typename E, int TG, int NT>
 hipError_t launch_gsel(const moe_problem_t& p, const RouteArgs& a, int blocks, hipStream_t s) {
   if constexpr (NT == 1) {
@@ -612,7 +772,7 @@ hipError_t launch_gsel(const moe_problem_t& p, const RouteArgs& a, int blocks, h
     if (p.N <= 8) return launch_gp<E, TG, 1, 8>(a, blocks, s);
     return launch_gp<E, TG, 1, 16>(a, blocks, s);
   } else {
-    return launch_gp<E, TG, NT, (16 * NT < 64 ? 16 * NT : 64)>(a, blocks, s);
+    return launch_gp<E, TG, NT, 16>(a, blocks, s);
   }
 }
 
@@ -641,13 +801,52 @@ hipError_t launch_tg(const moe_problem_t& p, const RouteArgs& a, int blocks, hip
 
 }  // namespace
 
-// Few-token batches (fewer than 256 tiles of 16 tokens) would leave most of
-// the chip idle with one block per 16 tokens: their logits are computed in
-// pre_splits slices of d by route_partial_kernel first (at least ~512
+// bf16 token batches with more than 32 experts (where the fp32 router
+// products, not the token stream, bound the router): the logits come from
+// route_logits_kernel over S slices of d, chosen so that the grid has at
+// least ~256 blocks (one per CU, whose LDS the ring fills) with S dividing
+// d/64; the selection kernel then reads them.  Narrower routers keep the
+// fused fp32 kernel, which streams the tokens in one launch.
+// Up to 32 experts: 4 waves of 32 tokens and a 5-stage ring (the token
+// stream is the traffic; four chunks in flight).  Wider: 8 waves of 32
+// tokens x 2 expert tiles of 32, 128 tokens per block, a 3-stage ring: the
+// weight parts, re-read by every block, are shared by twice as many tokens.
+struct Bf3Plan {
+  int exp_t, ne, np, tokb, gx, gy, S;
+};
+Bf3Plan bf3_plan(const moe_problem_t& p) {
+  Bf3Plan q;
+  q.exp_t = p.N > 32 ? 2 : 1;
+  q.ne = 32 * q.exp_t;
+  q.np = (p.N + q.ne - 1) / q.ne * q.ne;
+  q.tokb = 128;
+  q.gx = (p.T + q.tokb - 1) / q.tokb;
+  q.gy = q.np / q.ne;
+  const int want = (256 + q.gx * q.gy - 1) / (q.gx * q.gy);
+  const int kc = p.d / 64;
+  q.S = kc;
+  for (int c = 1; c <= kc; ++c)
+    if (kc % c == 0 && c >= want) {
+      q.S = c;
+      break;
+    }
+  return q;
+}
+// slices the selection kernel sums itself; more are summed by
+// route_pre_reduce_kernel first
+constexpr int kSelectSlices = 8;
+
+// fp32 token batches with fewer than 256 tiles of 16 tokens would leave most
+// of the chip idle with one block per 16 tokens: their logits are computed
+// in pre_splits slices of d by route_partial_kernel first (at least ~512
 // blocks), then summed by the routing blocks.  0: the fused path.
+bool use_bf3(const moe_problem_t& p) { return p.dtype == MOE_BF16 && p.N > 32; }
+
 int route_pre_splits(const moe_problem_t& p) {
+  if (p.T == 0) return 0;
+  if (use_bf3(p)) return bf3_plan(p).S;
   const int tiles = (p.T + 15) / 16;
-  if (tiles >= 256 || p.T == 0) return 0;
+  if (tiles >= 256) return 0;
   const int groups = (p.N + 63) / 64;
   int S = 1;
   while (S < 32 && S * 2 * 32 <= p.d / 4 && p.d % (S * 2 * 32) == 0 && tiles * groups * S < 512)
@@ -655,9 +854,16 @@ int route_pre_splits(const moe_problem_t& p) {
   return S;
 }
 
+// [S][T][N] partial logits, their sum when S > kSelectSlices (bf16) or S > 0
+// (fp32), and for bf16 the three weight parts [3][Np][d]
 size_t route_pre_bytes(const moe_problem_t& p) {
   const int S = route_pre_splits(p);
-  return S > 0 ? (size_t)(S + 1) * p.T * p.N * sizeof(float) : 0;
+  if (S == 0) return 0;
+  const size_t TN = (size_t)p.T * p.N * sizeof(float);
+  if (!use_bf3(p)) return (size_t)(S + 1) * TN;
+  const Bf3Plan q = bf3_plan(p);
+  const size_t logits = align_up((size_t)(S + (S > kSelectSlices ? 1 : 0)) * TN, kAlign);
+  return logits + (size_t)3 * q.np * p.d * sizeof(uint16_t);
 }
 
 // Small expert counts keep the router HBM-bound: few tokens per block, many
@@ -693,14 +899,44 @@ hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_ro
   a.gating = p.gating;
   a.pre = nullptr;
   a.pre_splits = route_pre_splits(p);
-  if (a.pre_splits > 0) {
+  const long long TN = (long long)p.T * p.N;
+  if (use_bf3(p)) {
+    const Bf3Plan q = bf3_plan(p);
+    const int S = q.S, dk = p.d / S;
+    uint16_t* wp = reinterpret_cast<uint16_t*>(
+        reinterpret_cast<char*>(pre) +
+        align_up((size_t)(S + (S > kSelectSlices ? 1 : 0)) * (size_t)TN * sizeof(float), kAlign));
+    const long long pieces = (long long)q.np * p.d / 4;
+    hipLaunchKernelGGL(route_split_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s,
+                       w_router, p.N, q.np, p.d, wp);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    const dim3 grid(q.gx, q.gy, S);
+    if (q.exp_t == 1)
+      hipLaunchKernelGGL((route_logits_kernel<1, 4, 5>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(u),
+                         (const uint16_t*)wp, p.T, p.d, p.N, q.np, dk, pre);
+    else
+      hipLaunchKernelGGL((route_logits_kernel<2, 8, 3>), grid, dim3(512), 0, s, static_cast<const uint16_t*>(u),
+                         (const uint16_t*)wp, p.T, p.d, p.N, q.np, dk, pre);
+    e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    a.pre = pre;
+    if (S > kSelectSlices) {
+      float* summed = pre + (size_t)S * TN;
+      hipLaunchKernelGGL(route_pre_reduce_kernel, dim3((unsigned)((TN + 255) / 256)), dim3(256), 0, s,
+                         (const float*)pre, S, TN, summed);
+      e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+      a.pre = summed;
+      a.pre_splits = 1;
+    }
+  } else if (a.pre_splits > 0) {
     const int S = a.pre_splits, dk = p.d / S;
     const int nt = pow2_at_least((p.N + 15) / 16);
     const dim3 grid((p.T + 15) / 16, S, (p.N + 63) / 64);
     if (p.dtype == MOE_BF16) {
       if (nt == 1) hipLaunchKernelGGL((route_partial_kernel<uint16_t, 1>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
-      else if (nt == 2) hipLaunchKernelGGL((route_partial_kernel<uint16_t, 2>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
-      else hipLaunchKernelGGL((route_partial_kernel<uint16_t, 4>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
+      else hipLaunchKernelGGL((route_partial_kernel<uint16_t, 2>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
     } else {
       if (nt == 1) hipLaunchKernelGGL((route_partial_kernel<float, 1>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
       else if (nt == 2) hipLaunchKernelGGL((route_partial_kernel<float, 2>), grid, dim3(kThreads), 0, s, u, w_router, p.T, p.d, p.N, dk, pre);
@@ -709,7 +945,6 @@ hipError_t launch_route(const moe_problem_t& p, const void* u, const float* w_ro
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     // the slices summed into slice S, which the routing blocks then read
-    const long long TN = (long long)p.T * p.N;
     float* summed = pre + (size_t)S * TN;
     hipLaunchKernelGGL(route_pre_reduce_kernel, dim3((unsigned)((TN + 255) / 256)), dim3(256), 0, s,
                        (const float*)pre, S, TN, summed);

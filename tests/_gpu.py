@@ -62,8 +62,11 @@ def assert_close(got, ref, dtype, what):
 
 
 def kth_gap(H, K):
-    """Gap between the K-th and (K+1)-th largest score per token (inf if K == N)."""
+    """Smallest gap between consecutive scores among the K+1 largest per
+    token (the K largest only if K == N): the top-K set and its slot order
+    (by rank) are fixed by the scores wherever this exceeds their error."""
     s = -np.sort(-H.astype(np.float64), axis=1)
-    if K >= H.shape[1]:
+    m = min(K + 1, H.shape[1])
+    if m < 2:
         return np.full(H.shape[0], np.inf)
-    return s[:, K - 1] - s[:, K]
+    return np.min(s[:, :m - 1] - s[:, 1:m], axis=1)

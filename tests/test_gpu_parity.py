@@ -6,8 +6,9 @@ from rows that the oracle's own dispatch permuted, combine from seeded
 expert outputs.  The chained-layer test compares the whole pass; its routing
 is checked bit-exactly with the oracle routing from the GPU's fp32 scores
 (the scores themselves are checked against the oracle's own logits), and
-independently against the oracle's own routing wherever the K-th and
-(K+1)-th scores are further apart than the score tolerance."""
+independently against the oracle's own routing wherever consecutive scores
+among the K+1 largest are further apart than twice the score tolerance (a
+closer pair can swap the slot order or the K-th expert under rounding)."""
 import numpy as np
 import pytest
 import torch
@@ -41,9 +42,11 @@ def _route_checks(w, p, x, r_gpu):
     # independent: the oracle's own routing, away from near ties
     own = O.route(po, H_o)
     sep = kth_gap(H_o, w.K) > 2 * SCORE_TOL
-    say(f"{w.name}: {int((~sep).sum())} of {w.T} tokens within a near tie of the K-th score")
+    say(f"{w.name}: {int((~sep).sum())} of {w.T} tokens with a near tie among their K+1 largest scores")
     assert np.array_equal(idx_g[sep], own["topk_idx"][sep])
-    assert (~sep).sum() <= max(4, w.T // 100)
+    # near ties are rare: at most about one token in a hundred per gap
+    # considered (K of them), so most tokens are checked independently
+    assert (~sep).sum() <= max(4, w.T * min(w.K, w.N - 1) // 100)
     return ro
 
 

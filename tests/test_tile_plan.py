@@ -2,7 +2,9 @@
 tests/tile_plan_check.hip walks the launched grid through the same
 split_rows / find_tile_2d / find_tail functions the kernel runs, for
 edge-case and random group sizes; tests/kmajor_layout_check.hip runs the
-k-major operand loads and transposing reads of the backward GEMMs."""
+k-major operand loads and transposing reads of the backward GEMMs;
+tests/router_split_check.hip checks that the router's three bf16 parts of an
+fp32 weight sum to it exactly."""
 import os
 import re
 import shutil
@@ -36,3 +38,8 @@ def test_tile_plan_covers_every_row_once(tmp_path):
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 def test_kmajor_operand_layout(tmp_path):
     _build_and_run(tmp_path, "kmajor_layout_check")
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_router_weight_split_is_exact(tmp_path):
+    _build_and_run(tmp_path, "router_split_check")
