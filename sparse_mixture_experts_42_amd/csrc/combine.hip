@@ -49,7 +49,7 @@ __device__ __forceinline__ void unpack(const u32x4& q, float* f, bool bf16) {
 // which is what keeps HBM busy when nothing is cached.
 constexpr int kChunk = 8;
 
-template <bool BF16>
+template <bool BF16, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* u, const u32x4* y_perm,
                                                       const int32_t* row_of, const float* gate,
                                                       const u32x4* y_shared, u32x4* out, int T,
@@ -78,7 +78,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* u, const u32x
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
           const int v = v0 + 64 * c;
-          q[c] = v < vec_per_row ? y_perm[rb + v] : u32x4{0u, 0u, 0u, 0u};
+          if constexpr (NT)
+            q[c] = v < vec_per_row ? __builtin_nontemporal_load(&y_perm[rb + v]) : u32x4{0u, 0u, 0u, 0u};
+          else
+            q[c] = v < vec_per_row ? y_perm[rb + v] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
@@ -125,16 +128,20 @@ hipError_t launch_combine(const moe_problem_t& p, const void* u, const void* y_p
   const int vec_per_row = (int)((size_t)p.d * es / 16);
   long long blocks = ((long long)p.T + 3) / 4;
   if (blocks > 4096) blocks = 4096;
-  if (p.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const u32x4*>(u), static_cast<const u32x4*>(y_perm), row_of,
-                       topk_gate, static_cast<const u32x4*>(y_shared), static_cast<u32x4*>(out),
-                       p.T, p.K, vec_per_row);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const u32x4*>(u), static_cast<const u32x4*>(y_perm), row_of,
-                       topk_gate, static_cast<const u32x4*>(y_shared), static_cast<u32x4*>(out),
-                       p.T, p.K, vec_per_row);
+  const bool nt = (size_t)p.T * p.K * p.d * es > kStreamRowsBytes;
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const u32x4*>(u),
+                       static_cast<const u32x4*>(y_perm), row_of, topk_gate,
+                       static_cast<const u32x4*>(y_shared), static_cast<u32x4*>(out), p.T, p.K,
+                       vec_per_row);
+  };
+  if (p.dtype == MOE_BF16) {
+    if (nt) run(combine_kernel<true, true>);
+    else run(combine_kernel<true, false>);
+  } else {
+    if (nt) run(combine_kernel<false, true>);
+    else run(combine_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

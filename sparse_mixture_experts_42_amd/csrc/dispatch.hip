@@ -114,6 +114,7 @@ static_assert(kTok % kRowTok == 0, "blocks tile the mask chunks");
 // Copy each token row of the block (read once, 16-byte vectors, kVecPerLane
 // per lane in flight) to every kept row srow[j*16 + k]; wave w takes tokens
 // w, w+4, ... of the block.
+template <bool NT>
 __device__ __forceinline__ void copy_rows(int t0, int T, int K, const int32_t* srow,
                                           const u32x4* u, u32x4* x_perm, int vec_per_row) {
   const int lane = threadIdx.x & 63;
@@ -135,14 +136,16 @@ __device__ __forceinline__ void copy_rows(int t0, int T, int K, const int32_t* s
 #pragma unroll
         for (int i = 0; i < kVecPerLane; ++i) {
           const int v = v0 + i * 64 + lane;
-          if (v < vec_per_row) dst[v] = q[i];
+          if (v >= vec_per_row) continue;
+          if constexpr (NT) __builtin_nontemporal_store(q[i], &dst[v]);
+          else dst[v] = q[i];
         }
       }
     }
   }
 }
 
-template <bool SCAN>
+template <bool SCAN, bool NT>
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int32_t* topk_idx, const int32_t* blk_count, int chunks, const int32_t* blk_base,
     int32_t* offsets, int32_t* expert_counts, int32_t* kept_counts, int T, int N, int K,
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     token_of_row[r] = -1;
   __syncthreads();
 
-  copy_rows(t0, T, K, srow, u, x_perm, vec_per_row);
+  copy_rows<NT>(t0, T, K, srow, u, x_perm, vec_per_row);
 }
 
 // ---------------------------------------------------------------------
@@ -319,6 +322,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_levels_kernel(
   if (tid == 0) offsets[0] = 0;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256) void dispatch_permute_levels_kernel(
     const int32_t* topk_idx, const int32_t* base, const int32_t* q, const int32_t* offsets, int T,
     int N, int K, int32_t* row_of, int32_t* token_of_row, const u32x4* u, u32x4* x_perm,
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_levels_kernel(
   for (int64_t r = offsets[N] + (int64_t)blockIdx.x * 256 + tid; r < total; r += stride)
     token_of_row[r] = -1;
   __syncthreads();
-  copy_rows(t0, T, K, srow, u, x_perm, vec_per_row);
+  copy_rows<NT>(t0, T, K, srow, u, x_perm, vec_per_row);
 }
 
 }  // namespace
@@ -390,6 +394,7 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
   const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
   const int vec_per_row = (int)((size_t)p.d * es / 16);
   const unsigned blocks = (unsigned)((p.T + kRowTok - 1) / kRowTok);
+  const bool nt = (size_t)p.T * p.K * p.d * es > kStreamRowsBytes;
   if (p.drop_order == MOE_DROP_CHOICE_RANK && capacity >= 0 && p.K > 1) {
     // (K = 1 or no capacity: both orders keep the same assignments)
     hipLaunchKernelGGL(dispatch_count_levels_kernel, dim3(disp_blocks), dim3(kTok), 0, s, topk_idx,
@@ -401,10 +406,16 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
                        capacity, expert_counts, kept_counts, offsets);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dispatch_permute_levels_kernel, dim3(blocks), dim3(256), 0, s, topk_idx,
-                       (const int32_t*)blk_base, (const int32_t*)level_q, (const int32_t*)offsets,
-                       p.T, p.N, p.K, row_of, token_of_row, static_cast<const u32x4*>(u),
-                       static_cast<u32x4*>(x_perm), vec_per_row);
+    if (nt)
+      hipLaunchKernelGGL(dispatch_permute_levels_kernel<true>, dim3(blocks), dim3(256), 0, s, topk_idx,
+                         (const int32_t*)blk_base, (const int32_t*)level_q, (const int32_t*)offsets,
+                         p.T, p.N, p.K, row_of, token_of_row, static_cast<const u32x4*>(u),
+                         static_cast<u32x4*>(x_perm), vec_per_row);
+    else
+      hipLaunchKernelGGL(dispatch_permute_levels_kernel<false>, dim3(blocks), dim3(256), 0, s, topk_idx,
+                         (const int32_t*)blk_base, (const int32_t*)level_q, (const int32_t*)offsets,
+                         p.T, p.N, p.K, row_of, token_of_row, static_cast<const u32x4*>(u),
+                         static_cast<u32x4*>(x_perm), vec_per_row);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(disp_blocks), dim3(kTok), 0, s, topk_idx, p.T,
@@ -418,16 +429,19 @@ hipError_t launch_dispatch(const moe_problem_t& p, const void* u, const int32_t*
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (scan_in_block)
-    hipLaunchKernelGGL(dispatch_permute_kernel<true>, dim3(blocks), dim3(256), 0, s, topk_idx,
-                       (const int32_t*)blk_count, disp_blocks, (const int32_t*)blk_base, offsets,
-                       expert_counts, kept_counts, p.T, p.N, p.K, capacity, row_of, token_of_row,
-                       static_cast<const u32x4*>(u), static_cast<u32x4*>(x_perm), vec_per_row);
-  else
-    hipLaunchKernelGGL(dispatch_permute_kernel<false>, dim3(blocks), dim3(256), 0, s, topk_idx,
-                       (const int32_t*)blk_count, disp_blocks, (const int32_t*)blk_base, offsets,
-                       expert_counts, kept_counts, p.T, p.N, p.K, capacity, row_of, token_of_row,
-                       static_cast<const u32x4*>(u), static_cast<u32x4*>(x_perm), vec_per_row);
+  auto permute = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, topk_idx, (const int32_t*)blk_count,
+                       disp_blocks, (const int32_t*)blk_base, offsets, expert_counts, kept_counts, p.T,
+                       p.N, p.K, capacity, row_of, token_of_row, static_cast<const u32x4*>(u),
+                       static_cast<u32x4*>(x_perm), vec_per_row);
+  };
+  if (scan_in_block) {
+    if (nt) permute(dispatch_permute_kernel<true, true>);
+    else permute(dispatch_permute_kernel<true, false>);
+  } else {
+    if (nt) permute(dispatch_permute_kernel<false, true>);
+    else permute(dispatch_permute_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

@@ -29,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(x >> 16);
 }
 
+// Row buffers of the grouped FFN (x_perm, y_perm) larger than this many
+// bytes do not stay in the 256 MB Infinity Cache between the stage that
+// writes them and the one that reads them: dispatch stores x_perm and
+// combine loads y_perm with non-temporal accesses, which stream them
+// without evicting what the cache still holds.  Below it the cache serves
+// the reads.
+constexpr size_t kStreamRowsBytes = (size_t)192 << 20;
+
 // ------------------------------------------------------------- layout
 constexpr size_t kAlign = 256;
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
