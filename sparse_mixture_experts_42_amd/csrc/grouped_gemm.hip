@@ -281,6 +281,8 @@ __device__ __forceinline__ bf16x8 read_kmajor(const char* tile, int kk, int col0
 struct NoPre {
   __device__ void operator()(int) const {}
 };
+template <typename P> struct IsNoPre { static constexpr bool value = false; };
+template <> struct IsNoPre<NoPre> { static constexpr bool value = true; };
 
 // PIPE tiles may continue a persistent block's previous tile: stage 0 uses
 // LDS buffer b0 (stage k buffer (k + b0) & 1), `issued` says its loads are
@@ -305,11 +307,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   static_assert(!BT || (EPI == EPI_NONE && BN == 256), "k-major B: plain epilogue, 256 columns");
   constexpr int BNH = GATED ? BN / 2 : BN;        // output columns per tile
 
-  // opaque to the compiler, so that a persistent caller's loop recomputes
-  // the per-lane addressing of each tile instead of keeping that of every
-  // tile shape live across the loop
+  // In a persistent caller's loop (which passes a Pre step) the thread index
+  // is made opaque to the compiler, so that the loop recomputes the per-lane
+  // addressing of each tile instead of keeping that of every tile shape live
+  // across it.  Elsewhere it stays visible: the compiler then proves that the
+  // transposing LDS reads of one stage miss the direct loads into the other,
+  // and waits for no load mid-stage.
   int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  if constexpr (!IsNoPre<Pre>::value) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   // the tile coordinates are block-uniform; saying so keeps the buffer
