@@ -62,6 +62,8 @@ EcWorkspace ec_workspace_layout(const moe_problem_t& p) {
   off = align_up(off + T * K * 4, kAlign);
   w.tk_gate = off;
   off = align_up(off + T * K * 4, kAlign);
+  w.sel = off;
+  off = align_up(off + ec_select_bytes(p.T, p.N), kAlign);
   w.tiles = off;
   off = align_up(off + gemm_plan_bytes(N), kAlign);
   w.act = off;
@@ -646,7 +648,7 @@ hipError_t ec_route_launch(const moe_problem_t* p, const void* u, const float* w
                                    s);
   if (e != hipSuccess) return e;
   return moe::launch_ec_select(*p, sc, w.C, probs, expert_tokens, expert_gates, row_of, gate_of,
-                               offsets, s);
+                               offsets, ws_at(ws, w.sel), s);
 }
 
 }  // namespace

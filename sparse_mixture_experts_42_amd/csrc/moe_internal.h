@@ -177,9 +177,14 @@ BwdWorkspace bwd_workspace_layout(const moe_problem_t& p);
 int wgrad_transposed_ld(const moe_problem_t& p);
 
 // expert choice (expert_choice.hip)
+// 64-token words of the per-expert selection masks; sel holds
+// uint64 [N][words] masks then int32 [N][words] chosen-before counts
+inline int ec_select_words(int T) { return (T + 63) / 64; }
+inline size_t ec_select_bytes(int T, int N) { return (size_t)N * ec_select_words(T) * 12; }
 hipError_t launch_ec_select(const moe_problem_t& p, const float* scores, int32_t C,
                             float* probsT, int32_t* expert_tokens, float* expert_gates,
-                            int32_t* row_of, float* gate_of, int32_t* offsets, hipStream_t s);
+                            int32_t* row_of, float* gate_of, int32_t* offsets, void* sel,
+                            hipStream_t s);
 hipError_t launch_ec_gather(const moe_problem_t& p, const void* u, const int32_t* tokens,
                             int rows, void* x_perm, hipStream_t s);
 hipError_t launch_ec_combine(const moe_problem_t& p, const void* u, const void* y_perm,
@@ -192,6 +197,7 @@ struct EcWorkspace {
   size_t scores;       // fp32 [T][N]      router scores when the caller keeps none
   size_t tk_idx;       // int32 [T][K]     token-choice top-K of the router (unused)
   size_t tk_gate;      // fp32 [T][K]
+  size_t sel;          // selection masks and counts (ec_select_bytes)
   size_t tiles;        // int32 [2][N+2]
   size_t act;          // elem [N*C][d_ff]
   size_t act_shared;   // elem [T][n_shared*d_ff_shared]

@@ -110,6 +110,31 @@ def test_ec_route_equal_affinities_take_lowest_tokens():
     assert (ro[C:] == -1).all() and (host(r["gate_of"])[C:] == 0).all()
 
 
+def test_ec_route_ties_at_the_threshold_across_token_chunks():
+    """Affinities that depend on t mod 3 only: each expert's C-th affinity is
+    shared by thousands of tokens on both sides of the 8192-token chunks the
+    selection walks, and the lowest-index tokens of that tie must be the
+    ones taken, in ascending order.  Checked bit for bit against the
+    oracle's selection from the GPU's affinities."""
+    T, N, K, dm = 20000, 4, 1, 64
+    say(f"ec route threshold ties T={T} N={N}")
+    p = M.problem(T=T, d=dm, N=N, K=K, d_ff=64)
+    C = M.moe_ec_capacity(T, K, N, 0.0)
+    u = torch.zeros(T, dm, dtype=torch.bfloat16)
+    u[:, 0] = (torch.arange(T) % 3).to(torch.bfloat16)
+    wr = torch.zeros(N, dm)
+    wr[:, 0] = 0.5 * torch.arange(N, dtype=torch.float32)
+    r = M.moe_ec_route(p, u.to(DEV), wr.to(DEV))
+    probs = host(r["probs"]).T.astype(np.float64)
+    sel = O.ec_select(O.Problem(T=T, d=dm, N=N, K=K, d_ff=64, dtype=O.BF16), probs, C)
+    assert np.array_equal(host(r["expert_tokens"]), sel["expert_tokens"])
+    assert np.array_equal(host(r["row_of"]), sel["row_of"])
+    assert np.array_equal(host(r["expert_gates"]).astype(np.float64), sel["expert_gates"])
+    # expert N-1 prefers t = 2 mod 3 (6667 tokens, more than C = 5000): its
+    # rows are the first C of them
+    assert (host(r["expert_tokens"]).reshape(N, C)[N - 1] == 2 + 3 * np.arange(C)).all()
+
+
 def test_ec_route_without_scores_matches():
     w = W.WORKLOADS["switch_top1"]
     xg = gpu(W.generate(w, only=W.ROUTER))
