@@ -95,6 +95,22 @@ def test_route_edge_shapes(T, N, K, gating):
     _route_checks(w, M.problem_of(w), x, r)
 
 
+@pytest.mark.parametrize("T,d,N,K,gating", [(4099, 4096, 20, 3, "topk_softmax"),
+                                            (8200, 2048, 5, 2, "softmax_topk"),
+                                            (4096, 4096, 32, 4, "topk_softmax")])
+def test_route_large_narrow_batches(T, d, N, K, gating):
+    """Narrow routers (at most 32 experts, register-direct fp32 kernel) over
+    large bf16 batches: ragged token tails, expert counts that pad to 16 or
+    32, noise and bias, both gating variants."""
+    w = W.Workload("bignarrow", T=T, d=d, N=N, K=K, d_ff=64, gating=gating, seed=T + N,
+                   noise=True, noise_weight=0.5, bias="zipf")
+    say(f"route large narrow T={T} d={d} N={N} K={K} {gating}")
+    x = W.generate(w, only=W.ROUTER)
+    xg = gpu(x)
+    r = M.moe_route(M.problem_of(w), xg["u"], xg["w_router"], xg["b_router"], xg["noise"])
+    _route_checks(w, M.problem_of(w), x, r)
+
+
 def test_route_ties_and_noise_off():
     """Equal scores pick the lowest indices; W_noise = 0 reproduces the
     noiseless scores bit for bit."""
