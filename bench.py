@@ -425,39 +425,63 @@ def main():
               "note": "moe_ec_layer_forward on the same batch and weights, HIP-event time per pass"}
         del ecb, ecws
 
-    # ---- backward pass on the same batch (gradients of every parameter)
+    # ---- backward pass on the same batch (gradients of every parameter).
+    # Training runs the forward that also keeps GEMM-1's fp32 pre-activations,
+    # and the backward takes them instead of recomputing GEMM-1 (the same
+    # gradients bit for bit); the recomputing backward is timed beside it.
     bwd = None
     if not args.no_backward and w.dtype == "bf16":
         g = torch.Generator().manual_seed(w.seed + 1)
         d_out = torch.randn(w.T, w.d, generator=g).to(torch.bfloat16).to(dev)
         bb = M.BwdBuffers(p, dev, intermediates=False)
         bws = M.backward_workspace(p, dev)
-        saved = M.saved_of(bufs.t)
-        bwd_args = (P, vp(xg["u"]), ctypes.byref(weights), ctypes.byref(saved), vp(d_out),
-                    ctypes.byref(bb.c), vp(bws), bws.numel(), sp)
         if bufs.t["scores"] is None and w.gating == "softmax_topk":
             raise RuntimeError("the backward of softmax-over-all gating needs the scores")
-        for _ in range(2):
-            L.moe_layer_backward(*bwd_args)
+        kb = M.LayerBuffers(p, dev, want_scores=bufs.t["scores"] is not None, keep_pre=True)
+        fwd_keep_args = (P, vp(xg["u"]), vp(xg["noise"]), ctypes.byref(weights), ctypes.byref(kb.c),
+                         vp(kb.t["out"]), vp(ws), ws.numel(), sp)
         n = max(args.steps, 10)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            st = L.moe_layer_backward(*bwd_args)
-            if st != 0:
-                raise RuntimeError(f"moe_layer_backward: {M.moe_status_string(st)}")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bwd_ms = e0.elapsed_time(e1) / n
+
+        def timed(fn, a):
+            for _ in range(2):
+                fn(*a)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                st = fn(*a)
+                if st != 0:
+                    raise RuntimeError(f"{fn.__name__}: {M.moe_status_string(st)}")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        fwd_keep_ms = timed(L.moe_layer_forward, fwd_keep_args)
+        saved_keep = M.saved_of(kb.t)
+        saved_plain = M.saved_of(bufs.t)
+        bwd_args = lambda sv: (P, vp(xg["u"]), ctypes.byref(weights), ctypes.byref(sv), vp(d_out),
+                               ctypes.byref(bb.c), vp(bws), bws.numel(), sp)
+        bwd_ms = timed(L.moe_layer_backward, bwd_args(saved_keep))
+        bwd_re_ms = timed(L.moe_layer_backward, bwd_args(saved_plain))
         gu = 2 if w.act == "swiglu" else 1
-        # dA, recomputed GEMM-1, dX, dW_down, dW_gate/up: 2*R*d*d_ff*(1 + gu + gu + 1 + gu)
-        bflops = 2.0 * R * w.d * w.d_ff * (2 + 3 * gu)
-        bflops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * (2 + 3 * gu)
-        log(f"backward: {bwd_ms:.3f} ms per pass, {bflops / (bwd_ms * 1e-3) / 1e12:.1f} TFLOP/s in its GEMMs")
+        # dA, dX, dW_down, dW_gate/up: 2*R*d*d_ff*(1 + gu + 1 + gu); the
+        # recomputing backward also runs GEMM-1 again (gu more)
+        bflops = 2.0 * R * w.d * w.d_ff * (2 + 2 * gu)
+        bflops += 2.0 * w.T * w.d * (w.n_shared * w.d_ff_shared) * (2 + 2 * gu)
+        reflops = bflops + 2.0 * (R * w.d * w.d_ff + w.T * w.d * w.n_shared * w.d_ff_shared) * gu
+        log(f"training forward (keeps pre-activations): {fwd_keep_ms:.3f} ms; backward from them: "
+            f"{bwd_ms:.3f} ms ({bflops / (bwd_ms * 1e-3) / 1e12:.1f} TFLOP/s in its GEMMs); "
+            f"recomputing backward: {bwd_re_ms:.3f} ms")
         bwd = {"ms_per_step": round(bwd_ms, 4), "tokens_per_s": round(w.T / (bwd_ms * 1e-3), 1),
                "gemm_flops": bflops, "gemm_tflops_over_pass": round(bflops / (bwd_ms * 1e-3) / 1e12, 1),
-               "note": "moe_layer_backward (all gradients) on the same batch, HIP-event time per pass"}
-        del bb, bws
+               "forward_keep_pre_ms": round(fwd_keep_ms, 4),
+               "training_step_ms": round(fwd_keep_ms + bwd_ms, 4),
+               "recompute": {"ms_per_step": round(bwd_re_ms, 4), "gemm_flops": reflops,
+                             "gemm_tflops_over_pass": round(reflops / (bwd_re_ms * 1e-3) / 1e12, 1),
+                             "training_step_ms": round(head["ms_per_step"] + bwd_re_ms, 4)},
+               "note": "moe_layer_backward (all gradients) on the same batch, HIP-event time per pass, "
+                       "from the pre-activations kept by the training forward (forward_keep_pre_ms); "
+                       "'recompute' runs GEMM-1 again instead, after the inference forward"}
+        del bb, bws, kb
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20

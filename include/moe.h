@@ -252,6 +252,17 @@ typedef struct moe_layer_outputs {
   void* x_perm;           /* [T*K][d] elem       */
   void* y_perm;           /* [T*K][d] elem       */
   void* y_shared;         /* [T][d] elem or NULL */
+  /* Optional, for training (NULL: not kept; bf16 problems only, else
+   * MOE_ERR_UNSUPPORTED): GEMM-1's fp32 pre-activations, which
+   * moe_layer_backward then takes instead of recomputing GEMM-1.  Row r of
+   * pre holds g = x_perm[r] W_gate^T in columns 0..d_ff-1 and, for SwiGLU,
+   * v = x_perm[r] W_up^T in columns d_ff..2*d_ff-1 (ReLU: g only); rows
+   * >= offsets[N] unspecified.  pre_shared is the same for the shared
+   * experts over every token (width n_shared*d_ff_shared per half), used
+   * iff n_shared > 0.  Keeping them adds their writes to the forward pass;
+   * the forward's other outputs do not change. */
+  float* pre;             /* [T*K][gu*d_ff] fp32 or NULL, gu = 2 (SwiGLU) or 1 */
+  float* pre_shared;      /* [T][gu*n_shared*d_ff_shared] fp32 or NULL */
 } moe_layer_outputs_t;
 
 /* The whole forward pass: moe_route, moe_dispatch, moe_grouped_ffn and
@@ -294,7 +305,10 @@ int moe_layer_forward_noalloc(const moe_problem_t* p, const void* u, const float
  *   d_scores     = the gating variant's Jacobian applied to d_gate
  *                  SOFTMAX_TOPK: dH_i = s_i (delta_i - sum_k g_k dg_k)
  *                  TOPK_SOFTMAX: dH_{e_k} = g_k (dg_k - sum_m g_m dg_m)
- *   dA = dY W_down,  dG = dA v SiLU'(g),  dU = dA SiLU(g)   (g, v recomputed)
+ *   dA = dY W_down,  dG = dA v SiLU'(g),  dU = dA SiLU(g)
+ *                  g, v: the forward's saved fp32 pre-activations when given
+ *                  (moe_saved_t.pre), else recomputed by GEMM-1 with the
+ *                  same kernels, so both ways give bit-identical gradients
  *   dX = W_gate^T dG + W_up^T dU;   dW_down = sum_rows dY a^T,
  *   dW_gate = sum_rows dG x^T,  dW_up = sum_rows dU x^T
  *   dW_router = sum_t dH_t u_t^T,  db = sum_t dH_t
@@ -315,6 +329,8 @@ typedef struct moe_saved {
   const int32_t* offsets;   /* [N+1] */
   const void* x_perm;       /* [T*K][d] elem */
   const void* y_perm;       /* [T*K][d] elem */
+  const float* pre;         /* moe_layer_outputs_t.pre, or NULL: recompute GEMM-1 */
+  const float* pre_shared;  /* moe_layer_outputs_t.pre_shared, or NULL (used iff n_shared > 0) */
 } moe_saved_t;
 
 /* Gradients (device pointers, all written).  Weight gradients have the

@@ -55,6 +55,11 @@ struct GemmArgs {
   // persistent launches: work-queue counters (kQueueInts, zero at launch),
   // or null for one block per tile
   int32_t* queue;
+  // forward SwiGLU / ReLU epilogues: also keep the fp32 pre-activations,
+  // P [rows][ldp] with g at column c and the up projection at Ndim + c; or
+  // null
+  float* P;
+  int ldp;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -224,6 +229,23 @@ __device__ __forceinline__ float sigmoid_fast(float g) {
 }
 
 __device__ __forceinline__ float silu_fast(float g) { return g * sigmoid_fast(g); }
+
+// Backward of the activation at one element, from the pre-activations g
+// (and v) and dA: a = SiLU(g) v, dG = dA v SiLU'(g), dU = dA SiLU(g), with
+// SiLU'(g) = s (1 + g (1 - s)), s = sigmoid(g); ReLU: a = max(g, 0),
+// dG = dA [g > 0].  The recompute GEMM's epilogue and act_bwd_kernel both
+// use these, so the two backward paths round identically.
+struct ActBwd {
+  float a, dg, du;
+};
+__device__ __forceinline__ ActBwd swiglu_bwd_point(float gv, float up, float da) {
+  const float sg = sigmoid_fast(gv);
+  const float sl = gv * sg;
+  return ActBwd{sl * up, da * up * sg * (1.0f + gv * (1.0f - sg)), da * sl};
+}
+__device__ __forceinline__ ActBwd relu_bwd_point(float gv, float da) {
+  return ActBwd{gv > 0.0f ? gv : 0.0f, gv > 0.0f ? da : 0.0f, 0.0f};
+}
 
 // ---------------------------------------------------- k-major operands
 // The backward GEMMs read operands whose reduction index k is the row index
@@ -694,12 +716,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const float gv = acc[i][0][v + q], uv = acc[i][TN / 2][v + q];
-          const float sg = sigmoid_fast(gv);
-          const float sl = gv * sg;
           const float da = __builtin_bit_cast(float, q ? (dp & 0xffff0000u) : (dp << 16));
-          pa[q] = sl * uv;
-          pg[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
-          pu[q] = da * sl;
+          const ActBwd r = swiglu_bwd_point(gv, uv, da);
+          pa[q] = r.a;
+          pg[q] = r.dg;
+          pu[q] = r.du;
         }
         if (!col_ok) continue;
         const int rr = 32 * i + 8 * (v >> 2) + (v & 3);   // uniform part of the row
@@ -724,12 +745,48 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
     const uint32_t lane_row = (uint32_t)(wm * WTM + 4 * (lane >> 5) + (odd ? 1 : 0));
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(C + (size_t)row0 * a.ldc + n0, (uint32_t)((size_t)rows * a.ldc * 2 - (size_t)n0 * 2));
+    // the fp32 pre-activations, when kept: g pairs (and up pairs) as 8-byte
+    // stores through descriptors over the tile's rows, like the output
+    constexpr bool KEEP = EPI == EPI_SWIGLU || EPI == EPI_RELU;
+    const bool keep = KEEP && a.P != nullptr;
+    __amdgpu_buffer_rsrc_t rPg = rC, rPu = rC;
+    if (keep) {
+      const size_t pbytes = (size_t)rows * a.ldp * 4;
+      rPg = make_rsrc(a.P + (size_t)row0 * a.ldp + n0, (uint32_t)(pbytes - (size_t)n0 * 4));
+      if constexpr (GATED)
+        rPu = make_rsrc(a.P + (size_t)row0 * a.ldp + a.Ndim + n0,
+                        (uint32_t)(pbytes - (size_t)(a.Ndim + n0) * 4));
+    }
+    auto pair_swap = [&](float x0, float x1, bool odd_lane) {
+      const float send = odd_lane ? x0 : x1;
+      const float got = __builtin_bit_cast(
+          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+      f32x2 pr;
+      pr[0] = odd_lane ? got : x0;
+      pr[1] = odd_lane ? x1 : got;
+      return pr;
+    };
     if (n0 + pc < a.Ndim) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < OUT_TN; ++j) {
           const uint32_t vC = (lane_row * a.ldc + pc + 32 * j) * 2u;
+          if (keep) {
+            const uint32_t vP = (lane_row * a.ldp + pc + 32 * j) * 4u;
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+              const int rr = 32 * i + 8 * (v >> 2) + (v & 3);
+              const f32x2 pg = pair_swap(acc[i][j][v], acc[i][j][v + 1], odd);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pg), rPg, vP,
+                                                    rr * a.ldp * 4, 0);
+              if constexpr (GATED) {
+                const f32x2 pu = pair_swap(acc[i][j + TN / 2][v], acc[i][j + TN / 2][v + 1], odd);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pu), rPu, vP,
+                                                      rr * a.ldp * 4, 0);
+              }
+            }
+          }
 #pragma unroll
           for (int v = 0; v < 16; v += 2) {
             float x[2];
@@ -773,18 +830,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
             const int r = wm * WTM + i * 32 + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
             const float da = r < rows ? bf16_to_f32(D[(size_t)(row0 + r) * a.ldd + col]) : 0.0f;
             const float gv = acc[i][j][v + q];
-            if constexpr (EPI == EPI_SWIGLU_BWD) {
-              const float up = acc[i][j + TN / 2][v + q];
-              const float sg = sigmoid_fast(gv);
-              const float sl = gv * sg;
-              pa[q] = sl * up;
-              pg[q] = da * up * sg * (1.0f + gv * (1.0f - sg));
-              pu[q] = da * sl;
-            } else {
-              pa[q] = gv > 0.0f ? gv : 0.0f;
-              pg[q] = gv > 0.0f ? da : 0.0f;
-              pu[q] = 0.0f;
-            }
+            const ActBwd rb = EPI == EPI_SWIGLU_BWD ? swiglu_bwd_point(gv, acc[i][j + TN / 2][v + q], da)
+                                                    : relu_bwd_point(gv, da);
+            pa[q] = rb.a;
+            pg[q] = rb.dg;
+            pu[q] = rb.du;
           }
           const uint32_t qa = __builtin_bit_cast(uint32_t, __builtin_convertvector(pa, bf16x2));
           const uint32_t qg = __builtin_bit_cast(uint32_t, __builtin_convertvector(pg, bf16x2));
@@ -826,6 +876,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
           const int r = wm * WTM + i * 32 + 8 * ((v + q) >> 2) + 4 * (lane >> 5) + ((v + q) & 3);
           if (r < rows)
             C[(size_t)(row0 + r) * a.ldc + col] = (uint16_t)(q ? packed >> 16 : packed & 0xffffu);
+          if constexpr (EPI == EPI_SWIGLU || EPI == EPI_RELU) {
+            if (a.P != nullptr && r < rows) {
+              float* prow = a.P + (size_t)(row0 + r) * a.ldp;
+              prow[col] = acc[i][j][v + q];
+              if constexpr (EPI == EPI_SWIGLU) prow[a.Ndim + col] = acc[i][j + TN / 2][v + q];
+            }
+          }
         }
       }
     }
@@ -1623,7 +1680,8 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
                               const void* w_down, const void* u, const void* ws_gate,
                               const void* ws_up, const void* ws_down, void* y_perm,
                               void* y_shared, int32_t* tiles, void* act, void* act_shared,
-                              hipStream_t s) {
+                              hipStream_t s, float* pre, float* pre_shared) {
+  const int gu = p.act == MOE_ACT_SWIGLU ? 2 : 1;
   const bool bf16 = p.dtype == MOE_BF16;
   const int epi1 = p.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
   // fp32 problems: one block per 32 rows; bf16: tiles sized to the mean
@@ -1663,9 +1721,12 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g1.kseg = p.d;
   g1.kseg_stride = 0;
   g1.b_group_stride = (size_t)p.d_ff * p.d;
+  g1.P = bf16 ? pre : nullptr;
+  g1.ldp = gu * p.d_ff;
   if ((e = run_gemm(g1, epi1, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
   GemmArgs g2 = g1;
+  g2.P = nullptr;
   g2.A = act;
   g2.B0 = w_down;
   g2.B1 = nullptr;
@@ -1716,8 +1777,11 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     s1.kseg = p.d;
     s1.kseg_stride = 0;
     s1.b_group_stride = 0;
+    s1.P = bf16 ? pre_shared : nullptr;
+    s1.ldp = gu * ws_w;
     if ((e = run_gemm(s1, epi1, bf16, sbm, mt, s)) != hipSuccess) return e;
     GemmArgs s2 = s1;
+    s2.P = nullptr;
     s2.A = act_shared;
     s2.queue = queues + 3 * kQueueInts;
     s2.B0 = ws_down;
@@ -1736,6 +1800,81 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
 }
 
 // ----------------------------------------------------------- backward
+// The activation backward without GEMM-1, from the forward's fp32
+// pre-activations P [rows][ldp] (g at column c, v at d_ff + c): the same
+// a, dG and dU as the recompute GEMM's epilogue, element for element (same
+// accumulators, same swiglu_bwd_point / relu_bwd_point, same bf16 rounding).
+// Rows [0, *nrows_dev) (or nrows when nrows_dev is null); 8 columns a thread.
+namespace {
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void act_bwd_kernel(const float* P, int ldp, const uint16_t* dA,
+                                                      int ldd, const int32_t* nrows_dev, int nrows,
+                                                      int dff, uint16_t* act, int ldc, uint16_t* dgu,
+                                                      int ldc2) {
+  const long long R = nrows_dev != nullptr ? *nrows_dev : nrows;
+  const int cpr = dff / 8;
+  const long long total = R * cpr;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (long long)gridDim.x * 256) {
+    const long long r = i / cpr;
+    const int c = (int)(i - r * cpr) * 8;
+    const float* pg = P + r * ldp + c;
+    float g[8], v[8], da[8];
+    *reinterpret_cast<float4*>(&g[0]) = *reinterpret_cast<const float4*>(pg);
+    *reinterpret_cast<float4*>(&g[4]) = *reinterpret_cast<const float4*>(pg + 4);
+    if constexpr (SWIGLU) {
+      *reinterpret_cast<float4*>(&v[0]) = *reinterpret_cast<const float4*>(pg + dff);
+      *reinterpret_cast<float4*>(&v[4]) = *reinterpret_cast<const float4*>(pg + dff + 4);
+    }
+    const u32x4 dq = *reinterpret_cast<const u32x4*>(dA + r * ldd + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      da[2 * q] = __uint_as_float(dq[q] << 16);
+      da[2 * q + 1] = __uint_as_float(dq[q] & 0xffff0000u);
+    }
+    uint32_t wa[4], wg[4], wu[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x2 pa, pgr, pu;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 2 * q + h;
+        const ActBwd rb = SWIGLU ? swiglu_bwd_point(g[k], v[k], da[k]) : relu_bwd_point(g[k], da[k]);
+        pa[h] = rb.a;
+        pgr[h] = rb.dg;
+        pu[h] = rb.du;
+      }
+      wa[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pa, bf16x2));
+      wg[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pgr, bf16x2));
+      if constexpr (SWIGLU) wu[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pu, bf16x2));
+    }
+    *reinterpret_cast<u32x4*>(act + r * ldc + c) = u32x4{wa[0], wa[1], wa[2], wa[3]};
+    *reinterpret_cast<u32x4*>(dgu + r * ldc2 + c) = u32x4{wg[0], wg[1], wg[2], wg[3]};
+    if constexpr (SWIGLU)
+      *reinterpret_cast<u32x4*>(dgu + r * ldc2 + dff + c) = u32x4{wu[0], wu[1], wu[2], wu[3]};
+  }
+}
+
+hipError_t run_act_bwd(bool swiglu, const float* P, int ldp, const void* dA, int ldd,
+                       const int32_t* nrows_dev, int nrows_max, int dff, void* act, int ldc,
+                       void* dgu, int ldc2, hipStream_t s) {
+  const long long total = (long long)nrows_max * (dff / 8);
+  if (total == 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  const int nrows = nrows_dev != nullptr ? 0 : nrows_max;
+  if (swiglu)
+    hipLaunchKernelGGL(act_bwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, P, ldp,
+                       static_cast<const uint16_t*>(dA), ldd, nrows_dev, nrows, dff,
+                       static_cast<uint16_t*>(act), ldc, static_cast<uint16_t*>(dgu), ldc2);
+  else
+    hipLaunchKernelGGL(act_bwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, P, ldp,
+                       static_cast<const uint16_t*>(dA), ldd, nrows_dev, nrows, dff,
+                       static_cast<uint16_t*>(act), ldc, static_cast<uint16_t*>(dgu), ldc2);
+  return hipGetLastError();
+}
+}  // namespace
+
 // The expert FFN backward, from the forward's rows and the output
 // gradients dY (see the header of this file for the forward GEMMs):
 //   dA  = dY W_down                      (k-major W_down)
@@ -1859,7 +1998,12 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   r1.ldd = dff;
   r1.C2 = b.dgu;
   r1.ldc2 = swiglu ? 2 * dff : dff;
-  if ((e = run_bwd_epi(r1, swiglu, bm, mtiles_max, s)) != hipSuccess) return e;
+  if (b.pre != nullptr)
+    e = run_act_bwd(swiglu, b.pre, (swiglu ? 2 : 1) * dff, b.dA, dff, b.offsets + p.N, rows_alloc,
+                    dff, b.act, dff, b.dgu, r1.ldc2, s);
+  else
+    e = run_bwd_epi(r1, swiglu, bm, mtiles_max, s);
+  if (e != hipSuccess) return e;
   // dX = [dG dU] [W_gate; W_up]
   GemmArgs n2 = base;
   n2.A = b.dgu;
@@ -1951,7 +2095,12 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   sr.ldd = wsw;
   sr.C2 = b.dgu_s;
   sr.ldc2 = swiglu ? 2 * wsw : wsw;
-  if ((e = run_bwd_epi(sr, swiglu, sbm, mt, s)) != hipSuccess) return e;
+  if (b.pre_shared != nullptr)
+    e = run_act_bwd(swiglu, b.pre_shared, (swiglu ? 2 : 1) * wsw, b.dA_s, wsw, nullptr, p.T, wsw,
+                    b.act_s, wsw, b.dgu_s, sr.ldc2, s);
+  else
+    e = run_bwd_epi(sr, swiglu, sbm, mt, s);
+  if (e != hipSuccess) return e;
   GemmArgs s2 = sb;
   s2.A = b.dgu_s;
   s2.lda = swiglu ? 2 * wsw : wsw;

@@ -375,6 +375,17 @@ int check_layer(const moe_problem_t* p, const void* u, const float* noise,
   MOE_TRY(check_ffn(p, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u, wt->ws_gate,
                     wt->ws_up, wt->ws_down, o->y_perm, o->y_shared));
   MOE_TRY(check_combine(p, u, o->y_perm, o->row_of, o->topk_gate, o->y_shared, out));
+  const bool keep_shared = p->n_shared > 0 && o->pre_shared != nullptr;
+  if (o->pre != nullptr || keep_shared) {
+    if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const long long gu = p->act == MOE_ACT_SWIGLU ? 2 : 1;
+    // the tiles address their fp32 rows through 32-bit buffer sizes
+    long long ldp = gu * p->d_ff;
+    if (gu * p->n_shared * (long long)p->d_ff_shared > ldp) ldp = gu * p->n_shared * (long long)p->d_ff_shared;
+    if (320LL * ldp * 4 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(maybe(o->pre, 16));
+    if (keep_shared) MOE_TRY(need(o->pre_shared, 16));
+  }
   return MOE_OK;
 }
 
@@ -399,7 +410,8 @@ int launch_layer(const moe_problem_t* p, const void* u, const float* noise,
   e = moe::launch_grouped_ffn(*p, p->T * p->K, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u,
                               wt->ws_gate, wt->ws_up, wt->ws_down, o->y_perm, ysh,
                               reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)), ws_at(ws, w.act),
-                              ws_at(ws, w.act_shared), s);
+                              ws_at(ws, w.act_shared), s, o->pre,
+                              p->n_shared > 0 ? o->pre_shared : nullptr);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(*p, u, o->y_perm, o->row_of, o->topk_gate, ysh, out, s);
   return hip_status(e);
@@ -534,6 +546,8 @@ int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_
   MOE_TRY(maybe(g->d_scores, 4));
   MOE_TRY(maybe(g->dy_perm, 16));
   MOE_TRY(maybe(g->dx_perm, 16));
+  MOE_TRY(maybe(sv->pre, 16));
+  if (shared) MOE_TRY(maybe(sv->pre_shared, 16));
   const moe::BwdWorkspace L = moe::bwd_workspace_layout(*p);
   MOE_TRY(check_ws(ws, ws_bytes, L.total));
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -565,6 +579,8 @@ int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_
   b.dw_gate = g->dw_gate;
   b.dw_up = g->dw_up;
   b.dw_down = g->dw_down;
+  b.pre = sv->pre;
+  b.pre_shared = shared ? sv->pre_shared : nullptr;
   if (L.ldt > 0) {
     b.kpad = reinterpret_cast<int32_t*>(ws_at(ws, L.kpad));
     b.dyT = ws_at(ws, L.dyT);

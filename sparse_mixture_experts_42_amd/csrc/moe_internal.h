@@ -14,6 +14,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- bf16
@@ -99,7 +100,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
                               const void* w_down, const void* u, const void* ws_gate,
                               const void* ws_up, const void* ws_down, void* y_perm,
                               void* y_shared, int32_t* tiles, void* act, void* act_shared,
-                              hipStream_t s);
+                              hipStream_t s, float* pre = nullptr, float* pre_shared = nullptr);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* u, const void* y_perm,
                           const int32_t* row_of, const float* topk_gate,
@@ -132,6 +133,9 @@ struct FfnBwdBuffers {
   void* dgu_s;              // [T][2*n_shared*d_ff_shared] workspace
   void* dx_shared;          // [T][d]
   void *dws_gate, *dws_up, *dws_down;
+  // the forward's fp32 pre-activations (null: recomputed by GEMM-1)
+  const float* pre;         // [rows][gu*d_ff]
+  const float* pre_shared;  // [T][gu*n_shared*d_ff_shared]
 };
 hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc,
                                        const FfnBwdBuffers& b, hipStream_t s);

@@ -46,7 +46,7 @@ class MoeLayerOutputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("scores", "topk_idx", "topk_gate", "mean_prob", "lse_sq", "expert_counts",
                  "kept_counts", "offsets", "row_of", "token_of_row", "x_perm", "y_perm",
-                 "y_shared")]
+                 "y_shared", "pre", "pre_shared")]
 
 
 class MoeEcOutputs(ctypes.Structure):
@@ -57,7 +57,8 @@ class MoeEcOutputs(ctypes.Structure):
 
 class MoeSaved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("scores", "topk_idx", "topk_gate", "row_of", "offsets", "x_perm", "y_perm")]
+                ("scores", "topk_idx", "topk_gate", "row_of", "offsets", "x_perm", "y_perm",
+                 "pre", "pre_shared")]
 
 
 class MoeGrads(ctypes.Structure):
@@ -314,10 +315,14 @@ def moe_combine(p: MoeProblem, u, y_perm, row_of, topk_gate, y_shared=None) -> t
 class LayerBuffers:
     """Preallocated outputs and intermediates of moe_layer_forward."""
 
-    def __init__(self, p: MoeProblem, device, want_scores=True):
+    def __init__(self, p: MoeProblem, device, want_scores=True, keep_pre=False):
         et = TORCH_DTYPE[p.dtype]
         e = lambda shape, dt: _empty(shape, dt, device)
+        gu = 2 if p.act == MOE_ACT_SWIGLU else 1
         self.t = dict(
+            pre=e((p.T * p.K, gu * p.d_ff), torch.float32) if keep_pre else None,
+            pre_shared=(e((p.T, gu * p.n_shared * p.d_ff_shared), torch.float32)
+                        if keep_pre and p.n_shared > 0 else None),
             scores=e((p.T, p.N), torch.float32) if want_scores else None,
             topk_idx=e((p.T, p.K), torch.int32), topk_gate=e((p.T, p.K), torch.float32),
             mean_prob=e((p.N,), torch.float32), lse_sq=e((p.T,), torch.float32),
@@ -374,12 +379,15 @@ def moe_layer_forward_noalloc(p: MoeProblem, u, noise, weights: MoeWeights,
     return bufs.t["out"]
 
 
-def layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], want_scores=True) -> Dict[str, torch.Tensor]:
+def layer_forward(p: MoeProblem, u, x: Dict[str, Optional[torch.Tensor]], want_scores=True,
+                  keep_pre=False) -> Dict[str, torch.Tensor]:
     """Convenience: allocate buffers and run the whole pass on workload tensors
-    x (keys as produced by workloads.generate, already on the GPU)."""
+    x (keys as produced by workloads.generate, already on the GPU).  keep_pre:
+    also keep GEMM-1's fp32 pre-activations ('pre', 'pre_shared') for the
+    backward pass."""
     w = make_weights(p, x["w_router"], x.get("b_router"), x["w_gate"], x.get("w_up"), x["w_down"],
                      x.get("ws_gate"), x.get("ws_up"), x.get("ws_down"))
-    bufs = LayerBuffers(p, u.device, want_scores)
+    bufs = LayerBuffers(p, u.device, want_scores, keep_pre)
     moe_layer_forward(p, u, x.get("noise"), w, bufs)
     return bufs.t
 

@@ -184,6 +184,40 @@ def test_other_entry_points_check_before_launch():
     assert L.moe_layer_forward(P, f(1), None, ctypes.byref(w), ctypes.byref(o), f(2), f(3), 1 << 40, None) == M.MOE_ERR_INVALID_ARG
 
 
+def test_kept_pre_activations_argument_checks():
+    """The forward's optional fp32 pre-activation outputs: 16-byte aligned,
+    bf16 problems only; the backward's saved copies likewise aligned.  All
+    refused before any HIP call."""
+    L = M.lib()
+    w = M.MoeWeights(*[FAKE + 4096 * i for i in range(8)])
+    fields = [n for n, _ in M.MoeLayerOutputs._fields_]
+    o = M.MoeLayerOutputs(*[FAKE + 4096 * (20 + i) for i in range(len(fields))])
+    f = lambda i: ctypes.c_void_p(FAKE + 256 * i)
+    fwd = lambda p, oo: L.moe_layer_forward(ctypes.byref(p), f(1), None, ctypes.byref(w),
+                                            ctypes.byref(oo), f(2), f(3), 100, None)
+    # with valid pointers the call gets as far as the (short) workspace
+    assert fwd(good(), o) == M.MOE_ERR_WORKSPACE
+    assert fwd(good(dtype="f32"), o) == M.MOE_ERR_UNSUPPORTED
+    o.pre = FAKE + 8
+    assert fwd(good(), o) == M.MOE_ERR_INVALID_ARG
+    o.pre = None
+    assert fwd(good(dtype="f32"), o) == M.MOE_ERR_WORKSPACE      # pre_shared unused without shared experts
+    sh = good(n_shared=1, d_ff_shared=128)
+    o.pre_shared = FAKE + 8
+    assert fwd(sh, o) == M.MOE_ERR_INVALID_ARG
+    o.pre_shared = FAKE + 4096 * 60
+    assert fwd(sh, o) == M.MOE_ERR_WORKSPACE
+    # backward: a misaligned saved copy is refused
+    sv = M.MoeSaved(*[FAKE + 4096 * (20 + i) for i in range(len(M.MoeSaved._fields_))])
+    g = M.MoeGrads(*[FAKE + 4096 * (40 + i) for i in range(len(M.MoeGrads._fields_))])
+    bwd = lambda p, ss, wsb: L.moe_layer_backward(ctypes.byref(p), f(1), ctypes.byref(w), ctypes.byref(ss),
+                                                  f(2), ctypes.byref(g), f(3), wsb, None)
+    p = good()
+    assert bwd(p, sv, 100) == M.MOE_ERR_WORKSPACE
+    sv.pre = FAKE + 8
+    assert bwd(p, sv, 1 << 40) == M.MOE_ERR_INVALID_ARG
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     p = good(T=4)

@@ -316,3 +316,80 @@ def test_backward_integer_data_is_exact(T, shared, cold):
         ref = O.ffn_weight_grads(po, xi, -1, u, dO, np.arange(64, dtype=np.int32))
         assert np.array_equal(host(t["dws_gate"][0]), ref["dw_gate"])
         assert np.array_equal(host(t["dws_down"][0]).T, ref["dw_down"])
+
+
+@pytest.mark.parametrize("T,N,K,act,shared", [
+    (300, 6, 2, "swiglu", 0),       # 128-row tiles
+    (200, 8, 3, "swiglu", 2),       # shared experts (one group over every token)
+    (129, 16, 4, "relu", 1),        # 32-row tiles, ReLU
+    (1300, 2, 2, "swiglu", 0),      # 256-row tiles, each group's last tile extended
+    (4200, 4, 1, "relu", 0)])       # 256-row tiles, ragged groups
+def test_backward_from_kept_pre_activations(T, N, K, act, shared):
+    """A forward that keeps GEMM-1's fp32 pre-activations changes none of its
+    other outputs, and a backward that takes them instead of recomputing
+    GEMM-1 gives the same gradients bit for bit: the kept values are the
+    recompute GEMM's own accumulators, and both paths share the activation
+    backward's arithmetic.  The kept g (and v) are checked against the
+    oracle's products x_perm W^T (shared experts: u Ws^T) on sampled rows,
+    to the fp32 accumulation bound."""
+    dffs = 64 if shared else 0
+    w = W.Workload("keep", T=T, d=256, N=N, K=K, d_ff=192, gating="topk_softmax", act=act,
+                   n_shared=shared, d_ff_shared=dffs, seed=T + N)
+    say(f"kept pre-activations T={T} N={N} K={K} {act} shared={shared} "
+        f"(row tile {M.moe_ffn_row_tile(T * K, N)})")
+    x = W.generate(w)
+    xg = gpu(x)
+    p = M.problem_of(w)
+    a = M.layer_forward(p, xg["u"], xg)
+    b = M.layer_forward(p, xg["u"], xg, keep_pre=True)
+    torch.cuda.synchronize()
+    R = int(a["offsets"][-1])
+    for k, v in a.items():
+        if v is None or k in ("pre", "pre_shared"):
+            continue
+        vb = b[k]
+        if k in ("x_perm", "y_perm"):
+            assert torch.equal(v[:R], vb[:R]), k
+        else:
+            assert torch.equal(v, vb), k
+    # kept values against the oracle's products on sampled rows
+    gu = 2 if act == "swiglu" else 1
+    pre = host(b["pre"])
+    assert pre.shape == (T * K, gu * w.d_ff)
+    xp = host(b["x_perm"]).astype(np.float64)
+    off = host(b["offsets"])
+    f64 = lambda t: t.to(torch.float64).numpy()
+    mats = [f64(x["w_gate"])] + ([f64(x["w_up"])] if gu == 2 else [])
+    rng = np.random.default_rng(T)
+    for r in np.unique(np.concatenate([off[:-1], np.maximum(off[1:] - 1, 0), rng.integers(0, max(R, 1), 24)])):
+        if r >= R:
+            continue
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        for h, Wm in enumerate(mats):
+            ref = Wm[e] @ xp[r]
+            bound = 2e-5 * (np.abs(Wm[e]) @ np.abs(xp[r])) + 1e-30
+            got = pre[r, h * w.d_ff:(h + 1) * w.d_ff]
+            assert (np.abs(got - ref) <= bound).all(), f"pre row {r} part {h}"
+    if shared:
+        ps = host(b["pre_shared"])
+        uu = f64(x["u"])
+        smats = [f64(x["ws_gate"]).reshape(-1, w.d)] + \
+            ([f64(x["ws_up"]).reshape(-1, w.d)] if gu == 2 else [])
+        wsw = shared * dffs
+        for t in (0, T // 2, T - 1):
+            for h, Wm in enumerate(smats):
+                ref = Wm @ uu[t]
+                bound = 2e-5 * (np.abs(Wm) @ np.abs(uu[t])) + 1e-30
+                assert (np.abs(ps[t, h * wsw:(h + 1) * wsw] - ref) <= bound).all(), f"pre_shared {t}"
+    # the backward from the kept values equals the recomputing one
+    d_out = _d_out(w, 7).to(DEV)
+    ga = {k: (None if v is None else v.clone()) for k, v in M.layer_backward(p, xg, a, d_out).items()}
+    gb = M.layer_backward(p, xg, b, d_out)
+    torch.cuda.synchronize()
+    for k, v in ga.items():
+        if v is None:
+            continue
+        if k in ("dy_perm", "dx_perm"):
+            assert torch.equal(v[:R], gb[k][:R]), k
+        else:
+            assert torch.equal(v, gb[k]), k
