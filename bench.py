@@ -101,10 +101,11 @@ CPU_SAMPLE = dict(tiny_fp32=256, switch_top1=4096, mixtral=1024, deepseekmoe=204
 
 
 def host_threads():
-    """Threads the oracle uses: the host cores this process may run on, at
-    most 16 (the host share of one GPU on the GPU machines)."""
-    from oracle import oracle as O
-    return O.nthreads_default()
+    """Threads the oracle uses: every host core this process may run on."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
 
 
 def measure_forward(w, args, dev, stream, headline):

@@ -87,6 +87,21 @@ __host__ __device__ inline void split_rows(int n, int BM, int tail_rows, int ext
   else full = q + 1;
 }
 
+// The tile plan -- group row offsets and the prefixes of full and tail
+// tiles -- seen through an accessor, so that the lookups below serve the
+// plan in memory (PtrPlan) and a plan held in registers alike.
+struct PtrPlan {
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const int32_t* tails;
+  __host__ __device__ int offset(int i) const { return offsets[i]; }
+  __host__ __device__ int tile(int i) const { return tiles[i]; }
+  __host__ __device__ int tail(int i) const { return tails[i]; }
+};
+__host__ __device__ inline PtrPlan ptr_plan(const GemmArgs& a) {
+  return PtrPlan{a.offsets, a.tiles, a.tails};
+}
+
 // Locate the row block: returns false when the block has no work.
 __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int& g, int& row0,
                                           int& rows) {
@@ -115,11 +130,15 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int
 constexpr int kPatchN = 4;   // n-tiles per patch: an XCD works on m-tiles x 4 n-tiles of one group
 
 // Full-height tiles of all groups (single-group form: from M).
-__host__ __device__ inline int full_tiles_total(const GemmArgs& a, int BM) {
-  if (a.offsets != nullptr) return a.tiles[a.G];
+template <typename P>
+__host__ __device__ inline int full_tiles_total_p(const GemmArgs& a, const P& pl, int BM) {
+  if (a.offsets != nullptr) return pl.tile(a.G);
   int f, t;
   split_rows(a.M, BM, a.tail_rows, a.ext_rows, f, t);
   return f;
+}
+__host__ __device__ inline int full_tiles_total(const GemmArgs& a, int BM) {
+  return full_tiles_total_p(a, ptr_plan(a), BM);
 }
 
 // 1-D grid: blocks [0, full tiles x n-tiles) are the full-height tiles, the
@@ -134,8 +153,10 @@ __host__ __device__ inline int full_tiles_total(const GemmArgs& a, int BM) {
 // a given position of successive patches tends to land on the same CU (the
 // CUs finish their tiles in the same order), and without the rotation the
 // same few CUs would draw every group's taller last tile.
-__host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntiles, int h, int real,
-                                             int& g, int& row0, int& rows, int& nt) {
+template <typename P>
+__host__ __device__ inline void find_tile_2d_p(const GemmArgs& a, const P& pl, int BM, int ntiles,
+                                               int h, int real, int& g, int& row0, int& rows,
+                                               int& nt) {
   int mt_g, base;
   const int full = real - real % 8;
   const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
@@ -147,12 +168,12 @@ __host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntil
     int lo = 0, hi = a.G;          // tiles[lo]*ntiles <= L < tiles[hi]*ntiles
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.tiles[mid] * ntiles <= L) lo = mid;
+      if (pl.tile(mid) * ntiles <= L) lo = mid;
       else hi = mid;
     }
     g = lo;
-    mt_g = a.tiles[g + 1] - a.tiles[g];
-    base = a.tiles[g] * ntiles;
+    mt_g = pl.tile(g + 1) - pl.tile(g);
+    base = pl.tile(g) * ntiles;
   }
   const int l = L - base;
   const int nb = l / (mt_g * kPatchN);
@@ -160,16 +181,21 @@ __host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntil
   const int nbe = ntiles - nb * kPatchN < kPatchN ? ntiles - nb * kPatchN : kPatchN;
   const int mt = (rem / nbe + nb) % mt_g;
   nt = nb * kPatchN + rem % nbe;
-  row0 = (a.offsets == nullptr ? 0 : a.offsets[g]) + mt * BM;
-  const int end = a.offsets == nullptr ? a.M : a.offsets[g + 1];
+  row0 = (a.offsets == nullptr ? 0 : pl.offset(g)) + mt * BM;
+  const int end = a.offsets == nullptr ? a.M : pl.offset(g + 1);
   rows = end - row0;
   if (mt < mt_g - 1 && rows > BM) rows = BM;
+}
+__host__ __device__ inline void find_tile_2d(const GemmArgs& a, int BM, int ntiles, int h, int real,
+                                             int& g, int& row0, int& rows, int& nt) {
+  find_tile_2d_p(a, ptr_plan(a), BM, ntiles, h, real, g, row0, rows, nt);
 }
 
 // Tail tile h (counted from the first tail block): n-tile fastest.  Returns
 // false past the last tail tile.
-__host__ __device__ inline bool find_tail(const GemmArgs& a, int BM, int ntiles, int h, int& g,
-                                          int& row0, int& rows, int& nt) {
+template <typename P>
+__host__ __device__ inline bool find_tail_p(const GemmArgs& a, const P& pl, int BM, int ntiles, int h,
+                                            int& g, int& row0, int& rows, int& nt) {
   if (a.tail_rows == 0) return false;
   const int ti = h / ntiles;
   nt = h - ti * ntiles;
@@ -182,19 +208,23 @@ __host__ __device__ inline bool find_tail(const GemmArgs& a, int BM, int ntiles,
     row0 = full * BM;
     end = a.M;
   } else {
-    if (ti >= a.tails[a.G]) return false;
+    if (ti >= pl.tail(a.G)) return false;
     int lo = 0, hi = a.G;          // tails[lo] <= ti < tails[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.tails[mid] <= ti) lo = mid;
+      if (pl.tail(mid) <= ti) lo = mid;
       else hi = mid;
     }
     g = lo;
-    row0 = a.offsets[g] + (a.tiles[g + 1] - a.tiles[g]) * BM;
-    end = a.offsets[g + 1];
+    row0 = pl.offset(g) + (pl.tile(g + 1) - pl.tile(g)) * BM;
+    end = pl.offset(g + 1);
   }
   rows = end - row0;
   return rows > 0;
+}
+__host__ __device__ inline bool find_tail(const GemmArgs& a, int BM, int ntiles, int h, int& g,
+                                          int& row0, int& rows, int& nt) {
+  return find_tail_p(a, ptr_plan(a), BM, ntiles, h, g, row0, rows, nt);
 }
 
 // ------------------------------------------------------------ bf16 MFMA
@@ -305,6 +335,93 @@ struct NoPre {
 };
 template <typename P> struct IsNoPre { static constexpr bool value = false; };
 template <> struct IsNoPre<NoPre> { static constexpr bool value = true; };
+
+// Forward epilogue of the 256-column tiles (8 waves of 2 x 4): lane holds
+// column lane%32 of rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32
+// accumulator.  Neighbouring lanes (columns c and c+1) swap one value of
+// each row pair, so that the even lane holds row r and the odd lane row
+// r+1, both at columns (c, c+1); each lane then stores one bf16 pair (4
+// bytes) through a buffer descriptor over the tile's rows, so stores to
+// rows past the group fall outside it and are dropped without a branch.
+template <int EPI, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_forward_tile(const GemmArgs& a, f32x16 (&acc)[TM][TN], int row0,
+                                                   int rows, int n0, int wm, int wn, int lane) {
+  constexpr bool GATED = gated<EPI>();
+  constexpr int OUT_TN = GATED ? TN / 2 : TN;
+  uint16_t* C = static_cast<uint16_t*>(a.C);
+  const bool odd = (lane & 1) != 0;
+  const int pc = (GATED ? wn * (WTN / 2) : wn * WTN) + (lane & 31) - (odd ? 1 : 0);
+  const uint32_t lane_row = (uint32_t)(wm * WTM + 4 * (lane >> 5) + (odd ? 1 : 0));
+  const __amdgpu_buffer_rsrc_t rC =
+      make_rsrc(C + (size_t)row0 * a.ldc + n0, (uint32_t)((size_t)rows * a.ldc * 2 - (size_t)n0 * 2));
+  // the fp32 pre-activations, when kept: g pairs (and up pairs) as 8-byte
+  // stores through descriptors over the tile's rows, like the output
+  constexpr bool KEEP = EPI == EPI_SWIGLU || EPI == EPI_RELU;
+  const bool keep = KEEP && a.P != nullptr;
+  __amdgpu_buffer_rsrc_t rPg = rC, rPu = rC;
+  if (keep) {
+    const size_t pbytes = (size_t)rows * a.ldp * 4;
+    rPg = make_rsrc(a.P + (size_t)row0 * a.ldp + n0, (uint32_t)(pbytes - (size_t)n0 * 4));
+    if constexpr (GATED)
+      rPu = make_rsrc(a.P + (size_t)row0 * a.ldp + a.Ndim + n0,
+                      (uint32_t)(pbytes - (size_t)(a.Ndim + n0) * 4));
+  }
+  auto pair_swap = [&](float x0, float x1, bool odd_lane) {
+    const float send = odd_lane ? x0 : x1;
+    const float got = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+    f32x2 pr;
+    pr[0] = odd_lane ? got : x0;
+    pr[1] = odd_lane ? x1 : got;
+    return pr;
+  };
+  // Ndim is a multiple of 64: a 32-column block is valid or not as a whole
+  {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < OUT_TN; ++j) {
+        if (n0 + pc + 32 * j >= a.Ndim) continue;
+        const uint32_t vC = (lane_row * a.ldc + pc + 32 * j) * 2u;
+        if (keep) {
+          const uint32_t vP = (lane_row * a.ldp + pc + 32 * j) * 4u;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const int rr = 32 * i + 8 * (v >> 2) + (v & 3);
+            const f32x2 pg = pair_swap(acc[i][j][v], acc[i][j][v + 1], odd);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pg), rPg, vP,
+                                                  rr * a.ldp * 4, 0);
+            if constexpr (GATED) {
+              const f32x2 pu = pair_swap(acc[i][j + TN / 2][v], acc[i][j + TN / 2][v + 1], odd);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pu), rPu, vP,
+                                                    rr * a.ldp * 4, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          float x[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float g = acc[i][j][v + q];
+            if constexpr (EPI == EPI_SWIGLU) x[q] = silu_fast(g) * acc[i][j + TN / 2][v + q];
+            else if constexpr (EPI == EPI_RELU) x[q] = g > 0.0f ? g : 0.0f;
+            else x[q] = g;
+          }
+          // quad_perm [1,0,3,2]: each lane receives its neighbour's value
+          const float send = odd ? x[0] : x[1];
+          const float got = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+          f32x2 pr;
+          pr[0] = odd ? got : x[0];
+          pr[1] = odd ? x[1] : got;
+          const int rr = 32 * i + 8 * (v >> 2) + (v & 3);   // uniform part of the row
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)),
+                                                rC, vC, rr * a.ldc * 2, 0);
+        }
+      }
+  }
+}
 
 // PIPE tiles may continue a persistent block's previous tile: stage 0 uses
 // LDS buffer b0 (stage k buffer (k + b0) & 1), `issued` says its loads are
@@ -734,82 +851,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
     return;
   }
   if constexpr (PIPE && (EPI == EPI_NONE || EPI == EPI_SWIGLU || EPI == EPI_RELU)) {
-    // Forward epilogue of the pipelined tiles.  Neighbouring lanes (columns
-    // c and c+1) swap one value of each row pair, so that the even lane
-    // holds row r and the odd lane row r+1, both at columns (c, c+1); each
-    // lane then stores one bf16 pair (4 bytes) through a buffer descriptor
-    // over the tile's rows, so stores to rows past the group fall outside
-    // it and are dropped without a branch.
-    const bool odd = (lane & 1) != 0;
-    const int pc = (GATED ? wn * (WTN / 2) : wn * WTN) + (lane & 31) - (odd ? 1 : 0);
-    const uint32_t lane_row = (uint32_t)(wm * WTM + 4 * (lane >> 5) + (odd ? 1 : 0));
-    const __amdgpu_buffer_rsrc_t rC =
-        make_rsrc(C + (size_t)row0 * a.ldc + n0, (uint32_t)((size_t)rows * a.ldc * 2 - (size_t)n0 * 2));
-    // the fp32 pre-activations, when kept: g pairs (and up pairs) as 8-byte
-    // stores through descriptors over the tile's rows, like the output
-    constexpr bool KEEP = EPI == EPI_SWIGLU || EPI == EPI_RELU;
-    const bool keep = KEEP && a.P != nullptr;
-    __amdgpu_buffer_rsrc_t rPg = rC, rPu = rC;
-    if (keep) {
-      const size_t pbytes = (size_t)rows * a.ldp * 4;
-      rPg = make_rsrc(a.P + (size_t)row0 * a.ldp + n0, (uint32_t)(pbytes - (size_t)n0 * 4));
-      if constexpr (GATED)
-        rPu = make_rsrc(a.P + (size_t)row0 * a.ldp + a.Ndim + n0,
-                        (uint32_t)(pbytes - (size_t)(a.Ndim + n0) * 4));
-    }
-    auto pair_swap = [&](float x0, float x1, bool odd_lane) {
-      const float send = odd_lane ? x0 : x1;
-      const float got = __builtin_bit_cast(
-          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-      f32x2 pr;
-      pr[0] = odd_lane ? got : x0;
-      pr[1] = odd_lane ? x1 : got;
-      return pr;
-    };
-    if (n0 + pc < a.Ndim) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < OUT_TN; ++j) {
-          const uint32_t vC = (lane_row * a.ldc + pc + 32 * j) * 2u;
-          if (keep) {
-            const uint32_t vP = (lane_row * a.ldp + pc + 32 * j) * 4u;
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-              const int rr = 32 * i + 8 * (v >> 2) + (v & 3);
-              const f32x2 pg = pair_swap(acc[i][j][v], acc[i][j][v + 1], odd);
-              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pg), rPg, vP,
-                                                    rr * a.ldp * 4, 0);
-              if constexpr (GATED) {
-                const f32x2 pu = pair_swap(acc[i][j + TN / 2][v], acc[i][j + TN / 2][v + 1], odd);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pu), rPu, vP,
-                                                      rr * a.ldp * 4, 0);
-              }
-            }
-          }
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            float x[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const float g = acc[i][j][v + q];
-              if constexpr (EPI == EPI_SWIGLU) x[q] = silu_fast(g) * acc[i][j + TN / 2][v + q];
-              else if constexpr (EPI == EPI_RELU) x[q] = g > 0.0f ? g : 0.0f;
-              else x[q] = g;
-            }
-            // quad_perm [1,0,3,2]: each lane receives its neighbour's value
-            const float send = odd ? x[0] : x[1];
-            const float got = __builtin_bit_cast(
-                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-            f32x2 pr;
-            pr[0] = odd ? got : x[0];
-            pr[1] = odd ? x[1] : got;
-            const int rr = 32 * i + 8 * (v >> 2) + (v & 3);   // uniform part of the row
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)),
-                                                  rC, vC, rr * a.ldc * 2, 0);
-          }
-        }
-    }
+    store_forward_tile<EPI, TM, TN, WTM, WTN>(a, acc, row0, rows, n0, wm, wn, lane);
     return;
   }
   if constexpr (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) {
@@ -914,59 +956,6 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-// Stage 0 of a 256-column tile (rows <= 320, 8 waves, row-major B) into LDS
-// buffer buf: the same loads, lane mapping and LDS slots as the first stage
-// the tile body issues itself, for a tile of BMk = 320, 256 or 64 rows.
-template <int EPI, int SAN, int SBN>
-__device__ __forceinline__ void issue_stage0(const GemmArgs& a, int g, int row0, int rows, int by,
-                                             int BMk, int buf, u32x4 (&sA)[2][SAN], u32x4 (&sB)[2][SBN]) {
-  constexpr int NW = 8, BN = 256, BI = BN / 8 / NW;
-  constexpr bool GATED = gated<EPI>();
-  constexpr int BNH = GATED ? BN / 2 : BN;
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  g = __builtin_amdgcn_readfirstlane(g);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  rows = __builtin_amdgcn_readfirstlane(rows);
-  by = __builtin_amdgcn_readfirstlane(by);
-  BMk = __builtin_amdgcn_readfirstlane(BMk);
-  const int AI = BMk / 8 / NW;
-  const int n0 = by * BNH;
-  const int lrow = lane >> 3;
-  const int lchunk_even = (lane & 7) ^ (lrow >> 1);
-  const int lchunk_odd = (lane & 7) ^ (4 + (lrow >> 1));
-  const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda, (uint32_t)rows * a.lda * 2);
-  lds_t* ldsA = (lds_t*)&sA[buf][wave * AI * 64];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    if (i >= AI) break;
-    const bool odd = ((wave * AI + i) & 1) != 0;
-    const uint32_t voff = (uint32_t)(((wave * AI + i) * 8 + lrow) * a.lda + (odd ? lchunk_odd : lchunk_even) * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t*)((char*)ldsA + i * 1024), 16, voff, 0, 0, 0);
-  }
-  const uint16_t* Bsrc = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
-  int b_local0 = wave * (BN / NW);
-  if constexpr (GATED) {
-    if (wave >= NW / 2) {
-      Bsrc = static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride;
-      b_local0 -= BN / 2;
-    }
-  }
-  Bsrc += (size_t)n0 * a.ldb;
-  const int b_valid = a.Ndim - n0 < BNH ? a.Ndim - n0 : BNH;
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bsrc, (uint32_t)b_valid * a.ldb * 2);
-  lds_t* ldsB = (lds_t*)&sB[buf][wave * BI * 64];
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const bool odd = ((wave * BI + i) & 1) != 0;
-    const uint32_t voff = (uint32_t)((b_local0 + i * 8 + lrow) * a.ldb + (odd ? lchunk_odd : lchunk_even) * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t*)((char*)ldsB + i * 1024), 16, voff, 0, 0, 0);
-  }
-}
-
 // Persistent launches split the 1-D tile space [0, total) into 9 queues:
 // queue y < 8 holds the y-th run of q = full/8 tiles of the patch order
 // (full = full tiles rounded down to a multiple of 8), queue 8 the rest.
@@ -978,77 +967,374 @@ __host__ __device__ inline int queue_slot(int y, int t, int q, int full, int res
 }
 
 // Tail tiles of all groups (single-group form: from M).
-__host__ __device__ inline int tail_tiles_total(const GemmArgs& a, int BM) {
-  if (a.offsets != nullptr) return a.tails[a.G];
+template <typename P>
+__host__ __device__ inline int tail_tiles_total_p(const GemmArgs& a, const P& pl, int BM) {
+  if (a.offsets != nullptr) return pl.tail(a.G);
   int f, t;
   split_rows(a.M, BM, a.tail_rows, a.ext_rows, f, t);
   return t;
 }
+__host__ __device__ inline int tail_tiles_total(const GemmArgs& a, int BM) {
+  return tail_tiles_total_p(a, ptr_plan(a), BM);
+}
 
-// Persistent form of grouped_gemm_bf16_kernel for the forward epilogues:
-// one block per compute unit, each taking tiles from a work queue until it
-// is empty, so the blocks that draw the taller 320-row tiles take fewer of
-// them and no block waits on a second wave of launches.
+// ------------------------------------------ ring-pipelined persistent GEMM
+// Persistent forward GEMM of 256x256 (and 64x256 tail) tiles on 8 waves,
+// whose main loop keeps loads two stages ahead for one operand.
 //
-// The tiles are the kernel's 1-D tile space (full tiles, then tail tiles).
-// Its first full tiles (a multiple of 8) are split into 8 equal contiguous
-// runs of the patch order, one per XCD: block b sits on XCD b % 8 (blocks
-// are dealt to the XCDs round-robin) and takes tiles from queue[b % 8], so
-// one XCD's compute units work through neighbouring patches and share their
+// The grouped GEMM's stage time is set by how long a stage's loads take to
+// arrive, not by the matrix cores: within one XCD, the 32 blocks of a patch
+// share every operand panel, so most of a stage's 64 KB comes from the L2,
+// but the panels of the streamed operand (the expert weights of the gate/up
+// GEMM) come from HBM.  With two LDS stages a load has at most one stage to
+// arrive.  Here the LDS is five 32-KB slots (all of the CU's 160 KB): the
+// streamed operand ("far") cycles through three slots and is loaded two
+// stages ahead, the other ("near") through two, one stage ahead.
+//
+// The loads are direct-to-LDS buffer loads issued in inline asm.  The
+// compiler, which does not see that they write the LDS, then inserts no
+// waits of its own for them, and the kernel waits itself: at the barrier of
+// stage kt it needs near(kt+1) and far(kt+1), while far(kt+2), issued after
+// near(kt+1), may stay in flight.  Loads complete in issue order as far as
+// vmcnt is concerned, so that wait is vmcnt(number of far loads per wave).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSlotU4 = 256 * 8;   // one slot: 256 tile rows x 128 B
+constexpr int kSlots = 5;          // 160 KB
+
+// Buffer resource words over [base, base + bytes) (the resource make_rsrc
+// builds): loads past the end return 0.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 d;
+  d[0] = (int)(uint32_t)p;
+  d[1] = (int)(uint32_t)(p >> 32);
+  d[2] = (int)bytes;
+  d[3] = 0x00020000;
+  return d;
+}
+
+// 16 bytes per lane from global memory to LDS at lds + 16 * lane.  M0 holds
+// the LDS address (set by the compiler for the asm operand); one wait state
+// separates its write from the load that reads it.
+__device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
+// Per-lane load addressing of one tile (the same lane mapping and LDS slots
+// as gemm_tile): load i of wave w fills tile rows 8q .. 8q+7, q = w*AI + i
+// (A) or w*BI + i (B), lane l row 8q + l/8, logical chunk (l%8) ^ swizzle.
+template <int EPI, int BM, int NW>
+struct RingAddr {
+  static constexpr int BN = 256, AI = BM / 8 / NW, BI = BN / 8 / NW;
+  static constexpr int BNH = gated<EPI>() ? BN / 2 : BN;
+  const uint16_t* a_base;
+  uint32_t a_bytes, a_voff_e, a_voff_o, a_step;
+  const uint16_t* b_base;   // column tile n0, segment 0
+  uint32_t b_bytes, b_voff_e, b_voff_o, b_step;
+  int wave;
+  __device__ __forceinline__ RingAddr(const GemmArgs& a, int g, int row0, int rows, int by, int wave_,
+                                      int lane) {
+    wave = wave_;
+    const int lrow = lane >> 3;
+    const int ce = (lane & 7) ^ (lrow >> 1), co = (lane & 7) ^ (4 + (lrow >> 1));
+    a_base = static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda;
+    a_bytes = (uint32_t)rows * a.lda * 2;
+    a_voff_e = (uint32_t)((wave * AI * 8 + lrow) * a.lda + ce * 8) * 2;
+    a_voff_o = (uint32_t)((wave * AI * 8 + lrow) * a.lda + co * 8) * 2;
+    a_step = 8u * a.lda * 2;
+    const int n0 = by * BNH;
+    b_base = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride;
+    int b_local0 = wave * (BN / NW);
+    if constexpr (gated<EPI>()) {
+      if (wave >= NW / 2) {
+        b_base = static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride;
+        b_local0 -= BN / 2;
+      }
+    }
+    b_base += (size_t)n0 * a.ldb;
+    const int b_valid = a.Ndim - n0 < BNH ? a.Ndim - n0 : BNH;
+    b_bytes = (uint32_t)b_valid * a.ldb * 2;
+    b_voff_e = (uint32_t)((b_local0 + lrow) * a.ldb + ce * 8) * 2;
+    b_voff_o = (uint32_t)((b_local0 + lrow) * a.ldb + co * 8) * 2;
+    b_step = 8u * a.ldb * 2;
+  }
+  // load i of the A rows of stage kt into pool slot `slot`
+  __device__ __forceinline__ void load_a(int kt, bool live, uint32_t slot_lds, int i) const {
+    const bool odd = ((wave * AI + i) & 1) != 0;
+    lds_load16(rsrc_words(a_base, live ? a_bytes : 0u), slot_lds + (uint32_t)((wave * AI + i) * 1024),
+               (odd ? a_voff_o : a_voff_e) + (uint32_t)i * a_step + (uint32_t)kt * 128u);
+  }
+  // where the B rows of stage kt start: K segment seg of B (the shared
+  // experts' down projection is segmented), k offset within it in bytes
+  __device__ __forceinline__ void b_stage(const GemmArgs& a, int kt, const uint16_t*& base,
+                                          uint32_t& koff) const {
+    const int kb = kt * 64;
+    const int seg = a.kseg == a.Kdim ? 0 : kb / a.kseg;
+    base = b_base + (size_t)seg * a.kseg_stride;
+    koff = (uint32_t)(kb - seg * a.kseg) * 2u;
+  }
+  // load i of the B rows of a stage located by b_stage
+  __device__ __forceinline__ void load_b(const uint16_t* base, uint32_t koff, bool live, uint32_t slot_lds,
+                                         int i) const {
+    const bool odd = ((wave * BI + i) & 1) != 0;
+    lds_load16(rsrc_words(base, live ? b_bytes : 0u), slot_lds + (uint32_t)((wave * BI + i) * 1024),
+               (odd ? b_voff_o : b_voff_e) + (uint32_t)i * b_step + koff);
+  }
+  __device__ __forceinline__ void load_b(const GemmArgs& a, int kt, bool live, uint32_t slot_lds,
+                                         int i) const {
+    const uint16_t* base;
+    uint32_t koff;
+    b_stage(a, kt, base, koff);
+    load_b(base, koff, live, slot_lds, i);
+  }
+};
+
+// Pool slots of a stage: the near operand cycles through two slots, the far
+// one through three.  Far B: A in slots 0-1, B in 2-4; far A: A in 0-2, B in
+// 3-4.
+template <bool FAR_B>
+__device__ __forceinline__ int ring_slot_a(int r2, int r3) { return FAR_B ? r2 : r3; }
+template <bool FAR_B>
+__device__ __forceinline__ int ring_slot_b(int r2, int r3) { return FAR_B ? 2 + r3 : 3 + r2; }
+
+// Loads that start a tile: near(0), far(0), far(1), in that order.
+template <int EPI, int BM, bool FAR_B, int NW>
+__device__ __forceinline__ void ring_stage0(const GemmArgs& a, const RingAddr<EPI, BM, NW>& ad, int nk,
+                                            uint32_t pool_lds) {
+  using AD = RingAddr<EPI, BM, NW>;
+  auto lds = [&](int slot) { return pool_lds + (uint32_t)slot * (kSlotU4 * 16); };
+  if constexpr (FAR_B) {
+#pragma unroll
+    for (int i = 0; i < AD::AI; ++i) ad.load_a(0, true, lds(ring_slot_a<FAR_B>(0, 0)), i);
+#pragma unroll
+    for (int i = 0; i < AD::BI; ++i) ad.load_b(a, 0, true, lds(ring_slot_b<FAR_B>(0, 0)), i);
+#pragma unroll
+    for (int i = 0; i < AD::BI; ++i) ad.load_b(a, 1, nk > 1, lds(ring_slot_b<FAR_B>(1, 1)), i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < AD::BI; ++i) ad.load_b(a, 0, true, lds(ring_slot_b<FAR_B>(0, 0)), i);
+#pragma unroll
+    for (int i = 0; i < AD::AI; ++i) ad.load_a(0, true, lds(ring_slot_a<FAR_B>(0, 0)), i);
+#pragma unroll
+    for (int i = 0; i < AD::AI; ++i) ad.load_a(1, nk > 1, lds(ring_slot_a<FAR_B>(1, 1)), i);
+  }
+}
+
+// One tile.  `issued`: its first loads (ring_stage0) are already in flight.
+// pre() runs after the main loop, once every wave is past the last stage
+// barrier and its own loads have landed; then no wave reads the pool any
+// more, and pre() may start the next tile's loads.
+template <int EPI, int BM, bool FAR_B, int NW, typename Pre>
+__device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, int rows, int by,
+                                          u32x4 (&pool)[kSlots][kSlotU4], bool issued, const Pre& pre) {
+  using AD = RingAddr<EPI, BM, NW>;
+  constexpr int WGN = NW / 2, BN = 256;
+  constexpr int WTM = BM / 2, WTN = BN / WGN;     // wave tile: 8 waves 128x64 (or 32x64), 4 waves 128x128
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr bool GATED = gated<EPI>();
+  constexpr int NI = FAR_B ? AD::AI : AD::BI;     // near loads per wave per stage
+  constexpr int FI = FAR_B ? AD::BI : AD::AI;     // far loads
+  constexpr int NL = NI + FI;
+  static_assert(!GATED || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+  // opaque thread index: the persistent loop recomputes each tile's per-lane
+  // addressing instead of keeping that of both tile heights live across it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  by = __builtin_amdgcn_readfirstlane(by);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int n0 = by * AD::BNH;
+  const AD ad(a, g, row0, rows, by, wave, lane);
+  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0][0];
+  auto slot_lds = [&](int slot) { return pool_lds + (uint32_t)slot * (kSlotU4 * 16); };
+  const int nk = a.Kdim / BK;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  auto brow = [&](int j) {
+    if constexpr (GATED)
+      return j < TN / 2 ? wn * (WTN / 2) + 32 * j : BN / 2 + wn * (WTN / 2) + 32 * (j - TN / 2);
+    else
+      return wn * WTN + 32 * j;
+  };
+  // fragment r of k-step rkk from pool slots sa / sb, in the order the
+  // matrix instructions of row 0 need them first: A row 0, the B columns,
+  // then A rows 1..
+  auto read_one = [&](bf16x8 (&ra)[TM], bf16x8 (&rb)[TN], int sa, int sb, int rkk, int r) {
+    const int c = rkk * 2 + (lane >> 5);
+    const int ia = r == 0 ? 0 : (r <= TN ? -1 : r - TN);
+    if (ia >= 0) ra[ia] = __builtin_bit_cast(bf16x8, pool[sa][swz(wm * WTM + ia * 32 + (lane & 31), c)]);
+    else rb[r - 1] = __builtin_bit_cast(bf16x8, pool[sb][swz(brow(r - 1) + (lane & 31), c)]);
+  };
+  // load l of those issued during stage kt: near(kt+1) first, then far(kt+2);
+  // bb / bk: where the B rows loaded during this stage start (b_stage)
+  const uint16_t* bb = nullptr;
+  uint32_t bk = 0;
+  auto issue = [&](int kt, int l, int r2n, int r3f) {
+    const bool near_live = kt + 1 < nk, far_live = kt + 2 < nk;
+    if constexpr (FAR_B) {
+      if (l < NI) ad.load_a(kt + 1, near_live, slot_lds(ring_slot_a<FAR_B>(r2n, 0)), l);
+      else ad.load_b(bb, bk, far_live, slot_lds(ring_slot_b<FAR_B>(0, r3f)), l - NI);
+    } else {
+      if (l < NI) ad.load_b(bb, bk, near_live, slot_lds(ring_slot_b<FAR_B>(r2n, 0)), l);
+      else ad.load_a(kt + 2, far_live, slot_lds(ring_slot_a<FAR_B>(0, r3f)), l - NI);
+    }
+  };
+  // matrix instructions i0..i1 (rows) of one k-step in a fixed order: after
+  // instruction s, fragment s / RS of the next k-step when s % RS == 0, and
+  // load l0 + s / 2 of the stage when s is odd; leftovers at the end
+  auto kstep = [&](const bf16x8 (&fa_)[TM], const bf16x8 (&fb_)[TN], int i0, int i1, bf16x8 (&ra)[TM],
+                   bf16x8 (&rb)[TN], int sa, int sb, int rkk, bool rd, int RS, int kt, int l0, int l1,
+                   int r2n, int r3f) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i < i0 || i >= i1) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
+        if (rd && s % RS == 0 && s / RS < TM + TN) read_one(ra, rb, sa, sb, rkk, s / RS);
+        if ((s & 1) && l0 + s / 2 < l1) issue(kt, l0 + s / 2, r2n, r3f);
+        __builtin_amdgcn_sched_barrier(0);
+        ++s;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TM + TN; ++t)
+      if (rd && t * RS >= s) read_one(ra, rb, sa, sb, rkk, t);
+#pragma unroll
+    for (int t = 0; t < NL; ++t)
+      if (l0 + t < l1 && 2 * t + 1 >= s) issue(kt, l0 + t, r2n, r3f);
+  };
+
+  constexpr int H = TM / 2;
+  bf16x8 fa[2][TM], fb[2][TN];
+  if (!issued) ring_stage0<EPI, BM, FAR_B, NW>(a, ad, nk, pool_lds);
+  // near(0) and far(0) landed; far(1) may be in flight
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(FI) : "memory");
+  __syncthreads();
+  int r2 = 0, r3 = 0;   // ring positions of stage kt: kt % 2, kt % 3
+#pragma unroll
+  for (int t = 0; t < TM + TN; ++t)
+    read_one(fa[0], fb[0], ring_slot_a<FAR_B>(0, 0), ring_slot_b<FAR_B>(0, 0), 0, t);
+  // k-steps 0, 1, 2 and the first half of 3 of stage kt; its loads (near
+  // kt+1 into the near ring's next slot, far kt+2 into the far ring's slot
+  // after next) go out during k-steps 0 and 1
+  auto body = [&](int kt) {
+    const int sa = ring_slot_a<FAR_B>(r2, r3), sb = ring_slot_b<FAR_B>(r2, r3);
+    const int r2n = r2 ^ 1, r3f = r3 == 0 ? 2 : r3 - 1;
+    ad.b_stage(a, FAR_B ? kt + 2 : kt + 1, bb, bk);
+    constexpr int LM = TM * TN / 2 < NL ? TM * TN / 2 : NL;
+    kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], sa, sb, 1, true, 2, kt, 0, LM, r2n, r3f);
+    kstep(fa[1], fb[1], 0, TM, fa[0], fb[0], sa, sb, 2, true, 2, kt, LM, NL, r2n, r3f);
+    kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], sa, sb, 3, true, 2, kt, 0, 0, r2n, r3f);
+    kstep(fa[1], fb[1], 0, H, fa[0], fb[0], 0, 0, 0, false, 1, kt, 0, 0, r2n, r3f);
+  };
+  body(0);
+  for (int kt = 1; kt < nk; ++kt) {
+    // stage kt's operands landed: every load but the far ones of stage kt+1
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(FI) : "memory");
+    __syncthreads();
+    r2 ^= 1;
+    r3 = r3 == 2 ? 0 : r3 + 1;
+    // second half of k-step 3 of stage kt-1, reading the first fragments of
+    // stage kt
+    kstep(fa[1], fb[1], H, TM, fa[0], fb[0], ring_slot_a<FAR_B>(r2, r3), ring_slot_b<FAR_B>(r2, r3), 0,
+          true, 1, kt, 0, 0, 0, 0);
+    body(kt);
+  }
+  kstep(fa[1], fb[1], H, TM, fa[0], fb[0], 0, 0, 0, false, 1, 0, 0, 0, 0, 0);
+  // the empty loads of the last stages still write the pool; once every
+  // wave's have landed, no wave touches the pool until pre() starts the
+  // next tile
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  pre();
+  store_forward_tile<EPI, TM, TN, WTM, WTN>(a, acc, row0, rows, n0, wm, wn, lane);
+}
+
+// The tile plan in VGPRs: lane l holds entry l + 64 r (r < 5) of the group
+// offsets and of the full- and tail-tile prefixes, so a lookup is a
+// readlane (uniform index) and needs no memory access.  Up to 320 entries:
+// G <= 256 groups.
+struct RegPlan {
+  int off[5], til[5], tal[5];
+  __device__ __forceinline__ static int pick(const int (&v)[5], int j) {
+    const int r = j >> 6;
+    const int x = r == 0 ? v[0] : r == 1 ? v[1] : r == 2 ? v[2] : r == 3 ? v[3] : v[4];
+    return __builtin_amdgcn_readlane(x, j & 63);
+  }
+  __device__ __forceinline__ int offset(int i) const { return pick(off, i); }
+  __device__ __forceinline__ int tile(int i) const { return pick(til, i); }
+  __device__ __forceinline__ int tail(int i) const { return pick(tal, i); }
+};
+
+// Persistent forward GEMM over the ring-pipelined tiles: one block per
+// compute unit, each taking tiles from work queues until they are empty, so
+// no block waits on a second wave of launches.
+//
+// The tiles are the 1-D tile space of the plan (full 256-row tiles, then
+// 64-row tail tiles; the plan has no extended tiles, ext_rows = 0).  Its
+// first full tiles (a multiple of 8) are split into 8 equal contiguous runs
+// of the patch order, one per XCD: block b sits on XCD b % 8 (blocks are
+// dealt to the XCDs round-robin) and takes tiles from queue[b % 8], so one
+// XCD's compute units work through neighbouring patches and share their
 // panels in that XCD's L2.  A block whose run is used up takes the other
-// runs' remaining tiles, then queue[8]: the leftover full tiles and the tail
-// tiles.  Counters are bumped by one lane with a global atomic; they start
-// at zero (the plan kernel clears them).
+// runs' remaining tiles, then queue[8]: the leftover full tiles and the
+// tail tiles.  Counters are bumped by one lane with a global atomic; they
+// start at zero (the plan kernel clears them).
 //
-// Each block reserves its next tile one tile ahead and, after the main loop
-// of the current tile, issues that tile's first stage into the free LDS
-// buffer, so those loads are in flight during the current epilogue.
-template <int EPI>
-__global__ __launch_bounds__(512) void grouped_gemm_bf16_persistent_kernel(GemmArgs ga) {
-  __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
-  __shared__ u32x4 sB[2][256 * 8];
-  // the tile plan (group offsets and tile prefixes), copied once so that
-  // locating a tile takes LDS reads instead of dependent global loads
-  __shared__ int32_t s_plan[3][257];
-  __shared__ int s_next, s_cur, s_spec;
-  constexpr int SAN = (256 + kExtRows) * 8, SBN = 256 * 8;
+// Thread 0 keeps the queue state in registers and reserves its next
+// position in the own run one tile ahead.  The claimed tile goes to the
+// other waves through one word of the far ring's third slot, which the
+// loads first write during stage 0 of the tile, after every wave has read
+// it.  After the main loop of a tile, the block claims and decodes the next
+// one and issues its first loads, which are then in flight during the
+// current tile's epilogue.
+template <int EPI, bool FAR_B, int NW>
+__global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArgs ga) {
+  __shared__ u32x4 pool[kSlots][kSlotU4];
   constexpr int BNH = gated<EPI>() ? 128 : 256;
   const int tid = threadIdx.x;
-  GemmArgs a = ga;
-  if (a.offsets != nullptr) {
-    for (int i = tid; i <= a.G; i += blockDim.x) {
-      s_plan[0][i] = a.offsets[i];
-      s_plan[1][i] = a.tiles[i];
-      s_plan[2][i] = a.tails[i];
-    }
-    a.offsets = s_plan[0];
-    a.tiles = s_plan[1];
-    a.tails = s_plan[2];
+  const int lane = tid & 63;
+  const GemmArgs a = ga;
+  RegPlan pl;
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    const int i = lane + 64 * r;
+    const bool in = a.offsets != nullptr && i <= a.G;
+    pl.off[r] = in ? a.offsets[i] : 0;
+    pl.til[r] = in ? a.tiles[i] : 0;
+    pl.tal[r] = in ? a.tails[i] : 0;
   }
-  if (tid == 0) {
-    s_cur = 0;
-    s_spec = -1;
-  }
-  __syncthreads();
+  int32_t* s_next = reinterpret_cast<int32_t*>(&pool[FAR_B ? 4 : 2][0]);
   const int ntiles = (a.Ndim + BNH - 1) / BNH;
-  const int real = full_tiles_total(a, 256) * ntiles;
-  const int total = real + tail_tiles_total(a, 256) * ntiles;
+  const int real = full_tiles_total_p(a, pl, 256) * ntiles;
+  const int total = real + tail_tiles_total_p(a, pl, 256) * ntiles;
   const int full = real - real % 8;
-  const int q = full / 8;                    // tiles per XCD run
-  const int rest = total - full;             // queue[8]: leftovers and tails
+  const int q = full / 8;
+  const int rest = total - full;
   const int xcd = blockIdx.x & 7;
   int32_t* queue = a.queue;
 
-  // Thread 0 only.  The queue being drained (s_cur 0: own run, 1..7: the
-  // runs of the next XCDs, 8: leftovers and tails, 9: none) and the
-  // position reserved in the own run ahead of time (s_spec, -1: none) live
-  // in LDS.  The reservation for the tile after next is requested here and
-  // its value written to s_spec only after the current tile's epilogue, so
-  // no wave waits on the atomic.
-  int pending = -1;
+  // thread 0's queue state: the queue being drained (0: own run, 1..7 the
+  // next XCDs' runs, 8: leftovers and tails, 9: none) and the position in
+  // the own run requested at the previous claim (-1: none), whose value is
+  // used one tile later, when it has long arrived
+  int cur = 0, pending = -1;
   auto claim = [&]() -> int {
-    int cur = s_cur;
-    int spec = s_spec;
+    int spec = pending;
     int h = -1;
     while (cur < 9) {
       const int y = cur < 8 ? (xcd + cur) & 7 : 8;
@@ -1058,22 +1344,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_persistent_kernel(GemmA
       if (h >= 0) break;
       ++cur;
     }
-    s_cur = cur;
-    s_spec = -1;
     pending = cur == 0 ? atomicAdd(&queue[xcd], 1) : -1;
     return h;
   };
-  // a tile of the 1-D space: coordinates and height class (320, 256, 64);
-  // false when it holds no rows
-  // (block-uniform results: kept in scalar registers)
   auto decode = [&](int h, int& g, int& row0, int& rows, int& by, int& bm) -> bool {
     bool ok = true;
     if (h < real) {
-      find_tile_2d(a, 256, ntiles, h, real, g, row0, rows, by);
-      bm = rows > 256 ? 256 + kExtRows : 256;
+      find_tile_2d_p(a, pl, 256, ntiles, h, real, g, row0, rows, by);
+      bm = 256;
     } else {
       bm = kTailRows;
-      ok = find_tail(a, 256, ntiles, h - real, g, row0, rows, by);
+      ok = find_tail_p(a, pl, 256, ntiles, h - real, g, row0, rows, by);
     }
     g = __builtin_amdgcn_readfirstlane(g);
     row0 = __builtin_amdgcn_readfirstlane(row0);
@@ -1083,45 +1364,45 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_persistent_kernel(GemmA
     return __builtin_amdgcn_readfirstlane((int)ok) != 0;
   };
 
-  if (tid == 0) s_next = claim();
+  if (tid == 0) *s_next = claim();
   __syncthreads();
-  if (tid == 0) s_spec = pending;
-  int h = __builtin_amdgcn_readfirstlane(s_next);
+  int h = __builtin_amdgcn_readfirstlane(*s_next);
   int g = 0, row0 = 0, rows = 0, by = 0, bm = 0;
   bool work = h >= 0 && decode(h, g, row0, rows, by, bm);
-  int b0 = 0;               // LDS buffer of the tile's stage 0
-  bool issued = false;      // its stage 0 already in flight
+  bool issued = false;
   const int nk = a.Kdim / BK;
+  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0][0];
   while (h >= 0) {
     int h_next = -1, g2 = 0, r2 = 0, n2 = 0, y2 = 0, bm2 = 0;
     bool next_work = false;
-    // after the main loop: publish the reserved tile, request the next
-    // reservation, and start the reserved tile's loads into the free buffer
-    auto pre = [&](int free_buf) {
-      if (tid == 0) s_next = claim();
+    // claim the next tile, decode it and start its loads
+    auto pre = [&]() {
+      if (tid == 0) *s_next = claim();
       __syncthreads();
-      h_next = __builtin_amdgcn_readfirstlane(s_next);
+      h_next = __builtin_amdgcn_readfirstlane(*s_next);
       next_work = h_next >= 0 && decode(h_next, g2, r2, n2, y2, bm2);
-      if (next_work) issue_stage0<EPI, SAN, SBN>(a, g2, r2, n2, y2, bm2, free_buf, sA, sB);
+      if (next_work) {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+        if (bm2 == 256)
+          ring_stage0<EPI, 256, FAR_B, NW>(a, RingAddr<EPI, 256, NW>(a, g2, r2, n2, y2, w, t & 63), nk,
+                                           pool_lds);
+        else
+          ring_stage0<EPI, kTailRows, FAR_B, NW>(a, RingAddr<EPI, kTailRows, NW>(a, g2, r2, n2, y2, w, t & 63),
+                                                 nk, pool_lds);
+      }
     };
     if (!work) {
-      // a tile slot without rows: nothing computed, nothing was issued for
-      // it, and buffer b0 stays free (every wave has read s_next before
-      // thread 0 writes it again)
+      // a tile slot without rows: every wave has read s_next before thread
+      // 0 writes it again
       __syncthreads();
-      pre(b0);
+      pre();
+    } else if (bm == 256) {
+      ring_tile<EPI, 256, FAR_B, NW>(a, g, row0, rows, by, pool, issued, pre);
     } else {
-      if (bm == 256 + kExtRows)
-        gemm_tile<EPI, 256 + kExtRows, 256, 2, 4, SAN, SBN, false, true>(a, g, row0, rows, by, sA, sB, b0, issued, pre);
-      else if (bm == 256)
-        gemm_tile<EPI, 256, 256, 2, 4, SAN, SBN, false, true>(a, g, row0, rows, by, sA, sB, b0, issued, pre);
-      else
-        gemm_tile<EPI, kTailRows, 256, 2, 4, SAN, SBN, false, true>(a, g, row0, rows, by, sA, sB, b0, issued, pre);
-      b0 = (nk + b0) & 1;
+      ring_tile<EPI, kTailRows, FAR_B, NW>(a, g, row0, rows, by, pool, issued, pre);
     }
-    // the reservation has long arrived; the next tile's first barrier
-    // publishes it
-    if (tid == 0) s_spec = pending;
     issued = next_work;
     work = next_work;
     h = h_next;
@@ -1630,7 +1911,8 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
     // one block per compute unit, a multiple of the 8 XCDs
     int blocks = cu_count() / 8 * 8;
     if (blocks < 8) blocks = 8;
-    hipLaunchKernelGGL((grouped_gemm_bf16_persistent_kernel<kFwd ? EPI : EPI_NONE>), dim3(blocks),
+    // the weights are the streamed operand: they run two stages ahead
+    hipLaunchKernelGGL((grouped_gemm_bf16_ring_kernel<kFwd ? EPI : EPI_NONE, true, 8>), dim3(blocks),
                        dim3(512), 0, s, a);
   } else if (bm == 256)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
@@ -1687,8 +1969,9 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   // fp32 problems: one block per 32 rows; bf16: tiles sized to the mean
   // group (all groups share one tile height so the plan is one prefix sum)
   const int bm = ffn_row_tile(rows_alloc, p.N, bf16);
+  // the persistent 256-row kernel runs full and tail tiles, no extended ones
   const int tail_rows = bf16 && bm == 256 ? kTailRows : 0;
-  const int ext_rows = bf16 && bm == 256 ? kExtRows : 0;
+  const int ext_rows = 0;
   // grid bound: at most rows/bm + 1 full tiles and one tail tile per group
   const int mtiles_max = (rows_alloc + bm - 1) / bm + p.N + (tail_rows > 0 ? p.N : 0);
   int32_t* tails = tiles + (p.N + 2);
@@ -1748,7 +2031,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     const int ws_w = p.n_shared * p.d_ff_shared;
     const int sbm = ffn_row_tile(p.T, 1, bf16);
     const int s_tail = bf16 && sbm == 256 ? kTailRows : 0;
-    const int s_ext = bf16 && sbm == 256 ? kExtRows : 0;
+    const int s_ext = 0;
     int mt = (p.T + sbm - 1) / sbm;
     if (s_tail > 0) {
       int f, t;

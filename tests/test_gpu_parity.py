@@ -300,12 +300,13 @@ def _tile_case(act, T, want_tile, want_shared_tile):
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
 def test_grouped_ffn_256_row_tiles(act):
     """3100 tokens x top-4 over 12 experts: a mean group of 1033 rows, so the
-    256-row kernel runs the routed groups.  Its three tile kinds all occur:
-    last tiles extended by 1, 44 and 64 rows (257, 300, 320, 576), 64-row
-    tail tiles (groups of 1 and 64 rows), partly filled 256-row tiles (65,
-    255, and the third tiles of 321 and 600), an exact multiple (512) and an
-    empty group.  The shared expert over 3100 tokens (12 tiles and 28 rows)
-    has its last tile extended.  Every row is checked."""
+    persistent 256-row kernel runs the routed groups.  Both of its tile
+    kinds occur in every position: 64-row tail tiles after a full tile (the
+    groups ending 1, 44 and 64 rows past a multiple of 256: 257, 300, 320,
+    576) and on their own (groups of 1 and 64 rows), partly filled 256-row
+    tiles (65, 255, and the third tiles of 321 and 600), an exact multiple
+    (512) and an empty group.  The shared expert over 3100 tokens (12 tiles
+    and 28 rows) ends in a tail tile.  Every row is checked."""
     _tile_case(act, 3100, 256, 256)
 
 
