@@ -979,28 +979,28 @@ __host__ __device__ inline int tail_tiles_total(const GemmArgs& a, int BM) {
 }
 
 // ------------------------------------------ ring-pipelined persistent GEMM
-// Persistent forward GEMM of 256x256 (and 64x256 tail) tiles on 8 waves,
-// whose main loop keeps loads two stages ahead for one operand.
+// Persistent forward GEMM of 256x256 tiles (and 64-row tail tiles) on 8
+// waves, whose main loop keeps the weight loads two stages ahead.
 //
 // The grouped GEMM's stage time is set by how long a stage's loads take to
-// arrive, not by the matrix cores: within one XCD, the 32 blocks of a patch
-// share every operand panel, so most of a stage's 64 KB comes from the L2,
-// but the panels of the streamed operand (the expert weights of the gate/up
-// GEMM) come from HBM.  With two LDS stages a load has at most one stage to
-// arrive.  Here the LDS is five 32-KB slots (all of the CU's 160 KB): the
-// streamed operand ("far") cycles through three slots and is loaded two
-// stages ahead, the other ("near") through two, one stage ahead.
+// arrive.  Within one XCD, the 32 blocks of a patch share every operand
+// panel, so most of a stage's 64 KB comes from the L2, but the weight panels
+// are streamed from HBM, and with two LDS stages a load has at most one
+// stage to arrive.  Here the LDS is five 32-KB slots (all of the CU's 160
+// KB): two for the activations (loaded one stage ahead) and three for the
+// weights (loaded two stages ahead).  The plan has no extended 320-row
+// tiles: their taller activation slots would leave room for only two weight
+// slots, and measured, such tiles gave back what they save in traffic.
 //
 // The loads are direct-to-LDS buffer loads issued in inline asm.  The
 // compiler, which does not see that they write the LDS, then inserts no
 // waits of its own for them, and the kernel waits itself: at the barrier of
-// stage kt it needs near(kt+1) and far(kt+1), while far(kt+2), issued after
-// near(kt+1), may stay in flight.  Loads complete in issue order as far as
-// vmcnt is concerned, so that wait is vmcnt(number of far loads per wave).
+// stage kt it needs A(kt+1) and B(kt+1), while B(kt+2), issued after
+// A(kt+1), may stay in flight.  Loads complete in issue order as far as
+// vmcnt is concerned, so that wait is vmcnt(number of B loads per wave).
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSlotU4 = 256 * 8;   // one slot: 256 tile rows x 128 B
-constexpr int kSlots = 5;          // 160 KB
+constexpr int kPoolU4 = 160 * 1024 / 16;   // the LDS pool in 16-byte units
 
 // Buffer resource words over [base, base + bytes) (the resource make_rsrc
 // builds): loads past the end return 0.
@@ -1022,12 +1022,28 @@ __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t lds, uint32_t vo
                :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
-// Per-lane load addressing of one tile (the same lane mapping and LDS slots
-// as gemm_tile): load i of wave w fills tile rows 8q .. 8q+7, q = w*AI + i
-// (A) or w*BI + i (B), lane l row 8q + l/8, logical chunk (l%8) ^ swizzle.
-template <int EPI, int BM, int NW>
+// Pool layout: two A slots, then three B slots, 32 KB each (256 tile rows
+// of 128 bytes).
+struct RingLayout {
+  static constexpr int kBAhead = 2;   // stages B is loaded ahead
+  static constexpr int kBSlots = 3;
+  static constexpr uint32_t kSlot = 256 * 128;
+  __device__ static constexpr uint32_t a_off(int s) { return (uint32_t)s * kSlot; }
+  __device__ static constexpr uint32_t b_off(int s) { return (2 + (uint32_t)s) * kSlot; }
+  static_assert((2 + kBSlots) * kSlot <= kPoolU4 * 16, "the slots fit the pool");
+};
+// The claimed tile reaches every wave through the pool's last 16 bytes, in
+// the third B slot, which the loads first write during stage 0 of a tile,
+// after its first barrier.
+constexpr int kNextU4 = kPoolU4 - 1;
+
+// Per-lane load addressing of one tile (the lane mapping and row layout of
+// gemm_tile): load i of wave w fills tile rows 8q .. 8q+7, q = w*AI + i (A)
+// or w*BI + i (B), lane l row 8q + l/8 at 16-byte slot l%8, which holds
+// logical chunk (l%8) ^ ((8q + l/8) >> 1 & 7).
+template <int EPI, int BM>
 struct RingAddr {
-  static constexpr int BN = 256, AI = BM / 8 / NW, BI = BN / 8 / NW;
+  static constexpr int NW = 8, BN = 256, AI = BM / 8 / NW, BI = BN / 8 / NW;
   static constexpr int BNH = gated<EPI>() ? BN / 2 : BN;
   const uint16_t* a_base;
   uint32_t a_bytes, a_voff_e, a_voff_o, a_step;
@@ -1060,7 +1076,7 @@ struct RingAddr {
     b_voff_o = (uint32_t)((b_local0 + lrow) * a.ldb + co * 8) * 2;
     b_step = 8u * a.ldb * 2;
   }
-  // load i of the A rows of stage kt into pool slot `slot`
+  // load i of the A rows of stage kt into the slot at LDS address slot_lds
   __device__ __forceinline__ void load_a(int kt, bool live, uint32_t slot_lds, int i) const {
     const bool odd = ((wave * AI + i) & 1) != 0;
     lds_load16(rsrc_words(a_base, live ? a_bytes : 0u), slot_lds + (uint32_t)((wave * AI + i) * 1024),
@@ -1082,64 +1098,44 @@ struct RingAddr {
     lds_load16(rsrc_words(base, live ? b_bytes : 0u), slot_lds + (uint32_t)((wave * BI + i) * 1024),
                (odd ? b_voff_o : b_voff_e) + (uint32_t)i * b_step + koff);
   }
-  __device__ __forceinline__ void load_b(const GemmArgs& a, int kt, bool live, uint32_t slot_lds,
-                                         int i) const {
-    const uint16_t* base;
-    uint32_t koff;
-    b_stage(a, kt, base, koff);
-    load_b(base, koff, live, slot_lds, i);
-  }
 };
 
-// Pool slots of a stage: the near operand cycles through two slots, the far
-// one through three.  Far B: A in slots 0-1, B in 2-4; far A: A in 0-2, B in
-// 3-4.
-template <bool FAR_B>
-__device__ __forceinline__ int ring_slot_a(int r2, int r3) { return FAR_B ? r2 : r3; }
-template <bool FAR_B>
-__device__ __forceinline__ int ring_slot_b(int r2, int r3) { return FAR_B ? 2 + r3 : 3 + r2; }
-
-// Loads that start a tile: near(0), far(0), far(1), in that order.
-template <int EPI, int BM, bool FAR_B, int NW>
-__device__ __forceinline__ void ring_stage0(const GemmArgs& a, const RingAddr<EPI, BM, NW>& ad, int nk,
+// Loads that start a tile, in this order: A(0), B(0), B(1).
+template <int EPI, int BM>
+__device__ __forceinline__ void ring_stage0(const GemmArgs& a, const RingAddr<EPI, BM>& ad, int nk,
                                             uint32_t pool_lds) {
-  using AD = RingAddr<EPI, BM, NW>;
-  auto lds = [&](int slot) { return pool_lds + (uint32_t)slot * (kSlotU4 * 16); };
-  if constexpr (FAR_B) {
+  using AD = RingAddr<EPI, BM>;
+  using L = RingLayout;
 #pragma unroll
-    for (int i = 0; i < AD::AI; ++i) ad.load_a(0, true, lds(ring_slot_a<FAR_B>(0, 0)), i);
+  for (int i = 0; i < AD::AI; ++i) ad.load_a(0, true, pool_lds + L::a_off(0), i);
+  const uint16_t* bb;
+  uint32_t bk;
+  ad.b_stage(a, 0, bb, bk);
 #pragma unroll
-    for (int i = 0; i < AD::BI; ++i) ad.load_b(a, 0, true, lds(ring_slot_b<FAR_B>(0, 0)), i);
+  for (int i = 0; i < AD::BI; ++i) ad.load_b(bb, bk, true, pool_lds + L::b_off(0), i);
+  ad.b_stage(a, 1, bb, bk);
 #pragma unroll
-    for (int i = 0; i < AD::BI; ++i) ad.load_b(a, 1, nk > 1, lds(ring_slot_b<FAR_B>(1, 1)), i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < AD::BI; ++i) ad.load_b(a, 0, true, lds(ring_slot_b<FAR_B>(0, 0)), i);
-#pragma unroll
-    for (int i = 0; i < AD::AI; ++i) ad.load_a(0, true, lds(ring_slot_a<FAR_B>(0, 0)), i);
-#pragma unroll
-    for (int i = 0; i < AD::AI; ++i) ad.load_a(1, nk > 1, lds(ring_slot_a<FAR_B>(1, 1)), i);
-  }
+  for (int i = 0; i < AD::BI; ++i) ad.load_b(bb, bk, nk > 1, pool_lds + L::b_off(1), i);
 }
 
 // One tile.  `issued`: its first loads (ring_stage0) are already in flight.
 // pre() runs after the main loop, once every wave is past the last stage
-// barrier and its own loads have landed; then no wave reads the pool any
-// more, and pre() may start the next tile's loads.
-template <int EPI, int BM, bool FAR_B, int NW, typename Pre>
+// barrier and every wave's loads have landed; then no wave reads the pool
+// any more, and pre() may start the next tile's loads.
+template <int EPI, int BM, typename Pre>
 __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, int rows, int by,
-                                          u32x4 (&pool)[kSlots][kSlotU4], bool issued, const Pre& pre) {
-  using AD = RingAddr<EPI, BM, NW>;
-  constexpr int WGN = NW / 2, BN = 256;
-  constexpr int WTM = BM / 2, WTN = BN / WGN;     // wave tile: 8 waves 128x64 (or 32x64), 4 waves 128x128
+                                          u32x4 (&pool)[kPoolU4], bool issued, const Pre& pre) {
+  using AD = RingAddr<EPI, BM>;
+  using L = RingLayout;
+  constexpr int WGN = 4, BN = 256;
+  constexpr int WTM = BM / 2, WTN = BN / WGN;     // wave tile: 128x64 or 32x64
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr bool GATED = gated<EPI>();
-  constexpr int NI = FAR_B ? AD::AI : AD::BI;     // near loads per wave per stage
-  constexpr int FI = FAR_B ? AD::BI : AD::AI;     // far loads
-  constexpr int NL = NI + FI;
+  constexpr int NL = AD::AI + AD::BI;             // loads per wave per stage: A first, then B
+  constexpr int FI = AD::BI;                      // loads that may stay in flight at a barrier
   static_assert(!GATED || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
   // opaque thread index: the persistent loop recomputes each tile's per-lane
-  // addressing instead of keeping that of both tile heights live across it
+  // addressing instead of keeping that of every tile height live across it
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
@@ -1151,8 +1147,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, in
   const int wm = wave / WGN, wn = wave % WGN;
   const int n0 = by * AD::BNH;
   const AD ad(a, g, row0, rows, by, wave, lane);
-  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0][0];
-  auto slot_lds = [&](int slot) { return pool_lds + (uint32_t)slot * (kSlotU4 * 16); };
+  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0];
   const int nk = a.Kdim / BK;
 
   f32x16 acc[TM][TN];
@@ -1168,35 +1163,31 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, in
     else
       return wn * WTN + 32 * j;
   };
-  // fragment r of k-step rkk from pool slots sa / sb, in the order the
+  // fragment r of k-step rkk from A slot sa and B slot sb, in the order the
   // matrix instructions of row 0 need them first: A row 0, the B columns,
   // then A rows 1..
   auto read_one = [&](bf16x8 (&ra)[TM], bf16x8 (&rb)[TN], int sa, int sb, int rkk, int r) {
     const int c = rkk * 2 + (lane >> 5);
     const int ia = r == 0 ? 0 : (r <= TN ? -1 : r - TN);
-    if (ia >= 0) ra[ia] = __builtin_bit_cast(bf16x8, pool[sa][swz(wm * WTM + ia * 32 + (lane & 31), c)]);
-    else rb[r - 1] = __builtin_bit_cast(bf16x8, pool[sb][swz(brow(r - 1) + (lane & 31), c)]);
+    if (ia >= 0)
+      ra[ia] = __builtin_bit_cast(bf16x8, pool[L::a_off(sa) / 16 + swz(wm * WTM + ia * 32 + (lane & 31), c)]);
+    else
+      rb[r - 1] = __builtin_bit_cast(bf16x8, pool[L::b_off(sb) / 16 + swz(brow(r - 1) + (lane & 31), c)]);
   };
-  // load l of those issued during stage kt: near(kt+1) first, then far(kt+2);
-  // bb / bk: where the B rows loaded during this stage start (b_stage)
+  // load l of those issued during stage kt: A(kt+1) into A slot sa_n, then
+  // B(kt + kBAhead) into B slot sb_n; bb / bk locate those B rows
   const uint16_t* bb = nullptr;
   uint32_t bk = 0;
-  auto issue = [&](int kt, int l, int r2n, int r3f) {
-    const bool near_live = kt + 1 < nk, far_live = kt + 2 < nk;
-    if constexpr (FAR_B) {
-      if (l < NI) ad.load_a(kt + 1, near_live, slot_lds(ring_slot_a<FAR_B>(r2n, 0)), l);
-      else ad.load_b(bb, bk, far_live, slot_lds(ring_slot_b<FAR_B>(0, r3f)), l - NI);
-    } else {
-      if (l < NI) ad.load_b(bb, bk, near_live, slot_lds(ring_slot_b<FAR_B>(r2n, 0)), l);
-      else ad.load_a(kt + 2, far_live, slot_lds(ring_slot_a<FAR_B>(0, r3f)), l - NI);
-    }
+  auto issue = [&](int kt, int l, int sa_n, int sb_n) {
+    if (l < AD::AI) ad.load_a(kt + 1, kt + 1 < nk, pool_lds + L::a_off(sa_n), l);
+    else ad.load_b(bb, bk, kt + L::kBAhead < nk, pool_lds + L::b_off(sb_n), l - AD::AI);
   };
-  // matrix instructions i0..i1 (rows) of one k-step in a fixed order: after
+  // matrix instructions of rows i0..i1 of one k-step in a fixed order: after
   // instruction s, fragment s / RS of the next k-step when s % RS == 0, and
   // load l0 + s / 2 of the stage when s is odd; leftovers at the end
   auto kstep = [&](const bf16x8 (&fa_)[TM], const bf16x8 (&fb_)[TN], int i0, int i1, bf16x8 (&ra)[TM],
                    bf16x8 (&rb)[TN], int sa, int sb, int rkk, bool rd, int RS, int kt, int l0, int l1,
-                   int r2n, int r3f) {
+                   int sa_n, int sb_n) {
     int s = 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -1205,7 +1196,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, in
       for (int j = 0; j < TN; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
         if (rd && s % RS == 0 && s / RS < TM + TN) read_one(ra, rb, sa, sb, rkk, s / RS);
-        if ((s & 1) && l0 + s / 2 < l1) issue(kt, l0 + s / 2, r2n, r3f);
+        if ((s & 1) && l0 + s / 2 < l1) issue(kt, l0 + s / 2, sa_n, sb_n);
         __builtin_amdgcn_sched_barrier(0);
         ++s;
       }
@@ -1215,43 +1206,40 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, in
       if (rd && t * RS >= s) read_one(ra, rb, sa, sb, rkk, t);
 #pragma unroll
     for (int t = 0; t < NL; ++t)
-      if (l0 + t < l1 && 2 * t + 1 >= s) issue(kt, l0 + t, r2n, r3f);
+      if (l0 + t < l1 && 2 * t + 1 >= s) issue(kt, l0 + t, sa_n, sb_n);
   };
 
   constexpr int H = TM / 2;
   bf16x8 fa[2][TM], fb[2][TN];
-  if (!issued) ring_stage0<EPI, BM, FAR_B, NW>(a, ad, nk, pool_lds);
-  // near(0) and far(0) landed; far(1) may be in flight
+  if (!issued) ring_stage0<EPI, BM>(a, ad, nk, pool_lds);
+  // A(0) and B(0) landed; B(1) may be in flight
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(FI) : "memory");
   __syncthreads();
-  int r2 = 0, r3 = 0;   // ring positions of stage kt: kt % 2, kt % 3
+  int ra2 = 0, rb = 0;   // slots of stage kt: kt % 2 (A) and kt % kBSlots (B)
 #pragma unroll
-  for (int t = 0; t < TM + TN; ++t)
-    read_one(fa[0], fb[0], ring_slot_a<FAR_B>(0, 0), ring_slot_b<FAR_B>(0, 0), 0, t);
-  // k-steps 0, 1, 2 and the first half of 3 of stage kt; its loads (near
-  // kt+1 into the near ring's next slot, far kt+2 into the far ring's slot
-  // after next) go out during k-steps 0 and 1
+  for (int t = 0; t < TM + TN; ++t) read_one(fa[0], fb[0], 0, 0, 0, t);
+  // k-steps 0, 1, 2 and the first half of 3 of stage kt; its loads go out
+  // during k-steps 0 and 1
   auto body = [&](int kt) {
-    const int sa = ring_slot_a<FAR_B>(r2, r3), sb = ring_slot_b<FAR_B>(r2, r3);
-    const int r2n = r2 ^ 1, r3f = r3 == 0 ? 2 : r3 - 1;
-    ad.b_stage(a, FAR_B ? kt + 2 : kt + 1, bb, bk);
+    const int sa_n = ra2 ^ 1;
+    const int sb_n = rb == 0 ? 2 : rb - 1;   // (kt + 2) % 3
+    ad.b_stage(a, kt + L::kBAhead, bb, bk);
     constexpr int LM = TM * TN / 2 < NL ? TM * TN / 2 : NL;
-    kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], sa, sb, 1, true, 2, kt, 0, LM, r2n, r3f);
-    kstep(fa[1], fb[1], 0, TM, fa[0], fb[0], sa, sb, 2, true, 2, kt, LM, NL, r2n, r3f);
-    kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], sa, sb, 3, true, 2, kt, 0, 0, r2n, r3f);
-    kstep(fa[1], fb[1], 0, H, fa[0], fb[0], 0, 0, 0, false, 1, kt, 0, 0, r2n, r3f);
+    kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], ra2, rb, 1, true, 2, kt, 0, LM, sa_n, sb_n);
+    kstep(fa[1], fb[1], 0, TM, fa[0], fb[0], ra2, rb, 2, true, 2, kt, LM, NL, sa_n, sb_n);
+    kstep(fa[0], fb[0], 0, TM, fa[1], fb[1], ra2, rb, 3, true, 2, kt, 0, 0, sa_n, sb_n);
+    kstep(fa[1], fb[1], 0, H, fa[0], fb[0], 0, 0, 0, false, 1, kt, 0, 0, sa_n, sb_n);
   };
   body(0);
   for (int kt = 1; kt < nk; ++kt) {
-    // stage kt's operands landed: every load but the far ones of stage kt+1
+    // stage kt's operands landed: every load but the B loads of stage kt+1
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(FI) : "memory");
     __syncthreads();
-    r2 ^= 1;
-    r3 = r3 == 2 ? 0 : r3 + 1;
+    ra2 ^= 1;
+    rb = rb + 1 == L::kBSlots ? 0 : rb + 1;
     // second half of k-step 3 of stage kt-1, reading the first fragments of
     // stage kt
-    kstep(fa[1], fb[1], H, TM, fa[0], fb[0], ring_slot_a<FAR_B>(r2, r3), ring_slot_b<FAR_B>(r2, r3), 0,
-          true, 1, kt, 0, 0, 0, 0);
+    kstep(fa[1], fb[1], H, TM, fa[0], fb[0], ra2, rb, 0, true, 1, kt, 0, 0, 0, 0);
     body(kt);
   }
   kstep(fa[1], fb[1], H, TM, fa[0], fb[0], 0, 0, 0, false, 1, 0, 0, 0, 0, 0);
@@ -1284,27 +1272,23 @@ struct RegPlan {
 // compute unit, each taking tiles from work queues until they are empty, so
 // no block waits on a second wave of launches.
 //
-// The tiles are the 1-D tile space of the plan (full 256-row tiles, then
-// 64-row tail tiles; the plan has no extended tiles, ext_rows = 0).  Its
-// first full tiles (a multiple of 8) are split into 8 equal contiguous runs
-// of the patch order, one per XCD: block b sits on XCD b % 8 (blocks are
-// dealt to the XCDs round-robin) and takes tiles from queue[b % 8], so one
-// XCD's compute units work through neighbouring patches and share their
-// panels in that XCD's L2.  A block whose run is used up takes the other
-// runs' remaining tiles, then queue[8]: the leftover full tiles and the
-// tail tiles.  Counters are bumped by one lane with a global atomic; they
-// start at zero (the plan kernel clears them).
+// The tiles are the 1-D tile space of the plan (full tiles, then tail
+// tiles).  Its first full tiles (a multiple of 8) are split into 8 equal
+// contiguous runs of the patch order, one per XCD: block b sits on XCD b % 8
+// (blocks are dealt to the XCDs round-robin) and takes tiles from
+// queue[b % 8], so one XCD's compute units work through neighbouring patches
+// and share their panels in that XCD's L2.  A block whose run is used up
+// takes the other runs' remaining tiles, then queue[8]: the leftover full
+// tiles and the tail tiles.  Counters are bumped by one lane with a global
+// atomic; they start at zero (the plan kernel clears them).
 //
 // Thread 0 keeps the queue state in registers and reserves its next
-// position in the own run one tile ahead.  The claimed tile goes to the
-// other waves through one word of the far ring's third slot, which the
-// loads first write during stage 0 of the tile, after every wave has read
-// it.  After the main loop of a tile, the block claims and decodes the next
-// one and issues its first loads, which are then in flight during the
-// current tile's epilogue.
-template <int EPI, bool FAR_B, int NW>
-__global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArgs ga) {
-  __shared__ u32x4 pool[kSlots][kSlotU4];
+// position in the own run one tile ahead.  After the main loop of a tile,
+// the block claims and decodes the next one and issues its first loads,
+// which are then in flight during the current tile's epilogue.
+template <int EPI>
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga) {
+  __shared__ u32x4 pool[kPoolU4];
   constexpr int BNH = gated<EPI>() ? 128 : 256;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1318,7 +1302,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArg
     pl.til[r] = in ? a.tiles[i] : 0;
     pl.tal[r] = in ? a.tails[i] : 0;
   }
-  int32_t* s_next = reinterpret_cast<int32_t*>(&pool[FAR_B ? 4 : 2][0]);
+  int32_t* s_next = reinterpret_cast<int32_t*>(&pool[kNextU4]);
   const int ntiles = (a.Ndim + BNH - 1) / BNH;
   const int real = full_tiles_total_p(a, pl, 256) * ntiles;
   const int total = real + tail_tiles_total_p(a, pl, 256) * ntiles;
@@ -1347,6 +1331,8 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArg
     pending = cur == 0 ? atomicAdd(&queue[xcd], 1) : -1;
     return h;
   };
+  // a tile of the 1-D space: coordinates and height class (256, 64); false
+  // when it holds no rows (block-uniform results)
   auto decode = [&](int h, int& g, int& row0, int& rows, int& by, int& bm) -> bool {
     bool ok = true;
     if (h < real) {
@@ -1371,7 +1357,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArg
   bool work = h >= 0 && decode(h, g, row0, rows, by, bm);
   bool issued = false;
   const int nk = a.Kdim / BK;
-  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0][0];
+  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0];
   while (h >= 0) {
     int h_next = -1, g2 = 0, r2 = 0, n2 = 0, y2 = 0, bm2 = 0;
     bool next_work = false;
@@ -1386,11 +1372,9 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArg
         asm volatile("" : "+v"(t));
         const int w = __builtin_amdgcn_readfirstlane(t >> 6);
         if (bm2 == 256)
-          ring_stage0<EPI, 256, FAR_B, NW>(a, RingAddr<EPI, 256, NW>(a, g2, r2, n2, y2, w, t & 63), nk,
-                                           pool_lds);
+          ring_stage0<EPI, 256>(a, RingAddr<EPI, 256>(a, g2, r2, n2, y2, w, t & 63), nk, pool_lds);
         else
-          ring_stage0<EPI, kTailRows, FAR_B, NW>(a, RingAddr<EPI, kTailRows, NW>(a, g2, r2, n2, y2, w, t & 63),
-                                                 nk, pool_lds);
+          ring_stage0<EPI, kTailRows>(a, RingAddr<EPI, kTailRows>(a, g2, r2, n2, y2, w, t & 63), nk, pool_lds);
       }
     };
     if (!work) {
@@ -1399,9 +1383,9 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_ring_kernel(GemmArg
       __syncthreads();
       pre();
     } else if (bm == 256) {
-      ring_tile<EPI, 256, FAR_B, NW>(a, g, row0, rows, by, pool, issued, pre);
+      ring_tile<EPI, 256>(a, g, row0, rows, by, pool, issued, pre);
     } else {
-      ring_tile<EPI, kTailRows, FAR_B, NW>(a, g, row0, rows, by, pool, issued, pre);
+      ring_tile<EPI, kTailRows>(a, g, row0, rows, by, pool, issued, pre);
     }
     issued = next_work;
     work = next_work;
@@ -1912,8 +1896,8 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
     int blocks = cu_count() / 8 * 8;
     if (blocks < 8) blocks = 8;
     // the weights are the streamed operand: they run two stages ahead
-    hipLaunchKernelGGL((grouped_gemm_bf16_ring_kernel<kFwd ? EPI : EPI_NONE, true, 8>), dim3(blocks),
-                       dim3(512), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_ring_kernel<kFwd ? EPI : EPI_NONE>), dim3(blocks), dim3(512), 0, s,
+                       a);
   } else if (bm == 256)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
   else if (bm == 128) {

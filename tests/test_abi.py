@@ -44,6 +44,7 @@ def test_reference_library_exports_its_probe():
     path = os.path.join(ROOT, "sparse_mixture_experts_42_amd", "libmoe_ref.so")
     L = ctypes.CDLL(path)
     assert hasattr(L, "moe_ref_mfma")
+    assert hasattr(L, "moe_ref_mfma_data")
 
 
 def test_status_strings():
