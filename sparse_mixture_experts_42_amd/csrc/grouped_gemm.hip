@@ -1021,6 +1021,12 @@ __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t lds, uint32_t vo
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
+// The same load marked non-temporal: for data read once (a decode-sized
+// layer's expert weights), streamed past the caches.
+__device__ __forceinline__ void lds_load16_nt(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
 
 // Pool layout: two A slots, then three B slots, 32 KB each (256 tile rows
 // of 128 bytes).
@@ -1041,9 +1047,9 @@ constexpr int kNextU4 = kPoolU4 - 1;
 // gemm_tile): load i of wave w fills tile rows 8q .. 8q+7, q = w*AI + i (A)
 // or w*BI + i (B), lane l row 8q + l/8 at 16-byte slot l%8, which holds
 // logical chunk (l%8) ^ ((8q + l/8) >> 1 & 7).
-template <int EPI, int BM>
+template <int EPI, int BM, int NW = 8>
 struct RingAddr {
-  static constexpr int NW = 8, BN = 256, AI = BM / 8 / NW, BI = BN / 8 / NW;
+  static constexpr int BN = 256, AI = BM / 8 / NW, BI = BN / 8 / NW;
   static constexpr int BNH = gated<EPI>() ? BN / 2 : BN;
   const uint16_t* a_base;
   uint32_t a_bytes, a_voff_e, a_voff_o, a_step;
@@ -1411,6 +1417,119 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_small_kernel(GemmArgs a
   int g, row0, rows, by;
   find_tile_2d(a, 32, ntiles, h, real, g, row0, rows, by);
   gemm_tile<EPI, 32, 256, 1, 4, 32 * 8, 256 * 8, BT>(a, g, row0, rows, by, sA, sB);
+}
+
+
+// -------------------------------------------- streaming GEMM, small groups
+// Groups of a few rows (decode-sized batches).  These GEMMs stream the
+// touched experts' weights from HBM once and do little arithmetic per
+// byte; what limits them is how evenly the weight bytes spread over the
+// CUs and how many are in flight.  Each block is one wave and one tile of
+// 32 rows x 64 weight rows (SwiGLU: 32 gate + 32 up rows, 32 output
+// columns), so a layer has four times the tiles of 256-row weight panels
+// and the last round of tiles is short.  The LDS holds kStreamSlots stages
+// of 4 KB of activation rows and 8 KB of weight rows; both are loaded
+// kStreamSlots - 1 stages ahead (36 loads of 1 KB in flight per wave), three
+// blocks per CU.  The weights are read once, so their loads are
+// non-temporal.  Each output element sums its k in the same order as the
+// 32-row tiles of gemm_tile.
+constexpr int kStreamSlots = 4;
+
+template <int EPI>
+__global__ __launch_bounds__(64) void grouped_gemm_bf16_stream_kernel(GemmArgs a) {
+  constexpr int BM = 32, BN = 64, NS = kStreamSlots, D = NS - 1;
+  constexpr bool GATED = gated<EPI>();
+  constexpr int BNH = GATED ? BN / 2 : BN;             // output columns per tile
+  constexpr int TN = 2;                                // 32x32 accumulators
+  constexpr uint32_t ASLOT = BM * 128, BSLOT = BN * 128;
+  constexpr int AI = BM / 8, BI = BN / 8, NL = AI + BI;   // 1-KB loads per stage
+  static_assert((D - 1) * NL <= 63, "vmcnt counts at most 63 loads");
+  __shared__ u32x4 pool[NS * (ASLOT + BSLOT) / 16];
+  const int ntiles = (a.Ndim + BNH - 1) / BNH;
+  const int real = full_tiles_total(a, BM) * ntiles;
+  const int h = blockIdx.x;
+  if (h >= real) return;
+  int g, row0, rows, by;
+  find_tile_2d(a, BM, ntiles, h, real, g, row0, rows, by);
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  by = __builtin_amdgcn_readfirstlane(by);
+  const int lane = threadIdx.x & 63;
+  const int n0 = by * BNH;
+  // load i fills tile rows 8i .. 8i+7: lane l row 8i + l/8 at 16-byte slot
+  // l%8, which holds logical chunk (l%8) ^ ((8i + l/8) >> 1 & 7)
+  const int lrow = lane >> 3;
+  const int ce = (lane & 7) ^ (lrow >> 1), co = (lane & 7) ^ (4 + (lrow >> 1));
+  const uint16_t* a_base = static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda;
+  const uint32_t a_bytes = (uint32_t)rows * a.lda * 2;
+  const uint32_t a_voff_e = (uint32_t)(lrow * a.lda + ce * 8) * 2, a_voff_o = (uint32_t)(lrow * a.lda + co * 8) * 2;
+  // B rows: gated, rows 0-31 the gate rows and 32-63 the up rows of output
+  // columns n0 .. n0+31; plain, rows 0-63 of columns n0 .. n0+63
+  const int b_valid = a.Ndim - n0 < BNH ? a.Ndim - n0 : BNH;
+  const uint16_t* b0 = static_cast<const uint16_t*>(a.B0) + (size_t)g * a.b_group_stride + (size_t)n0 * a.ldb;
+  const uint16_t* b1 = GATED ? static_cast<const uint16_t*>(a.B1) + (size_t)g * a.b_group_stride +
+                                   (size_t)n0 * a.ldb
+                             : b0;
+  const uint32_t b_bytes = (uint32_t)b_valid * a.ldb * 2;
+  const uint32_t b_voff_e = (uint32_t)(lrow * a.ldb + ce * 8) * 2, b_voff_o = (uint32_t)(lrow * a.ldb + co * 8) * 2;
+  const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0];
+  auto a_off = [](int s) { return (uint32_t)s * ASLOT; };
+  auto b_off = [](int s) { return NS * ASLOT + (uint32_t)s * BSLOT; };
+  const int nk = a.Kdim / BK;
+  // stage kt into slot kt % NS: A rows, then B rows
+  auto issue = [&](int kt) {
+    const int s = kt % NS;
+    const bool live = kt < nk;
+    const uint32_t ka = (uint32_t)kt * 128u;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      lds_load16(rsrc_words(a_base, live ? a_bytes : 0u), pool_lds + a_off(s) + (uint32_t)i * 1024u,
+                 ((i & 1) ? a_voff_o : a_voff_e) + (uint32_t)i * 8u * a.lda * 2u + ka);
+    const int kb = live ? kt * 64 : 0;
+    const int seg = a.kseg == a.Kdim ? 0 : kb / a.kseg;
+    const uint32_t koff = (uint32_t)(kb - seg * a.kseg) * 2u;
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      // gated: loads 0-3 the gate rows, 4-7 the up rows (row 8i - 32)
+      const bool up = GATED && i >= BI / 2;
+      const int r8 = up ? i - BI / 2 : i;
+      const uint16_t* base = (up ? b1 : b0) + (size_t)seg * a.kseg_stride;
+      lds_load16_nt(rsrc_words(base, live ? b_bytes : 0u), pool_lds + b_off(s) + (uint32_t)i * 1024u,
+                    ((i & 1) ? b_voff_o : b_voff_e) + (uint32_t)r8 * 8u * a.ldb * 2u + koff);
+    }
+  };
+  f32x16 acc[1][TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[0][j][v] = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < D; ++kt) issue(kt);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed; the D - 1 stages after it may still be in flight.  One
+    // wave: its own program order keeps the slot of stage kt + D, which stage
+    // kt - 1 used, free of reads
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"((D - 1) * NL) : "memory");
+    issue(kt + D);
+    const int s = kt % NS;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      const bf16x8 fa = __builtin_bit_cast(bf16x8, pool[a_off(s) / 16 + swz(lane & 31, c)]);
+      bf16x8 fb[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[j] = __builtin_bit_cast(bf16x8, pool[b_off(s) / 16 + swz(32 * j + (lane & 31), c)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[0][j], 0, 0, 0);
+    }
+  }
+  // the empty loads of the last stages still write the pool: drain them
+  // before the block ends and another block takes this LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_forward_tile<EPI, 1, TN, BM, BN>(a, acc, row0, rows, n0, 0, 0, lane);
 }
 
 // Groups of a few hundred rows (e.g. a Switch-shaped layer with capacity
@@ -1907,6 +2026,9 @@ hipError_t launch_bf16(const GemmArgs& a, int bm, int mtiles, hipStream_t s) {
     else
       hipLaunchKernelGGL((grouped_gemm_bf16_mid_kernel<EPI, BT>), grid, dim3(512), 0, s, a);
   }
+  else if (kFwd)
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<kFwd ? EPI : EPI_NONE>),
+                       dim3(mtiles * ((a.Ndim + BNH / 4 - 1) / (BNH / 4))), dim3(64), 0, s, a);
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_small_kernel<EPI, BT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
