@@ -23,7 +23,8 @@ namespace {
 // accumulators of GEMM-1 with the activation gradient dA = dY W_down as the
 // extra input D: they write the activation a (to C, for dW_down) and the
 // pre-activation gradients (to C2, [rows][2*Ndim]: dG then dU; ReLU: dG).
-enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_RELU_BWD = 4 };
+// EPI_NONE_T stores the plain product transposed (the weight gradients).
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_RELU_BWD = 4, EPI_NONE_T = 5 };
 
 template <int EPI>
 constexpr bool gated() { return EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD; }
@@ -60,6 +61,10 @@ struct GemmArgs {
   // null
   float* P;
   int ldp;
+  // EPI_NONE_T: output column n < ct_split is row n of C, column n >= ct_split
+  // row n - ct_split of C2 (both with leading dimension ldc); output rows
+  // past M are not stored
+  int ct_split;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -423,6 +428,56 @@ __device__ __forceinline__ void store_forward_tile(const GemmArgs& a, f32x16 (&a
   }
 }
 
+// Transposed store of a plain tile: output element (m, n) goes to row n of
+// C (n < ct_split) or of C2 (row n - ct_split), at column m.  A lane holds
+// four consecutive m of one n in each group of four accumulator values.
+// Stored straight from the accumulators, each store instruction would touch
+// 32 rows at 16 bytes each; instead each wave passes its WTN x WTM block
+// through its own WTN x WTM x 2-byte LDS region (bf16, rows n, the 16-byte
+// chunk c of row n at slot c ^ (n % chunks)), then stores whole 16-byte
+// pieces, a wave instruction covering 64 * 16 / (2 WTM) rows contiguously.
+template <int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_transposed_tile(const GemmArgs& a, f32x16 (&acc)[TM][TN], int row0,
+                                                      int rows, int n0, int wm, int wn, int lane,
+                                                      u32x4* region) {
+  constexpr int CH = WTM / 8;                 // 16-byte chunks per LDS row
+  static_assert(CH == 16 && WTN % 32 == 0, "128 m per wave");
+  uint32_t* r32 = reinterpret_cast<uint32_t*>(region);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int nl = 32 * j + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * i + q;              // m = 32 i + 8 q + 4 (lane / 32) + 0..3
+        f32x2 lo, hi;
+        lo[0] = acc[i][j][4 * q];
+        lo[1] = acc[i][j][4 * q + 1];
+        hi[0] = acc[i][j][4 * q + 2];
+        hi[1] = acc[i][j][4 * q + 3];
+        u32x2 w;
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+        *reinterpret_cast<u32x2*>(r32 + (nl * CH + (c ^ (nl % CH))) * 4 + 2 * (lane >> 5)) = w;
+      }
+  }
+  // the wave reads back what it wrote: 16 lanes a row, 4 rows an instruction
+  const int m0 = row0 + wm * WTM;
+  const int c = lane & 15;
+  const int m = m0 + 8 * c;
+#pragma unroll
+  for (int it = 0; it < WTN / 4; ++it) {
+    const int nl = 4 * it + (lane >> 4);
+    const u32x4 v = region[nl * CH + (c ^ (nl % CH))];
+    const int n = n0 + wn * WTN + nl;
+    if (n >= a.Ndim || m >= row0 + rows) continue;
+    uint16_t* row = n < a.ct_split ? static_cast<uint16_t*>(a.C) + (size_t)n * a.ldc
+                                   : static_cast<uint16_t*>(a.C2) + (size_t)(n - a.ct_split) * a.ldc;
+    *reinterpret_cast<u32x4*>(row + m) = v;
+  }
+}
+
 // PIPE tiles may continue a persistent block's previous tile: stage 0 uses
 // LDS buffer b0 (stage k buffer (k + b0) & 1), `issued` says its loads are
 // already in flight, and pre(buf) runs after the main loop, once every wave
@@ -443,7 +498,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   static_assert(AI >= 1 && BI >= 1, "every wave loads A and B rows");
   static_assert(!GATED || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
   static_assert(SAN >= BM * 8 && SBN >= BN * 8, "LDS stages hold the tile");
-  static_assert(!BT || (EPI == EPI_NONE && BN == 256), "k-major B: plain epilogue, 256 columns");
+  static_assert(!BT || ((EPI == EPI_NONE || EPI == EPI_NONE_T) && BN == 256),
+                "k-major B: plain epilogue, 256 columns");
   constexpr int BNH = GATED ? BN / 2 : BN;        // output columns per tile
 
   // In a persistent caller's loop (which passes a Pre step) the thread index
@@ -852,6 +908,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
   }
   if constexpr (PIPE && (EPI == EPI_NONE || EPI == EPI_SWIGLU || EPI == EPI_RELU)) {
     store_forward_tile<EPI, TM, TN, WTM, WTN>(a, acc, row0, rows, n0, wm, wn, lane);
+    return;
+  }
+  if constexpr (EPI == EPI_NONE_T) {
+    // every wave is past its last fragment read before any region is written
+    __syncthreads();
+    constexpr int RU4 = WTM * WTN * 2 / 16;   // 16-byte units per region
+    constexpr int NA = 2 * SAN / RU4;         // regions in sA
+    static_assert(NA >= NW || (NW - NA) * RU4 <= 2 * SBN, "a region per wave");
+    u32x4* region = wave < NA ? &sA[0][0] + wave * RU4 : &sB[0][0] + (wave - NA) * RU4;
+    store_transposed_tile<TM, TN, WTM, WTN>(a, acc, row0, rows, n0, wm, wn, lane, region);
     return;
   }
   if constexpr (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) {
@@ -1825,11 +1891,18 @@ struct KGemmArgs {
   void* C;                 // group g: [M][ldc] at C + g * c_group_stride
   int ldc;
   size_t c_group_stride;
+  // transposed output (EPI_NONE_T): group g's output column n < ct_split is
+  // row n of C + g * c_group_stride, column n >= ct_split row n - ct_split of
+  // C2 + g * c_group_stride; each row holds the M outputs of its column
+  void* C2;
+  int ct_split;
 };
 
 // One block per (group, 256 x 256 output tile), in the XCD-contiguous,
 // patch-rotated order of the forward GEMMs.  A group without rows writes
-// zeros.
+// zeros.  EPI is EPI_NONE (output [M][N]) or EPI_NONE_T (output stored
+// transposed, [N][M], split at ct_split between C and C2).
+template <int EPI>
 __global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
   __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
   __shared__ u32x4 sB[2][256 * 8];
@@ -1848,12 +1921,22 @@ __global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
   const int kg = k.offsets[g + 1] - k.offsets[g];
   const int kp = k.kpad[g + 1] - k.kpad[g];
   uint16_t* C = static_cast<uint16_t*>(k.C) + (size_t)g * k.c_group_stride;
+  uint16_t* C2 = EPI == EPI_NONE_T ? static_cast<uint16_t*>(k.C2) + (size_t)g * k.c_group_stride : nullptr;
   const int row0 = mt * 256, rows = k.M - row0 < 256 ? k.M - row0 : 256, n0 = nt * 256;
   if (kp == 0) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int id = threadIdx.x; id < 256 * 32; id += 512) {
-      const int r = id >> 5, col = n0 + 8 * (id & 31);
-      if (r < rows && col < k.N) *reinterpret_cast<u32x4*>(C + (size_t)(row0 + r) * k.ldc + col) = z;
+      const int r = id >> 5, col = 8 * (id & 31);
+      if constexpr (EPI == EPI_NONE_T) {
+        // output column n0 + r: M values from row0 + col
+        const int n = n0 + r;
+        if (n < k.N && col < rows) {
+          uint16_t* dst = n < k.ct_split ? C + (size_t)n * k.ldc : C2 + (size_t)(n - k.ct_split) * k.ldc;
+          *reinterpret_cast<u32x4*>(dst + row0 + col) = z;
+        }
+      } else if (r < rows && n0 + col < k.N) {
+        *reinterpret_cast<u32x4*>(C + (size_t)(row0 + r) * k.ldc + n0 + col) = z;
+      }
     }
     return;
   }
@@ -1867,10 +1950,12 @@ __global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
   a.Kdim = kp;
   a.Ndim = k.N;
   a.C = C;
+  a.C2 = C2;
+  a.ct_split = k.ct_split;
   a.ldc = k.ldc;
   a.G = 1;
   a.M = k.M;
-  gemm_tile<EPI_NONE, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, true, true>(a, 0, row0, rows, nt, sA, sB);
+  gemm_tile<EPI, 256, 256, 2, 4, (256 + kExtRows) * 8, 256 * 8, true, true>(a, 0, row0, rows, nt, sA, sB);
 }
 
 // --------------------------------------------------------------- fp32
@@ -2309,13 +2394,18 @@ hipError_t run_wgrad(const WgradArgs& w, hipStream_t s) {
   return hipGetLastError();
 }
 
+// C2 == null: output [M][ldc] per group; else stored transposed, output
+// column n < ct_split to row n of C, the others to row n - ct_split of C2
 hipError_t run_kgemm(const void* AT, int ldat, const void* B, int ldb, const int32_t* offsets,
                      const int32_t* kpad, int G, int M, int N, void* C, int ldc, size_t c_stride,
-                     hipStream_t s) {
-  KGemmArgs k{AT, ldat, B, ldb, offsets, kpad, G, M, N, C, ldc, c_stride};
+                     hipStream_t s, void* C2 = nullptr, int ct_split = 0) {
+  KGemmArgs k{AT, ldat, B, ldb, offsets, kpad, G, M, N, C, ldc, c_stride, C2, ct_split};
   const long long blocks = (long long)G * ((M + 255) / 256) * ((N + 255) / 256);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_kgemm_kernel, dim3((unsigned)blocks), dim3(512), 0, s, k);
+  if (C2 != nullptr)
+    hipLaunchKernelGGL(grouped_kgemm_kernel<EPI_NONE_T>, dim3((unsigned)blocks), dim3(512), 0, s, k);
+  else
+    hipLaunchKernelGGL(grouped_kgemm_kernel<EPI_NONE>, dim3((unsigned)blocks), dim3(512), 0, s, k);
   return hipGetLastError();
 }
 
@@ -2410,22 +2500,18 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   // weight gradients
   const int gu = swiglu ? 2 : 1;
   if (b.kpad != nullptr) {
-    // transposed form: dW_down = dY^T a, [dW_gate; dW_up] = [dG dU]^T X
+    // transposed form: dW_down = dY^T a from dY transposed
     hipLaunchKernelGGL(kpad_kernel, dim3(1), dim3(64), 0, s, b.offsets, p.N, b.kpad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = run_transpose(b.dy_perm, d, d, b.offsets, b.kpad, p.N, b.dyT, b.ldt, s)) != hipSuccess) return e;
     if ((e = run_kgemm(b.dyT, b.ldt, b.act, dff, b.offsets, b.kpad, p.N, d, dff, b.dw_down, dff,
                        (size_t)d * dff, s)) != hipSuccess)
       return e;
-    if ((e = run_transpose(b.dgu, gu * dff, gu * dff, b.offsets, b.kpad, p.N, b.dguT, b.ldt, s)) !=
-        hipSuccess)
-      return e;
-    if ((e = run_kgemm(b.dguT, b.ldt, b.x_perm, d, b.offsets, b.kpad, p.N, dff, d, b.dw_gate, d,
-                       (size_t)dff * d, s)) != hipSuccess)
-      return e;
-    if (swiglu &&
-        (e = run_kgemm(static_cast<const uint16_t*>(b.dguT) + (size_t)dff * b.ldt, b.ldt, b.x_perm, d,
-                       b.offsets, b.kpad, p.N, dff, d, b.dw_up, d, (size_t)dff * d, s)) != hipSuccess)
+    // [dW_gate; dW_up]^T = X^T [dG dU]: X transposed (d columns) rather than
+    // [dG dU] (2 d_ff columns), the product stored transposed, split at d_ff
+    if ((e = run_transpose(b.x_perm, d, d, b.offsets, b.kpad, p.N, b.xT, b.ldt, s)) != hipSuccess) return e;
+    if ((e = run_kgemm(b.xT, b.ldt, b.dgu, gu * dff, b.offsets, b.kpad, p.N, d, gu * dff, b.dw_gate, d,
+                       (size_t)dff * d, s, swiglu ? b.dw_up : b.dw_gate, dff)) != hipSuccess)
       return e;
   } else {
     if ((e = run_wgrad(wgrad_args(b.dy_perm, d, b.act, dff, b.offsets, p.N, 0, d, dff, b.dw_down,

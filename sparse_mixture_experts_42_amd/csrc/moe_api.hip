@@ -105,7 +105,7 @@ BwdWorkspace bwd_workspace_layout(const moe_problem_t& p) {
   if (w.ldt > 0) {
     w.kpad = take((N + 1) * 4);
     w.dyT = take(d * (size_t)w.ldt * es);
-    w.dguT = take(gu * dff * (size_t)w.ldt * es);
+    w.xT = take(d * (size_t)w.ldt * es);
   }
   w.total = off;
   return w;
@@ -116,7 +116,10 @@ int wgrad_transposed_ld(const moe_problem_t& p) {
   if (rows < 512LL * p.N) return 0;            // short groups: the direct kernel
   const long long ld = (rows + 63LL * p.N + 63) / 64 * 64;
   // a 256-row tile of the transposed operand is addressed through one buffer
-  // descriptor, whose size is 32-bit: 256 * ld * 2 bytes stays below 2 GiB
+  // descriptor, whose size is 32-bit: 256 * ld * 2 bytes stays below 2 GiB;
+  // so is each group's k-major operand, at most rows x 2 d_ff elements
+  const long long gu = p.act == MOE_ACT_SWIGLU ? 2 : 1;
+  if (rows * gu * p.d_ff * 2 >= (1LL << 31)) return 0;
   return ld <= (1LL << 22) ? (int)ld : 0;
 }
 
@@ -584,7 +587,7 @@ int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_
   if (L.ldt > 0) {
     b.kpad = reinterpret_cast<int32_t*>(ws_at(ws, L.kpad));
     b.dyT = ws_at(ws, L.dyT);
-    b.dguT = ws_at(ws, L.dguT);
+    b.xT = ws_at(ws, L.xT);
     b.ldt = L.ldt;
   }
   if (shared) {

@@ -122,7 +122,7 @@ struct FfnBwdBuffers {
   // weight gradients in transposed form (null kpad: the direct k-major kernel)
   int32_t* kpad;            // [N+1] workspace
   void* dyT;                // [d][ldt] workspace
-  void* dguT;               // [2*d_ff][ldt] workspace (ReLU: [d_ff][ldt])
+  void* xT;                 // [d][ldt] workspace
   int ldt;
   // shared experts (n_shared > 0)
   const void* u;            // [T][d]
@@ -170,7 +170,7 @@ struct BwdWorkspace {
   size_t dx_shared;    // elem [T][d]
   size_t kpad;         // int32 [N+1]         (transposed weight gradients only)
   size_t dyT;          // elem [d][ldt]
-  size_t dguT;         // elem [2*d_ff][ldt]  (ReLU: d_ff)
+  size_t xT;           // elem [d][ldt]
   int ldt;             // 0: weight gradients by the direct k-major kernel
   size_t total;
 };
