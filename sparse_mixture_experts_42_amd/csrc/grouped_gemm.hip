@@ -571,8 +571,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       // segment, columns n0 .. n0+255
       const uint16_t* base = static_cast<const uint16_t*>(seg == 0 ? a.B0 : a.B1) +
                              (size_t)g * a.b_group_stride + n0;
+      // the descriptor ends at column Ndim of the segment's last row, so a
+      // group whose columns start inside a wider row reads nothing past them
       const __amdgpu_buffer_rsrc_t rBT =
-          make_rsrc(base, (uint32_t)((size_t)a.kseg * a.ldb - n0) * 2u);
+          make_rsrc(base, (uint32_t)((size_t)(a.kseg - 1) * a.ldb + a.Ndim - n0) * 2u);
       const uint32_t krow = (uint32_t)(kb - seg * a.kseg) * (uint32_t)a.ldb * 2u;
 #pragma unroll
       for (int i = 0; i < BI; ++i)
@@ -1844,22 +1846,30 @@ __global__ void kpad_kernel(const int32_t* offsets, int G, int32_t* kpad) {
 
 // S [rows][C] (leading dimension lds) -> T [C][ldt] (bf16): row r of group
 // g becomes column kpad[g] + r - offsets[g]; each group's padding columns
-// are zero.  One block per 64 x 64 tile of T; blocks past kpad[G] exit.
+// are zero.  With offsets null, the S rows 0 .. rows1-1 are one group at
+// column 0, zero-filled up to ldt.  One block per 64 x 64 tile of T; blocks
+// past the last column exit.
 __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint16_t* S, int lds, int C,
                                                                const int32_t* offsets,
                                                                const int32_t* kpad, int G,
-                                                               uint16_t* T, int ldt) {
+                                                               uint16_t* T, int ldt, int rows1) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][64 + 8];   // 144-byte rows
   const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  if (p0 >= kpad[G]) return;
-  int lo = 0, hi = G;                      // kpad[lo] <= p0 < kpad[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (kpad[mid] <= p0) lo = mid;
-    else hi = mid;
+  int r0, nrows;                           // source rows left in the group
+  if (offsets == nullptr) {
+    r0 = p0;
+    nrows = rows1 - p0;
+  } else {
+    if (p0 >= kpad[G]) return;
+    int lo = 0, hi = G;                    // kpad[lo] <= p0 < kpad[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (kpad[mid] <= p0) lo = mid;
+      else hi = mid;
+    }
+    r0 = offsets[lo] + (p0 - kpad[lo]);
+    nrows = offsets[lo + 1] - r0;
   }
-  const int r0 = offsets[lo] + (p0 - kpad[lo]);
-  const int nrows = offsets[lo + 1] - r0;  // source rows left in the group (> 0)
 #pragma unroll
   for (int q = threadIdx.x; q < 512; q += 256) {
     const int r = q >> 3, cc = (q & 7) * 8;
@@ -1880,13 +1890,17 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint16_t* S
   }
 }
 
-struct KGemmArgs {
-  const void* AT;          // [M][ldat]: the transposed operand
+// One weight-gradient problem: per group g, C_g = AT_g B_g reduced over the
+// group's rows, with AT the transposed operand and B read k-major.
+struct KGemmSet {
+  const void* AT;          // [M][ldat]: group g's k columns from kpad[g]
   int ldat;
-  const void* B;           // [rows][ldb]: rows offsets[g] .. of group g, k-major
+  const void* B;           // [rows][ldb]: rows offsets[g] .. of group g
   int ldb;
-  const int32_t* offsets;  // [G+1] group rows
-  const int32_t* kpad;     // [G+1] group columns in AT
+  const int32_t* offsets;  // [G+1] group rows; or null: every group reduces
+  const int32_t* kpad;     // over rows 0 .. rows-1, AT columns from 0, and
+  int rows;                // takes B columns from g * b_group_cols
+  size_t b_group_cols;
   int G, M, N;
   void* C;                 // group g: [M][ldc] at C + g * c_group_stride
   int ldc;
@@ -1898,17 +1912,33 @@ struct KGemmArgs {
   int ct_split;
 };
 
-// One block per (group, 256 x 256 output tile), in the XCD-contiguous,
-// patch-rotated order of the forward GEMMs.  A group without rows writes
+// Blocks 0 .. head-1 take the tiles of set[0] (head: its tile count rounded
+// up to a multiple of 8, 0 for none), the rest those of set[1].
+struct KGemmArgs {
+  KGemmSet set[2];
+  int head;
+};
+
+__host__ __device__ inline int kgemm_tiles(const KGemmSet& k) {
+  return k.G * ((k.M + 255) / 256) * ((k.N + 255) / 256);
+}
+
+// One block per (set, group, 256 x 256 output tile).  Within a set the tiles
+// run in the XCD-contiguous, patch-rotated order of the forward GEMMs; set 0
+// (a few long reductions, e.g. shared experts over every token) comes
+// first, so its blocks start at once, spread over the XCDs, while set 1's
+// shorter tiles fill the other compute units.  A group without rows writes
 // zeros.  EPI is EPI_NONE (output [M][N]) or EPI_NONE_T (output stored
 // transposed, [N][M], split at ct_split between C and C2).
 template <int EPI>
-__global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
+__global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs ka) {
   __shared__ u32x4 sA[2][(256 + kExtRows) * 8];
   __shared__ u32x4 sB[2][256 * 8];
+  const bool first = (int)blockIdx.x < ka.head;
+  const KGemmSet k = first ? ka.set[0] : ka.set[1];
   const int mtn = (k.M + 255) / 256, ntn = (k.N + 255) / 256;
   const int per = mtn * ntn, total = k.G * per;
-  const int h = blockIdx.x;
+  const int h = first ? (int)blockIdx.x : (int)blockIdx.x - ka.head;   // head % 8 == 0
   if (h >= total) return;
   const int full = total - total % 8;
   const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
@@ -1918,8 +1948,10 @@ __global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
   const int nbe = ntn - nb * kPatchN < kPatchN ? ntn - nb * kPatchN : kPatchN;
   const int mt = (rem / nbe + nb) % mtn;
   const int nt = nb * kPatchN + rem % nbe;
-  const int kg = k.offsets[g + 1] - k.offsets[g];
-  const int kp = k.kpad[g + 1] - k.kpad[g];
+  const int r0 = k.offsets ? k.offsets[g] : 0;
+  const int kg = k.offsets ? k.offsets[g + 1] - r0 : k.rows;
+  const int kc = k.offsets ? k.kpad[g] : 0;
+  const int kp = k.offsets ? k.kpad[g + 1] - kc : (k.rows + BK - 1) / BK * BK;
   uint16_t* C = static_cast<uint16_t*>(k.C) + (size_t)g * k.c_group_stride;
   uint16_t* C2 = EPI == EPI_NONE_T ? static_cast<uint16_t*>(k.C2) + (size_t)g * k.c_group_stride : nullptr;
   const int row0 = mt * 256, rows = k.M - row0 < 256 ? k.M - row0 : 256, n0 = nt * 256;
@@ -1941,9 +1973,9 @@ __global__ __launch_bounds__(512) void grouped_kgemm_kernel(KGemmArgs k) {
     return;
   }
   GemmArgs a{};
-  a.A = static_cast<const uint16_t*>(k.AT) + k.kpad[g];
+  a.A = static_cast<const uint16_t*>(k.AT) + kc;
   a.lda = k.ldat;
-  a.B0 = static_cast<const uint16_t*>(k.B) + (size_t)k.offsets[g] * k.ldb;
+  a.B0 = static_cast<const uint16_t*>(k.B) + (size_t)r0 * k.ldb + (k.offsets ? 0 : (size_t)g * k.b_group_cols);
   a.B1 = a.B0;
   a.ldb = k.ldb;
   a.kseg = kg;             // the group's rows: B rows past them read 0
@@ -2394,26 +2426,54 @@ hipError_t run_wgrad(const WgradArgs& w, hipStream_t s) {
   return hipGetLastError();
 }
 
-// C2 == null: output [M][ldc] per group; else stored transposed, output
-// column n < ct_split to row n of C, the others to row n - ct_split of C2
-hipError_t run_kgemm(const void* AT, int ldat, const void* B, int ldb, const int32_t* offsets,
-                     const int32_t* kpad, int G, int M, int N, void* C, int ldc, size_t c_stride,
-                     hipStream_t s, void* C2 = nullptr, int ct_split = 0) {
-  KGemmArgs k{AT, ldat, B, ldb, offsets, kpad, G, M, N, C, ldc, c_stride, C2, ct_split};
-  const long long blocks = (long long)G * ((M + 255) / 256) * ((N + 255) / 256);
+// One launch over set s1 and, when s0 is given, the long tiles of s0 first.
+// s1.C2 == null: plain outputs [M][ldc] per group; else both sets stored
+// transposed, output column n < ct_split to row n of C, the others to row
+// n - ct_split of C2.
+hipError_t run_kgemm(const KGemmSet& s1, const KGemmSet* s0, hipStream_t s) {
+  KGemmArgs k{};
+  k.set[1] = s1;
+  if (s0 != nullptr) {
+    k.set[0] = *s0;
+    k.head = (kgemm_tiles(*s0) + 7) / 8 * 8;
+  }
+  const long long blocks = (long long)k.head + kgemm_tiles(s1);
   if (blocks == 0) return hipSuccess;
-  if (C2 != nullptr)
+  if (s1.C2 != nullptr)
     hipLaunchKernelGGL(grouped_kgemm_kernel<EPI_NONE_T>, dim3((unsigned)blocks), dim3(512), 0, s, k);
   else
     hipLaunchKernelGGL(grouped_kgemm_kernel<EPI_NONE>, dim3((unsigned)blocks), dim3(512), 0, s, k);
   return hipGetLastError();
 }
 
+// the routed experts' set: groups by offsets, AT columns by kpad
+KGemmSet kgemm_set(const void* AT, int ldat, const void* B, int ldb, const int32_t* offsets,
+                   const int32_t* kpad, int G, int M, int N, void* C, int ldc, size_t c_stride,
+                   void* C2 = nullptr, int ct_split = 0) {
+  KGemmSet k{};
+  k.AT = AT;
+  k.ldat = ldat;
+  k.B = B;
+  k.ldb = ldb;
+  k.offsets = offsets;
+  k.kpad = kpad;
+  k.G = G;
+  k.M = M;
+  k.N = N;
+  k.C = C;
+  k.ldc = ldc;
+  k.c_group_stride = c_stride;
+  k.C2 = C2;
+  k.ct_split = ct_split;
+  return k;
+}
+
+// S [rows][C] -> T [C][ldt] per group (offsets null: rows1 rows, one group)
 hipError_t run_transpose(const void* S, int lds, int C, const int32_t* offsets, const int32_t* kpad,
-                         int G, void* T, int ldt, hipStream_t s) {
+                         int G, void* T, int ldt, hipStream_t s, int rows1 = 0) {
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ldt / 64));
   hipLaunchKernelGGL(transpose_groups_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(S),
-                     lds, C, offsets, kpad, G, static_cast<uint16_t*>(T), ldt);
+                     lds, C, offsets, kpad, G, static_cast<uint16_t*>(T), ldt, rows1);
   return hipGetLastError();
 }
 
@@ -2497,22 +2557,109 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   n2.C = b.dx_perm;
   n2.ldc = d;
   if ((e = launch_bf16<EPI_NONE, true>(n2, bm, mtiles_max, s)) != hipSuccess) return e;
-  // weight gradients
   const int gu = swiglu ? 2 : 1;
+  // shared experts' data gradients over all T tokens, dY = d_out
+  const int dffs = p.d_ff_shared, wsw = p.n_shared * dffs;
+  if (p.n_shared > 0) {
+    const int sbm = ffn_row_tile(p.T, 1, true);
+    const int s_tail = sbm == 256 ? kTailRows : 0;
+    const int s_ext = sbm == 256 ? kExtRows : 0;
+    int mt = (p.T + sbm - 1) / sbm;
+    if (s_tail > 0) {
+      int f, t;
+      split_rows(p.T, sbm, s_tail, s_ext, f, t);
+      mt = f + t;
+    }
+    GemmArgs sb{};
+    sb.G = 1;
+    sb.M = p.T;
+    sb.rows_alloc = p.T;
+    sb.tail_rows = s_tail;
+    sb.ext_rows = s_ext;
+    for (int k = 0; k < p.n_shared; ++k) {
+      GemmArgs a1 = sb;
+      a1.A = b.d_out;
+      a1.lda = d;
+      a1.B0 = static_cast<const uint16_t*>(b.ws_down) + (size_t)k * d * dffs;
+      a1.ldb = dffs;
+      a1.Kdim = d;
+      a1.kseg = d;
+      a1.Ndim = dffs;
+      a1.C = static_cast<uint16_t*>(b.dA_s) + (size_t)k * dffs;
+      a1.ldc = wsw;
+      if ((e = launch_bf16<EPI_NONE, true>(a1, sbm, mt, s)) != hipSuccess) return e;
+    }
+    GemmArgs sr = sb;
+    sr.A = b.u;
+    sr.lda = d;
+    sr.B0 = b.ws_gate;
+    sr.B1 = b.ws_up;
+    sr.ldb = d;
+    sr.Kdim = d;
+    sr.kseg = d;
+    sr.Ndim = wsw;
+    sr.C = b.act_s;
+    sr.ldc = wsw;
+    sr.D = b.dA_s;
+    sr.ldd = wsw;
+    sr.C2 = b.dgu_s;
+    sr.ldc2 = gu * wsw;
+    if (b.pre_shared != nullptr)
+      e = run_act_bwd(swiglu, b.pre_shared, gu * wsw, b.dA_s, wsw, nullptr, p.T, wsw, b.act_s, wsw,
+                      b.dgu_s, sr.ldc2, s);
+    else
+      e = run_bwd_epi(sr, swiglu, sbm, mt, s);
+    if (e != hipSuccess) return e;
+    GemmArgs s2 = sb;
+    s2.A = b.dgu_s;
+    s2.lda = gu * wsw;
+    s2.B0 = b.ws_gate;
+    s2.B1 = b.ws_up;
+    s2.ldb = d;
+    s2.Kdim = gu * wsw;
+    s2.kseg = wsw;
+    s2.Ndim = d;
+    s2.C = b.dx_shared;
+    s2.ldc = d;
+    if ((e = launch_bf16<EPI_NONE, true>(s2, sbm, mt, s)) != hipSuccess) return e;
+  }
+
+  // weight gradients
   if (b.kpad != nullptr) {
-    // transposed form: dW_down = dY^T a from dY transposed
+    // transposed form.  dW_down = dY^T a from dY transposed; [dW_gate;
+    // dW_up]^T = X^T [dG dU] from X transposed (d columns rather than the
+    // 2 d_ff of [dG dU]), the product stored transposed, split at d_ff.  The
+    // shared experts' gradients (every token) run in the same launches as a
+    // first set of long tiles: dWs_down[k] = d_out^T a_s[:, k-th d_ff_s
+    // columns], [dWs_gate; dWs_up]^T = u^T [dG_s dU_s].
     hipLaunchKernelGGL(kpad_kernel, dim3(1), dim3(64), 0, s, b.offsets, p.N, b.kpad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const bool sh = p.n_shared > 0 && b.dOT != nullptr;
+    KGemmSet sd{}, sg{};
+    if (sh) {
+      if ((e = run_transpose(b.d_out, d, d, nullptr, nullptr, 1, b.dOT, b.ldts, s, p.T)) != hipSuccess) return e;
+      sd = kgemm_set(b.dOT, b.ldts, b.act_s, wsw, nullptr, nullptr, p.n_shared, d, dffs, b.dws_down, dffs,
+                     (size_t)d * dffs);
+      sd.rows = p.T;
+      sd.b_group_cols = dffs;
+    }
     if ((e = run_transpose(b.dy_perm, d, d, b.offsets, b.kpad, p.N, b.dyT, b.ldt, s)) != hipSuccess) return e;
-    if ((e = run_kgemm(b.dyT, b.ldt, b.act, dff, b.offsets, b.kpad, p.N, d, dff, b.dw_down, dff,
-                       (size_t)d * dff, s)) != hipSuccess)
+    if ((e = run_kgemm(kgemm_set(b.dyT, b.ldt, b.act, dff, b.offsets, b.kpad, p.N, d, dff, b.dw_down, dff,
+                                 (size_t)d * dff),
+                       sh ? &sd : nullptr, s)) != hipSuccess)
       return e;
-    // [dW_gate; dW_up]^T = X^T [dG dU]: X transposed (d columns) rather than
-    // [dG dU] (2 d_ff columns), the product stored transposed, split at d_ff
+    if (sh) {
+      if ((e = run_transpose(b.u, d, d, nullptr, nullptr, 1, b.uT, b.ldts, s, p.T)) != hipSuccess) return e;
+      sg = kgemm_set(b.uT, b.ldts, b.dgu_s, gu * wsw, nullptr, nullptr, 1, d, gu * wsw, b.dws_gate, d, 0,
+                     swiglu ? b.dws_up : b.dws_gate, wsw);
+      sg.rows = p.T;
+    }
     if ((e = run_transpose(b.x_perm, d, d, b.offsets, b.kpad, p.N, b.xT, b.ldt, s)) != hipSuccess) return e;
-    if ((e = run_kgemm(b.xT, b.ldt, b.dgu, gu * dff, b.offsets, b.kpad, p.N, d, gu * dff, b.dw_gate, d,
-                       (size_t)dff * d, s, swiglu ? b.dw_up : b.dw_gate, dff)) != hipSuccess)
+    if ((e = run_kgemm(kgemm_set(b.xT, b.ldt, b.dgu, gu * dff, b.offsets, b.kpad, p.N, d, gu * dff, b.dw_gate,
+                                 d, (size_t)dff * d, swiglu ? b.dw_up : b.dw_gate, dff),
+                       sh ? &sg : nullptr, s)) != hipSuccess)
       return e;
+    if (sh || p.n_shared == 0) return hipSuccess;
   } else {
     if ((e = run_wgrad(wgrad_args(b.dy_perm, d, b.act, dff, b.offsets, p.N, 0, d, dff, b.dw_down,
                                   nullptr, d, (size_t)d * dff, dff, dff, 0),
@@ -2522,78 +2669,15 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
                                   b.dw_gate, b.dw_up, dff, (size_t)dff * d, d, d, 0),
                        s)) != hipSuccess)
       return e;
+    if (p.n_shared == 0) return hipSuccess;
   }
-
-  if (p.n_shared == 0) return hipSuccess;
-  // shared experts over all T tokens, dY = d_out
-  const int dffs = p.d_ff_shared, wsw = p.n_shared * dffs;
-  const int sbm = ffn_row_tile(p.T, 1, true);
-  const int s_tail = sbm == 256 ? kTailRows : 0;
-  const int s_ext = sbm == 256 ? kExtRows : 0;
-  int mt = (p.T + sbm - 1) / sbm;
-  if (s_tail > 0) {
-    int f, t;
-    split_rows(p.T, sbm, s_tail, s_ext, f, t);
-    mt = f + t;
-  }
-  GemmArgs sb{};
-  sb.G = 1;
-  sb.M = p.T;
-  sb.rows_alloc = p.T;
-  sb.tail_rows = s_tail;
-  sb.ext_rows = s_ext;
-  for (int k = 0; k < p.n_shared; ++k) {
-    GemmArgs a1 = sb;
-    a1.A = b.d_out;
-    a1.lda = d;
-    a1.B0 = static_cast<const uint16_t*>(b.ws_down) + (size_t)k * d * dffs;
-    a1.ldb = dffs;
-    a1.Kdim = d;
-    a1.kseg = d;
-    a1.Ndim = dffs;
-    a1.C = static_cast<uint16_t*>(b.dA_s) + (size_t)k * dffs;
-    a1.ldc = wsw;
-    if ((e = launch_bf16<EPI_NONE, true>(a1, sbm, mt, s)) != hipSuccess) return e;
-  }
-  GemmArgs sr = sb;
-  sr.A = b.u;
-  sr.lda = d;
-  sr.B0 = b.ws_gate;
-  sr.B1 = b.ws_up;
-  sr.ldb = d;
-  sr.Kdim = d;
-  sr.kseg = d;
-  sr.Ndim = wsw;
-  sr.C = b.act_s;
-  sr.ldc = wsw;
-  sr.D = b.dA_s;
-  sr.ldd = wsw;
-  sr.C2 = b.dgu_s;
-  sr.ldc2 = swiglu ? 2 * wsw : wsw;
-  if (b.pre_shared != nullptr)
-    e = run_act_bwd(swiglu, b.pre_shared, (swiglu ? 2 : 1) * wsw, b.dA_s, wsw, nullptr, p.T, wsw,
-                    b.act_s, wsw, b.dgu_s, sr.ldc2, s);
-  else
-    e = run_bwd_epi(sr, swiglu, sbm, mt, s);
-  if (e != hipSuccess) return e;
-  GemmArgs s2 = sb;
-  s2.A = b.dgu_s;
-  s2.lda = swiglu ? 2 * wsw : wsw;
-  s2.B0 = b.ws_gate;
-  s2.B1 = b.ws_up;
-  s2.ldb = d;
-  s2.Kdim = swiglu ? 2 * wsw : wsw;
-  s2.kseg = wsw;
-  s2.Ndim = d;
-  s2.C = b.dx_shared;
-  s2.ldc = d;
-  if ((e = launch_bf16<EPI_NONE, true>(s2, sbm, mt, s)) != hipSuccess) return e;
+  // shared experts' weight gradients by the direct kernel
   if ((e = run_wgrad(wgrad_args(b.d_out, d, b.act_s, wsw, nullptr, 1, p.T, d, wsw, b.dws_down,
                                 nullptr, d, 0, dffs, dffs, (size_t)d * dffs),
                      s)) != hipSuccess)
     return e;
-  return run_wgrad(wgrad_args(b.dgu_s, swiglu ? 2 * wsw : wsw, b.u, d, nullptr, 1, p.T,
-                              swiglu ? 2 * wsw : wsw, d, b.dws_gate, b.dws_up, wsw, 0, d, d, 0),
+  return run_wgrad(wgrad_args(b.dgu_s, gu * wsw, b.u, d, nullptr, 1, p.T, gu * wsw, d, b.dws_gate,
+                              b.dws_up, wsw, 0, d, d, 0),
                    s);
 }
 

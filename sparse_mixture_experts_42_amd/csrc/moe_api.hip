@@ -106,6 +106,14 @@ BwdWorkspace bwd_workspace_layout(const moe_problem_t& p) {
     w.kpad = take((N + 1) * 4);
     w.dyT = take(d * (size_t)w.ldt * es);
     w.xT = take(d * (size_t)w.ldt * es);
+    // the shared experts join the transposed launches while their operands
+    // stay within one 32-bit buffer descriptor each
+    const long long ts = (long long)(T + 63) / 64 * 64;
+    if (p.n_shared > 0 && ts <= (1LL << 22) && (long long)T * gu * wsw * 2 < (1LL << 31)) {
+      w.ldts = (int)ts;
+      w.dOT = take(d * (size_t)ts * es);
+      w.uT = take(d * (size_t)ts * es);
+    }
   }
   w.total = off;
   return w;
@@ -589,6 +597,11 @@ int moe_layer_backward(const moe_problem_t* p, const void* u, const moe_weights_
     b.dyT = ws_at(ws, L.dyT);
     b.xT = ws_at(ws, L.xT);
     b.ldt = L.ldt;
+    if (L.ldts > 0) {
+      b.dOT = ws_at(ws, L.dOT);
+      b.uT = ws_at(ws, L.uT);
+      b.ldts = L.ldts;
+    }
   }
   if (shared) {
     b.u = u;

@@ -124,6 +124,11 @@ struct FfnBwdBuffers {
   void* dyT;                // [d][ldt] workspace
   void* xT;                 // [d][ldt] workspace
   int ldt;
+  // shared experts' weight gradients in the same launches (null dOT: by the
+  // direct kernel): d_out and u transposed, [d][ldts] workspace each
+  void* dOT;
+  void* uT;
+  int ldts;
   // shared experts (n_shared > 0)
   const void* u;            // [T][d]
   const void* d_out;        // [T][d]
@@ -172,6 +177,8 @@ struct BwdWorkspace {
   size_t dyT;          // elem [d][ldt]
   size_t xT;           // elem [d][ldt]
   int ldt;             // 0: weight gradients by the direct k-major kernel
+  size_t dOT, uT;      // elem [d][ldts] (transposed form with shared experts)
+  int ldts;            // 0: shared experts' weight gradients by the direct kernel
   size_t total;
 };
 BwdWorkspace bwd_workspace_layout(const moe_problem_t& p);

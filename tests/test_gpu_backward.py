@@ -121,7 +121,10 @@ def _check_weight_grads(w, po, xi, x, t, ro, dsp, dO, experts, f_of, shared_f=No
     (1, 4, 2, "softmax_topk", "swiglu", 0.0, 1),
     # router weight gradient over 256-token slices (wide router, long
     # batch), the last slice ragged
-    (1100, 12, 2, "softmax_topk", "swiglu", 0.0, 0)])
+    (1100, 12, 2, "softmax_topk", "swiglu", 0.0, 0),
+    # groups over 512 rows on average: transposed weight gradients, with
+    # the shared experts' as a first set of long tiles in the same launches
+    (1100, 4, 2, "softmax_topk", "swiglu", 0.0, 2)])
 def test_backward_small_shapes(T, N, K, gating, act, cf, shared):
     """Every gradient and intermediate against the oracle.  The mean group
     T*K/N picks the GEMM tiles: 1300 tokens on both of two experts give two
@@ -245,7 +248,7 @@ def _cold_bias(w, x, lo, hi):
 
 
 @pytest.mark.parametrize("T,shared,cold", [(300, 0, None), (300, 1, None), (2100, 0, "empty"),
-                                           (4200, 0, "short")])
+                                           (2100, 1, None), (4200, 0, "short")])
 def test_backward_integer_data_is_exact(T, shared, cold):
     """ReLU experts, top-1 with softmax over the one selected score (gate 1,
     so no gradient reaches the router), sparse weights and inputs in
@@ -253,7 +256,9 @@ def test_backward_integer_data_is_exact(T, shared, cold):
     so every gradient must equal the oracle's bit for bit.  With 2100 tokens
     the experts average over 512 rows, so the weight gradients take the
     transposed form; the last expert's bias keeps it empty, and its weight
-    gradients must come out zero.  With 4200 tokens the groups average 1050
+    gradients must come out zero; with a shared expert, its weight gradients
+    (every token) run as the first tiles of the same launches.  With 4200
+    tokens the groups average 1050
     rows, so the GEMMs run 256-row tiles; the last expert's bias leaves it
     24 to 56 rows, which run as a 64-row tail tile."""
     N, d, dff = 4, 128, 192
@@ -314,6 +319,7 @@ def test_backward_integer_data_is_exact(T, shared, cold):
         assert np.array_equal(host(t["dw_down"][e]).T, ref["dw_down"]), f"dw_down[{e}]"
     if shared:
         ref = O.ffn_weight_grads(po, xi, -1, u, dO, np.arange(64, dtype=np.int32))
+        assert np.abs(ref["dw_gate"]).max() <= 256 and np.abs(ref["dw_down"]).max() <= 256
         assert np.array_equal(host(t["dws_gate"][0]), ref["dw_gate"])
         assert np.array_equal(host(t["dws_down"][0]).T, ref["dw_down"])
 
