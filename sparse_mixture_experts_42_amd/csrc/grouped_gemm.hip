@@ -360,7 +360,9 @@ __device__ __forceinline__ void store_forward_tile(const GemmArgs& a, f32x16 (&a
   const __amdgpu_buffer_rsrc_t rC =
       make_rsrc(C + (size_t)row0 * a.ldc + n0, (uint32_t)((size_t)rows * a.ldc * 2 - (size_t)n0 * 2));
   // the fp32 pre-activations, when kept: g pairs (and up pairs) as 8-byte
-  // stores through descriptors over the tile's rows, like the output
+  // stores through descriptors over the tile's rows, like the output; they
+  // are read once, by the backward, so the stores are non-temporal and do
+  // not push the operands the GEMM re-reads out of the caches
   constexpr bool KEEP = EPI == EPI_SWIGLU || EPI == EPI_RELU;
   const bool keep = KEEP && a.P != nullptr;
   __amdgpu_buffer_rsrc_t rPg = rC, rPu = rC;
@@ -395,11 +397,11 @@ __device__ __forceinline__ void store_forward_tile(const GemmArgs& a, f32x16 (&a
             const int rr = 32 * i + 8 * (v >> 2) + (v & 3);
             const f32x2 pg = pair_swap(acc[i][j][v], acc[i][j][v + 1], odd);
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pg), rPg, vP,
-                                                  rr * a.ldp * 4, 0);
+                                                  rr * a.ldp * 4, 2);
             if constexpr (GATED) {
               const f32x2 pu = pair_swap(acc[i][j + TN / 2][v], acc[i][j + TN / 2][v + 1], odd);
               __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pu), rPu, vP,
-                                                    rr * a.ldp * 4, 0);
+                                                    rr * a.ldp * 4, 2);
             }
           }
         }
@@ -1834,14 +1836,22 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
 
 // kpad[g]: first column of group g in the transposed operands (a multiple
 // of BK); kpad[G]: the padded total.
-__global__ void kpad_kernel(const int32_t* offsets, int G, int32_t* kpad) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
-  int acc = 0;
-  for (int g = 0; g < G; ++g) {
-    kpad[g] = acc;
-    acc += (offsets[g + 1] - offsets[g] + BK - 1) / BK * BK;
+// One 256-thread block (G <= 256): thread g holds group g's padded size, and
+// a block scan in LDS gives the exclusive prefix.
+__global__ __launch_bounds__(256) void kpad_kernel(const int32_t* offsets, int G, int32_t* kpad) {
+  __shared__ int sc[256];
+  const int g = threadIdx.x;
+  const int own = g < G ? (offsets[g + 1] - offsets[g] + BK - 1) / BK * BK : 0;
+  sc[g] = own;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = g >= off ? sc[g - off] : 0;
+    __syncthreads();
+    sc[g] += v;
+    __syncthreads();
   }
-  kpad[G] = acc;
+  if (g < G) kpad[g] = sc[g] - own;
+  if (g == G - 1) kpad[G] = sc[g];
 }
 
 // S [rows][C] (leading dimension lds) -> T [C][ldt] (bf16): row r of group
@@ -2632,7 +2642,7 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
     // shared experts' gradients (every token) run in the same launches as a
     // first set of long tiles: dWs_down[k] = d_out^T a_s[:, k-th d_ff_s
     // columns], [dWs_gate; dWs_up]^T = u^T [dG_s dU_s].
-    hipLaunchKernelGGL(kpad_kernel, dim3(1), dim3(64), 0, s, b.offsets, p.N, b.kpad);
+    hipLaunchKernelGGL(kpad_kernel, dim3(1), dim3(256), 0, s, b.offsets, p.N, b.kpad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const bool sh = p.n_shared > 0 && b.dOT != nullptr;
     KGemmSet sd{}, sg{};
