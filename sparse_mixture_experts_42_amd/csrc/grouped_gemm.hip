@@ -1686,13 +1686,16 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  lds_t* ldsA[2] = {(lds_t*)&sA[0][wave * PER * 64], (lds_t*)&sA[1][wave * PER * 64]};
-  lds_t* ldsB[2] = {(lds_t*)&sB[0][wave * PER * 64], (lds_t*)&sB[1][wave * PER * 64]};
+  // LDS addresses of this wave's part of each operand stage
+  const uint32_t ldsA[2] = {(uint32_t)(uintptr_t)(lds_t*)&sA[0][wave * PER * 64],
+                            (uint32_t)(uintptr_t)(lds_t*)&sA[1][wave * PER * 64]};
+  const uint32_t ldsB[2] = {(uint32_t)(uintptr_t)(lds_t*)&sB[0][wave * PER * 64],
+                            (uint32_t)(uintptr_t)(lds_t*)&sB[1][wave * PER * 64]};
 
   // tile h: group, output tile origin, the group's rows and operand descriptors
   struct Tile {
     int g, m0, n0, rows;
-    __amdgpu_buffer_rsrc_t rA, rB;
+    i32x4 rA, rB;
   };
   auto setup = [&](int h) __attribute__((always_inline)) {
     Tile t;
@@ -1707,23 +1710,24 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
     t.n0 = nt * 256;
     const long long abytes = ((long long)t.rows * a.lda - t.m0) * 2;
     const long long bbytes = ((long long)t.rows * a.ldb - t.n0) * 2;
-    t.rA = make_rsrc(static_cast<const uint16_t*>(a.A) + (size_t)r0 * a.lda + t.m0,
-                     (uint32_t)(abytes > 0 ? abytes : 0));
-    t.rB = make_rsrc(static_cast<const uint16_t*>(a.B) + (size_t)r0 * a.ldb + t.n0,
-                     (uint32_t)(bbytes > 0 ? bbytes : 0));
+    t.rA = rsrc_words(static_cast<const uint16_t*>(a.A) + (size_t)r0 * a.lda + t.m0,
+                      (uint32_t)(abytes > 0 ? abytes : 0));
+    t.rB = rsrc_words(static_cast<const uint16_t*>(a.B) + (size_t)r0 * a.ldb + t.n0,
+                      (uint32_t)(bbytes > 0 ? bbytes : 0));
     return t;
   };
+  // The loads are inline asm, so the compiler, which does not see that they
+  // write LDS, adds no waits for them before the transposing reads of the
+  // other buffer; the stage's explicit vmcnt(0) and barrier order them.
   auto issue = [&](const Tile& t, int kt, int buf) __attribute__((always_inline)) {
     const uint32_t ka = (uint32_t)kt * BK * (uint32_t)a.lda * 2u;
     const uint32_t kb = (uint32_t)kt * BK * (uint32_t)a.ldb * 2u;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rA, (lds_t*)((char*)ldsA[buf] + i * 1024), 16,
-                                               kmajor_voff(wave * PER + i, lane, a.lda) + ka, 0, 0, 0);
+      lds_load16(t.rA, ldsA[buf] + i * 1024u, kmajor_voff(wave * PER + i, lane, a.lda) + ka);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rB, (lds_t*)((char*)ldsB[buf] + i * 1024), 16,
-                                               kmajor_voff(wave * PER + i, lane, a.ldb) + kb, 0, 0, 0);
+      lds_load16(t.rB, ldsB[buf] + i * 1024u, kmajor_voff(wave * PER + i, lane, a.ldb) + kb);
   };
 
   // Persistent: block b takes tiles b, b + gridDim, ...  A tile's first
