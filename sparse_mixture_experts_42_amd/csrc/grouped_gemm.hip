@@ -1738,6 +1738,13 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
   if (h >= total) return;
   Tile t = setup(h);
   if (t.rows > 0) issue(t, 0, 0);
+  constexpr int kOut = 256 * 32 / 512;        // 16-byte output pieces per thread
+  // Memory operations complete in issue order as vmcnt counts them.  After
+  // a tile whose kOut stores per thread all issued (no edge), the next
+  // tile's first-stage loads, issued before those stores, are done once at
+  // most kOut operations are outstanding: the stores keep draining while
+  // the next tile computes.
+  bool drain_all = true;
   for (; h < total; h += gridDim.x) {
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -1748,7 +1755,10 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = (t.rows + BK - 1) / BK;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (drain_all)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kOut) : "memory");
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
@@ -1803,7 +1813,6 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
         stile[r * 128 + (c >> 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
       }
   __syncthreads();
-  constexpr int kOut = 256 * 32 / 512;        // 16-byte pieces per thread
   u32x4 outv[kOut];
   const u32x4* vt = &smem[0][0];
 #pragma unroll
@@ -1814,6 +1823,7 @@ __global__ __launch_bounds__(512) void grouped_wgrad_kernel(WgradArgs a) {
     t = setup(h + gridDim.x);
     if (t.rows > 0) issue(t, 0, 0);
   }
+  drain_all = cur.m0 + 256 > a.M || cur.n0 + 256 > a.N;
   uint16_t* out0 = static_cast<uint16_t*>(a.C) + (size_t)cur.g * a.c_group_stride;
   uint16_t* out1 =
       a.C2 != nullptr ? static_cast<uint16_t*>(a.C2) + (size_t)cur.g * a.c_group_stride : nullptr;
