@@ -65,6 +65,12 @@ struct GemmArgs {
   // row n - ct_split of C2 (both with leading dimension ldc); output rows
   // past M are not stored
   int ct_split;
+  // persistent plain GEMMs: split-K of the tail tiles (null: none), partial
+  // sums [kSplitSlots][8 waves][32 values][64 lanes] fp32 and kSplitSlots
+  // counters, one per tail tile (zero at launch; the last piece of a tile
+  // sets its counter to zero again)
+  float* split_part;
+  int32_t* split_cnt;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -1126,9 +1132,11 @@ struct RingAddr {
   const uint16_t* b_base;   // column tile n0, segment 0
   uint32_t b_bytes, b_voff_e, b_voff_o, b_step;
   int wave;
+  int kt0;                  // first stage of the tile's k range (split-K pieces)
   __device__ __forceinline__ RingAddr(const GemmArgs& a, int g, int row0, int rows, int by, int wave_,
-                                      int lane) {
+                                      int lane, int kt0_ = 0) {
     wave = wave_;
+    kt0 = kt0_;
     const int lrow = lane >> 3;
     const int ce = (lane & 7) ^ (lrow >> 1), co = (lane & 7) ^ (4 + (lrow >> 1));
     a_base = static_cast<const uint16_t*>(a.A) + (size_t)row0 * a.lda;
@@ -1156,13 +1164,13 @@ struct RingAddr {
   __device__ __forceinline__ void load_a(int kt, bool live, uint32_t slot_lds, int i) const {
     const bool odd = ((wave * AI + i) & 1) != 0;
     lds_load16(rsrc_words(a_base, live ? a_bytes : 0u), slot_lds + (uint32_t)((wave * AI + i) * 1024),
-               (odd ? a_voff_o : a_voff_e) + (uint32_t)i * a_step + (uint32_t)kt * 128u);
+               (odd ? a_voff_o : a_voff_e) + (uint32_t)i * a_step + (uint32_t)(kt0 + kt) * 128u);
   }
   // where the B rows of stage kt start: K segment seg of B (the shared
   // experts' down projection is segmented), k offset within it in bytes
   __device__ __forceinline__ void b_stage(const GemmArgs& a, int kt, const uint16_t*& base,
                                           uint32_t& koff) const {
-    const int kb = kt * 64;
+    const int kb = (kt0 + kt) * 64;
     const int seg = a.kseg == a.Kdim ? 0 : kb / a.kseg;
     base = b_base + (size_t)seg * a.kseg_stride;
     koff = (uint32_t)(kb - seg * a.kseg) * 2u;
@@ -1194,13 +1202,23 @@ __device__ __forceinline__ void ring_stage0(const GemmArgs& a, const RingAddr<EP
   for (int i = 0; i < AD::BI; ++i) ad.load_b(bb, bk, nk > 1, pool_lds + L::b_off(1), i);
 }
 
+// The k range of a tile: stages kt0 .. kt0+nk-1.  A tail tile of a plain
+// (EPI_NONE) GEMM may run as S split-K pieces; piece `piece` of tail tile
+// `tt` then leaves fp32 partial sums in a.split_part, and the piece that
+// finishes last adds them up in piece order and stores the tile.
+struct KRange {
+  int kt0, nk;
+  int S, piece, tt;
+};
+
 // One tile.  `issued`: its first loads (ring_stage0) are already in flight.
 // pre() runs after the main loop, once every wave is past the last stage
 // barrier and every wave's loads have landed; then no wave reads the pool
 // any more, and pre() may start the next tile's loads.
 template <int EPI, int BM, typename Pre>
 __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, int rows, int by,
-                                          u32x4 (&pool)[kPoolU4], bool issued, const Pre& pre) {
+                                          u32x4 (&pool)[kPoolU4], bool issued, const Pre& pre,
+                                          const KRange& kr) {
   using AD = RingAddr<EPI, BM>;
   using L = RingLayout;
   constexpr int WGN = 4, BN = 256;
@@ -1222,9 +1240,9 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, in
   by = __builtin_amdgcn_readfirstlane(by);
   const int wm = wave / WGN, wn = wave % WGN;
   const int n0 = by * AD::BNH;
-  const AD ad(a, g, row0, rows, by, wave, lane);
+  const AD ad(a, g, row0, rows, by, wave, lane, kr.kt0);
   const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0];
-  const int nk = a.Kdim / BK;
+  const int nk = kr.nk;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -1324,6 +1342,47 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int g, int row0, in
   // next tile
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (EPI == EPI_NONE && BM == kTailRows) {
+    if (kr.S > 1) {
+      // Partial sums of this piece: value r (of 32) of lane l of wave w at
+      // [slot][w][r][l], slot = tt * S + piece, so each store instruction
+      // writes 256 contiguous bytes.  The stores and, in the last
+      // piece, the loads are system-scope atomics: written through to memory
+      // and read from it, so pieces on different XCDs (separate L2s) see
+      // each other's values.  The counter's add follows the stores' wait.
+      float* own = a.split_part + ((size_t)(kr.tt * kr.S + kr.piece) * 8 + wave) * 32 * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          __hip_atomic_store(own + (16 * j + v) * 64, acc[0][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      int32_t* flag = reinterpret_cast<int32_t*>(&pool[kNextU4]) + 1;
+      if (tid == 0) *flag = atomicAdd(&a.split_cnt[kr.tt], 1) == kr.S - 1;
+      // pre()'s barrier publishes the flag; its loads avoid this word
+      pre();
+      if (__builtin_amdgcn_readfirstlane(*flag) == 0) return;
+      f32x16 sum[TM][TN];
+#pragma unroll
+      for (int i = 0; i < kr.S; ++i) {
+        const float* src = a.split_part + ((size_t)(kr.tt * kr.S + i) * 8 + wave) * 32 * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x = i == kr.piece ? acc[0][j][v]
+                                          : __hip_atomic_load(src + (16 * j + v) * 64, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_SYSTEM);
+            sum[0][j][v] = i == 0 ? x : sum[0][j][v] + x;
+          }
+      }
+      // the counter is zero again for the next launch that uses it
+      if (tid == 0) __hip_atomic_store(&a.split_cnt[kr.tt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      store_forward_tile<EPI, TM, TN, WTM, WTN>(a, sum, row0, rows, n0, wm, wn, lane);
+      return;
+    }
+  }
   pre();
   store_forward_tile<EPI, TM, TN, WTM, WTN>(a, acc, row0, rows, n0, wm, wn, lane);
 }
@@ -1381,7 +1440,21 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   int32_t* s_next = reinterpret_cast<int32_t*>(&pool[kNextU4]);
   const int ntiles = (a.Ndim + BNH - 1) / BNH;
   const int real = full_tiles_total_p(a, pl, 256) * ntiles;
-  const int total = real + tail_tiles_total_p(a, pl, 256) * ntiles;
+  const int tail_tiles = tail_tiles_total_p(a, pl, 256) * ntiles;
+  const int nk = a.Kdim / BK;
+  // Tail tiles (64 rows) are few and, with a long K, slow for their work:
+  // they mostly stream their weight panel.  When they would leave most
+  // blocks idle at the end, a plain GEMM splits each into S k-ranges, so
+  // that about one piece per block remains (S * tail_tiles <= kSplitSlots).
+  int S = 1;
+  if (EPI == EPI_NONE && a.split_part != nullptr && tail_tiles > 0) {
+    const int nb = (int)gridDim.x < kSplitSlots ? (int)gridDim.x : kSplitSlots;
+    S = nb / tail_tiles;
+    if (S > 4) S = 4;
+    if (S > nk / 4) S = nk / 4;
+    if (S < 1) S = 1;
+  }
+  const int total = real + tail_tiles * S;
   const int full = real - real % 8;
   const int q = full / 8;
   const int rest = total - full;
@@ -1407,22 +1480,31 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
     pending = cur == 0 ? atomicAdd(&queue[xcd], 1) : -1;
     return h;
   };
-  // a tile of the 1-D space: coordinates and height class (256, 64); false
-  // when it holds no rows (block-uniform results)
-  auto decode = [&](int h, int& g, int& row0, int& rows, int& by, int& bm) -> bool {
+  // a tile of the 1-D space: coordinates, height class (256, 64) and k
+  // range; false when it holds no rows (block-uniform results)
+  auto decode = [&](int h, int& g, int& row0, int& rows, int& by, int& bm, KRange& kr) -> bool {
     bool ok = true;
+    kr = KRange{0, nk, 1, 0, 0};
     if (h < real) {
       find_tile_2d_p(a, pl, 256, ntiles, h, real, g, row0, rows, by);
       bm = 256;
     } else {
       bm = kTailRows;
-      ok = find_tail_p(a, pl, 256, ntiles, h - real, g, row0, rows, by);
+      const int tt = (h - real) / S, piece = (h - real) - tt * S;
+      ok = find_tail_p(a, pl, 256, ntiles, tt, g, row0, rows, by);
+      const int k0 = piece * nk / S, k1 = (piece + 1) * nk / S;
+      kr = KRange{k0, k1 - k0, S, piece, tt};
     }
     g = __builtin_amdgcn_readfirstlane(g);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     rows = __builtin_amdgcn_readfirstlane(rows);
     by = __builtin_amdgcn_readfirstlane(by);
     bm = __builtin_amdgcn_readfirstlane(bm);
+    kr.kt0 = __builtin_amdgcn_readfirstlane(kr.kt0);
+    kr.nk = __builtin_amdgcn_readfirstlane(kr.nk);
+    kr.S = __builtin_amdgcn_readfirstlane(kr.S);
+    kr.piece = __builtin_amdgcn_readfirstlane(kr.piece);
+    kr.tt = __builtin_amdgcn_readfirstlane(kr.tt);
     return __builtin_amdgcn_readfirstlane((int)ok) != 0;
   };
 
@@ -1430,19 +1512,20 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   __syncthreads();
   int h = __builtin_amdgcn_readfirstlane(*s_next);
   int g = 0, row0 = 0, rows = 0, by = 0, bm = 0;
-  bool work = h >= 0 && decode(h, g, row0, rows, by, bm);
+  KRange kr{0, nk, 1, 0, 0};
+  bool work = h >= 0 && decode(h, g, row0, rows, by, bm, kr);
   bool issued = false;
-  const int nk = a.Kdim / BK;
   const uint32_t pool_lds = (uint32_t)(uintptr_t)(lds_t*)&pool[0];
   while (h >= 0) {
     int h_next = -1, g2 = 0, r2 = 0, n2 = 0, y2 = 0, bm2 = 0;
+    KRange kr2{0, nk, 1, 0, 0};
     bool next_work = false;
     // claim the next tile, decode it and start its loads
     auto pre = [&]() {
       if (tid == 0) *s_next = claim();
       __syncthreads();
       h_next = __builtin_amdgcn_readfirstlane(*s_next);
-      next_work = h_next >= 0 && decode(h_next, g2, r2, n2, y2, bm2);
+      next_work = h_next >= 0 && decode(h_next, g2, r2, n2, y2, bm2, kr2);
       if (next_work) {
         int t = threadIdx.x;
         asm volatile("" : "+v"(t));
@@ -1450,7 +1533,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
         if (bm2 == 256)
           ring_stage0<EPI, 256>(a, RingAddr<EPI, 256>(a, g2, r2, n2, y2, w, t & 63), nk, pool_lds);
         else
-          ring_stage0<EPI, kTailRows>(a, RingAddr<EPI, kTailRows>(a, g2, r2, n2, y2, w, t & 63), nk, pool_lds);
+          ring_stage0<EPI, kTailRows>(a, RingAddr<EPI, kTailRows>(a, g2, r2, n2, y2, w, t & 63, kr2.kt0),
+                                      kr2.nk, pool_lds);
       }
     };
     if (!work) {
@@ -1459,9 +1543,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
       __syncthreads();
       pre();
     } else if (bm == 256) {
-      ring_tile<EPI, 256>(a, g, row0, rows, by, pool, issued, pre);
+      ring_tile<EPI, 256>(a, g, row0, rows, by, pool, issued, pre, kr);
     } else {
-      ring_tile<EPI, kTailRows>(a, g, row0, rows, by, pool, issued, pre);
+      ring_tile<EPI, kTailRows>(a, g, row0, rows, by, pool, issued, pre, kr);
     }
     issued = next_work;
     work = next_work;
@@ -1471,6 +1555,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
     rows = n2;
     by = y2;
     bm = bm2;
+    kr = kr2;
   }
 }
 
@@ -2099,8 +2184,10 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* offsets, 
                                                         int32_t* queues) {
   __shared__ int32_t s[256], t[256];
   const int g = threadIdx.x;
-  // the persistent GEMM launches that follow start from empty queues
-  if (queues != nullptr && g < kQueueSets * kQueueInts) queues[g] = 0;
+  // the persistent GEMM launches that follow start from empty queues and
+  // zero split-K counters
+  if (queues != nullptr)
+    for (int i = g; i < kQueueSets * kQueueInts + kSplitSlots; i += 256) queues[i] = 0;
   int f = 0, tl = 0;
   if (g < G) split_rows(offsets[g + 1] - offsets[g], BMr, tail_rows, ext_rows, f, tl);
   s[g] = f;
@@ -2209,7 +2296,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
                               const void* w_down, const void* u, const void* ws_gate,
                               const void* ws_up, const void* ws_down, void* y_perm,
                               void* y_shared, int32_t* tiles, void* act, void* act_shared,
-                              hipStream_t s, float* pre, float* pre_shared) {
+                              float* split, hipStream_t s, float* pre, float* pre_shared) {
   const int gu = p.act == MOE_ACT_SWIGLU ? 2 : 1;
   const bool bf16 = p.dtype == MOE_BF16;
   const int epi1 = p.act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_RELU;
@@ -2255,8 +2342,14 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g1.ldp = gu * p.d_ff;
   if ((e = run_gemm(g1, epi1, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
+  // the down GEMMs may split their tail tiles' k range (one after the other,
+  // sharing the partial-sum buffer and the counters, which each launch
+  // leaves at zero)
+  int32_t* split_cnt = queues + kQueueSets * kQueueInts;
   GemmArgs g2 = g1;
   g2.P = nullptr;
+  g2.split_part = bf16 ? split : nullptr;
+  g2.split_cnt = split_cnt;
   g2.A = act;
   g2.B0 = w_down;
   g2.B1 = nullptr;
@@ -2312,6 +2405,8 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
     if ((e = run_gemm(s1, epi1, bf16, sbm, mt, s)) != hipSuccess) return e;
     GemmArgs s2 = s1;
     s2.P = nullptr;
+    s2.split_part = bf16 ? split : nullptr;
+    s2.split_cnt = split_cnt;
     s2.A = act_shared;
     s2.queue = queues + 3 * kQueueInts;
     s2.B0 = ws_down;

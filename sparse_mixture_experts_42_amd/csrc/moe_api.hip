@@ -33,6 +33,11 @@ Workspace workspace_layout(const moe_problem_t& p) {
   off = align_up(off + T * K * (size_t)p.d_ff * es, kAlign);
   w.act_shared = off;
   if (p.n_shared > 0) off = align_up(off + T * (size_t)p.n_shared * p.d_ff_shared * es, kAlign);
+  const bool bf16 = p.dtype == MOE_BF16;
+  w.has_split = bf16 && (ffn_row_tile(p.T * p.K, p.N, true) == 256 ||
+                         (p.n_shared > 0 && ffn_row_tile(p.T, 1, true) == 256));
+  w.split = off;
+  if (w.has_split) off = align_up(off + kSplitBytes, kAlign);
   w.total = off;
   return w;
 }
@@ -343,7 +348,9 @@ int moe_grouped_ffn(const moe_problem_t* p, const void* x_perm, const int32_t* o
   return hip_status(moe::launch_grouped_ffn(
       *p, p->T * p->K, x_perm, offsets, w_gate, w_up, w_down, u, ws_gate, ws_up, ws_down, y_perm,
       p->n_shared > 0 ? y_shared : nullptr, reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)),
-      ws_at(ws, w.act), ws_at(ws, w.act_shared), static_cast<hipStream_t>(stream)));
+      ws_at(ws, w.act), ws_at(ws, w.act_shared),
+      w.has_split ? reinterpret_cast<float*>(ws_at(ws, w.split)) : nullptr,
+      static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_problem_t* p, const void* u, const void* y_perm, const int32_t* row_of,
@@ -421,8 +428,9 @@ int launch_layer(const moe_problem_t* p, const void* u, const float* noise,
   e = moe::launch_grouped_ffn(*p, p->T * p->K, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down, u,
                               wt->ws_gate, wt->ws_up, wt->ws_down, o->y_perm, ysh,
                               reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)), ws_at(ws, w.act),
-                              ws_at(ws, w.act_shared), s, o->pre,
-                              p->n_shared > 0 ? o->pre_shared : nullptr);
+                              ws_at(ws, w.act_shared),
+                              w.has_split ? reinterpret_cast<float*>(ws_at(ws, w.split)) : nullptr, s,
+                              o->pre, p->n_shared > 0 ? o->pre_shared : nullptr);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_combine(*p, u, o->y_perm, o->row_of, o->topk_gate, ysh, out, s);
   return hip_status(e);
@@ -755,7 +763,7 @@ int moe_ec_layer_forward(const moe_problem_t* p, const void* u, const float* noi
   e = moe::launch_grouped_ffn(*p, rows, o->x_perm, o->offsets, wt->w_gate, wt->w_up, wt->w_down,
                               u, wt->ws_gate, wt->ws_up, wt->ws_down, o->y_perm, ysh,
                               reinterpret_cast<int32_t*>(ws_at(ws, w.tiles)), ws_at(ws, w.act),
-                              ws_at(ws, w.act_shared), s);
+                              ws_at(ws, w.act_shared), nullptr, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_ec_combine(*p, u, o->y_perm, o->row_of, o->gate_of, ysh, out, s));
 }

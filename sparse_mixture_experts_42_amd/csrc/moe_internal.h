@@ -55,7 +55,14 @@ constexpr int kDispatchTok = 256;   // tokens per dispatch block
 // of kQueueInts, zeroed by the plan kernel before each grouped FFN).
 constexpr int kQueueInts = 16;
 constexpr int kQueueSets = 4;
-inline size_t gemm_plan_bytes(size_t N) { return (2 * (N + 2) + kQueueSets * kQueueInts) * 4; }
+// Split-K of the persistent plain GEMM's tail tiles: at most kSplitSlots
+// pieces, each with 64 KB of fp32 partial sums, and one counter per tail
+// tile (after the queue counters, zeroed with them).
+constexpr int kSplitSlots = 256;
+constexpr size_t kSplitBytes = (size_t)kSplitSlots * 64 * 256 * 4;
+inline size_t gemm_plan_bytes(size_t N) {
+  return (2 * (N + 2) + kQueueSets * kQueueInts + kSplitSlots) * 4;
+}
 
 struct Workspace {
   size_t route_part;   // fp32 [route_blocks][N]   per-block softmax sums
@@ -66,6 +73,9 @@ struct Workspace {
   size_t tiles;        // int32 gemm_plan_bytes(N)  grouped-GEMM tile prefixes, queue counters
   size_t act;          // elem [T*K][d_ff]        gated activations
   size_t act_shared;   // elem [T][n_shared*d_ff_shared]
+  size_t split;        // fp32 kSplitBytes: split-K partial sums of the persistent
+                       // down GEMMs' tail tiles (only when a 256-row GEMM runs)
+  bool has_split;
   size_t total;
   int route_blocks;
   int disp_blocks;
@@ -100,7 +110,8 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
                               const void* w_down, const void* u, const void* ws_gate,
                               const void* ws_up, const void* ws_down, void* y_perm,
                               void* y_shared, int32_t* tiles, void* act, void* act_shared,
-                              hipStream_t s, float* pre = nullptr, float* pre_shared = nullptr);
+                              float* split, hipStream_t s, float* pre = nullptr,
+                              float* pre_shared = nullptr);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* u, const void* y_perm,
                           const int32_t* row_of, const float* topk_gate,

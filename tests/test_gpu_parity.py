@@ -267,11 +267,11 @@ def test_grouped_ffn_ragged(T, N, K, d, dff, act, shared):
 TILE_SIZES = [257, 320, 321, 300, 0, 255, 1, 600, 64, 65, 576, 512]
 
 
-def _tile_case(act, T, want_tile, want_shared_tile):
-    K, d, dff = 4, 128, 192
+def _tile_case(act, T, want_tile, want_shared_tile, d=128, dff=192, dffs=128, repeat=False):
+    K = 4
     sizes = TILE_SIZES
     w = W.Workload("tails", T=T, d=d, N=len(sizes), K=K, d_ff=dff, act=act, n_shared=1,
-                   d_ff_shared=128, seed=77, dtype="bf16")
+                   d_ff_shared=dffs, seed=77, dtype="bf16")
     # the launch's tile height follows the mean group size T*K/N
     assert M.moe_ffn_row_tile(T * K, len(sizes)) == want_tile
     assert M.moe_ffn_row_tile(T, 1) == want_shared_tile
@@ -285,10 +285,18 @@ def _tile_case(act, T, want_tile, want_shared_tile):
     x_perm = torch.randn(T * K, d, generator=g).to(torch.bfloat16)
     say(f"ffn tiles {act}: {want_tile}-row tiles, groups {sizes}, shared over {T} tokens")
     xg = gpu(x)
-    o = M.moe_grouped_ffn(p, x_perm.to(DEV), torch.from_numpy(offsets).to(DEV), xg["w_gate"],
-                          xg["w_up"], xg["w_down"], xg["u"], xg["ws_gate"], xg["ws_up"],
-                          xg["ws_down"])
+    run = lambda: M.moe_grouped_ffn(p, x_perm.to(DEV), torch.from_numpy(offsets).to(DEV), xg["w_gate"],
+                                    xg["w_up"], xg["w_down"], xg["u"], xg["ws_gate"], xg["ws_up"],
+                                    xg["ws_down"])
+    o = run()
     torch.cuda.synchronize()
+    if repeat:
+        # the same call again gives the same bits (split-K pieces finish in
+        # any order; their sums are added in piece order)
+        o2 = run()
+        torch.cuda.synchronize()
+        assert torch.equal(o["y_perm"][:R], o2["y_perm"][:R])
+        assert torch.equal(o["y_shared"], o2["y_shared"])
     eor = np.repeat(np.arange(len(sizes), dtype=np.int32), sizes)
     xi = _io.inputs(po, x)
     y_ref = O.ffn_rows(po, xi, elems(x_perm[:R]), eor)
@@ -308,6 +316,18 @@ def test_grouped_ffn_256_row_tiles(act):
     (512) and an empty group.  The shared expert over 3100 tokens (12 tiles
     and 28 rows) ends in a tail tile.  Every row is checked."""
     _tile_case(act, 3100, 256, 256)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_grouped_ffn_256_row_tiles_split_k(act):
+    """The same groups with a down projection long enough to split: d_ff =
+    1024 (16 k-stages) and 384 output columns (a full and a partly filled
+    column tile), so the 6 tail tiles of each column (12 in all) run as 4
+    k-range pieces each, their fp32 partial sums added by the piece that
+    finishes last; the shared expert's down GEMM (d_ff_s = 512, 8 stages)
+    splits its 2 tail tiles in 2.  Every row is checked, and a second call
+    gives the same bits."""
+    _tile_case(act, 3100, 256, 256, d=384, dff=1024, dffs=512, repeat=True)
 
 
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
