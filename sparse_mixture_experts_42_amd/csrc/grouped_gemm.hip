@@ -1042,6 +1042,24 @@ __host__ __device__ inline int queue_slot(int y, int t, int q, int full, int res
   return t < rest ? full + t : -1;
 }
 
+// Split-K of the tail tiles of a persistent plain GEMM: the number of
+// pieces per tail tile (1: none) for `tail_tiles` tail tiles, `blocks`
+// blocks and nk stages, so that about one piece per block remains, each of
+// at least 4 stages, and the pieces fit kSplitSlots partial-sum slots.
+__host__ __device__ inline int split_pieces(int tail_tiles, int blocks, int nk) {
+  if (tail_tiles <= 0) return 1;
+  const int nb = blocks < kSplitSlots ? blocks : kSplitSlots;
+  int S = nb / tail_tiles;
+  if (S > 4) S = 4;
+  if (S > nk / 4) S = nk / 4;
+  return S < 1 ? 1 : S;
+}
+// Piece p of S of a tail tile: stages kt0 .. kt0+n-1 of 0 .. nk-1.
+__host__ __device__ inline void split_range(int p, int S, int nk, int& kt0, int& n) {
+  kt0 = p * nk / S;
+  n = (p + 1) * nk / S - kt0;
+}
+
 // Tail tiles of all groups (single-group form: from M).
 template <typename P>
 __host__ __device__ inline int tail_tiles_total_p(const GemmArgs& a, const P& pl, int BM) {
@@ -1446,14 +1464,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   // they mostly stream their weight panel.  When they would leave most
   // blocks idle at the end, a plain GEMM splits each into S k-ranges, so
   // that about one piece per block remains (S * tail_tiles <= kSplitSlots).
-  int S = 1;
-  if (EPI == EPI_NONE && a.split_part != nullptr && tail_tiles > 0) {
-    const int nb = (int)gridDim.x < kSplitSlots ? (int)gridDim.x : kSplitSlots;
-    S = nb / tail_tiles;
-    if (S > 4) S = 4;
-    if (S > nk / 4) S = nk / 4;
-    if (S < 1) S = 1;
-  }
+  const int S = EPI == EPI_NONE && a.split_part != nullptr ? split_pieces(tail_tiles, gridDim.x, nk) : 1;
   const int total = real + tail_tiles * S;
   const int full = real - real % 8;
   const int q = full / 8;
@@ -1492,8 +1503,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
       bm = kTailRows;
       const int tt = (h - real) / S, piece = (h - real) - tt * S;
       ok = find_tail_p(a, pl, 256, ntiles, tt, g, row0, rows, by);
-      const int k0 = piece * nk / S, k1 = (piece + 1) * nk / S;
-      kr = KRange{k0, k1 - k0, S, piece, tt};
+      int k0, n;
+      split_range(piece, S, nk, k0, n);
+      kr = KRange{k0, n, S, piece, tt};
     }
     g = __builtin_amdgcn_readfirstlane(g);
     row0 = __builtin_amdgcn_readfirstlane(row0);

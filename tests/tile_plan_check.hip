@@ -1,7 +1,9 @@
 // Host-side check of the grouped-GEMM tile plan: for random and edge-case
 // group sizes, the tiles that split_rows, find_tile_2d and find_tail assign
 // to the launched grid cover every row of every group exactly once per
-// column tile, stay inside their group and within the tile bodies' heights.
+// column tile, stay inside their group and within the tile bodies' heights;
+// the persistent launch's queues hand out every tile slot once; and the
+// split-K pieces of the tail tiles cover each tile's k range once.
 // Built with hipcc as a host program (no GPU needed) by tests/test_tile_plan.py.
 #include "grouped_gemm.hip"
 #include <cstdio>
@@ -92,6 +94,27 @@ static int check_queues(const std::vector<int>& sizes, int ntiles, int blocks, s
   return 0;
 }
 
+// Split-K of the tail tiles: the piece count stays within the partial-sum
+// slots and the blocks, each piece has at least 4 stages, and the pieces of
+// a tile cover its stages 0 .. nk-1 exactly once, in order.
+static int check_split(int tail_tiles, int blocks, int nk) {
+  const int S = split_pieces(tail_tiles, blocks, nk);
+  if (S < 1 || S > 4) { printf("S=%d\n", S); return 1; }
+  if (S > 1 && (S * tail_tiles > kSplitSlots || S * tail_tiles > blocks)) {
+    printf("S=%d tails=%d blocks=%d\n", S, tail_tiles, blocks);
+    return 1;
+  }
+  int next = 0;
+  for (int p = 0; p < S; ++p) {
+    int kt0, n;
+    split_range(p, S, nk, kt0, n);
+    if (kt0 != next || n < (S > 1 ? 4 : 1)) { printf("piece %d of %d: %d+%d, nk=%d\n", p, S, kt0, n, nk); return 1; }
+    next = kt0 + n;
+  }
+  if (next != nk) { printf("pieces end at %d, nk=%d\n", next, nk); return 1; }
+  return 0;
+}
+
 int main() {
   std::mt19937 rng(1);
   int fails = 0, n = 0;
@@ -114,6 +137,15 @@ int main() {
     std::vector<int> s(G);
     for (auto& x : s) { int k = rng() % 3; x = k == 0 ? rng() % 70 : k == 1 ? 256 * (rng() % 9) + rng() % 80 : rng() % 3000; }
     fails += check_queues(s, 1 + rng() % 120, 8 * (1 + rng() % 32), rng); ++n;
+  }
+  for (int tt : {0, 1, 2, 12, 63, 64, 65, 80, 85, 128, 129, 256, 300})
+    for (int blocks : {8, 64, 248, 256, 304})
+      for (int nk : {1, 3, 4, 7, 8, 16, 22, 224, 225}) {
+        if (tt == 0) continue;
+        fails += check_split(tt, blocks, nk); ++n;
+      }
+  for (int it = 0; it < 20000; ++it) {
+    fails += check_split(1 + rng() % 400, 8 * (1 + rng() % 40), 1 + rng() % 500); ++n;
   }
   printf("%d cases, %d failures\n", n, fails);
   return fails != 0;
