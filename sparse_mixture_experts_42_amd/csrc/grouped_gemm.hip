@@ -71,6 +71,10 @@ struct GemmArgs {
   // sets its counter to zero again)
   float* split_part;
   int32_t* split_cnt;
+  // order of the full tiles over the XCDs (xcd_pos): 0 = one contiguous
+  // run of the patch order per XCD; P > 0 = runs dealt in chunks of P tiles
+  // round-robin, so the 8 XCDs work on neighbouring chunks at once
+  int xcd_chunk;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -139,6 +143,7 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int
 }
 
 constexpr int kPatchN = 4;   // n-tiles per patch: an XCD works on m-tiles x 4 n-tiles of one group
+constexpr int kXcdChunk = 32;   // chunk of the interleaved XCD order: one XCD's 32 CUs
 
 // Full-height tiles of all groups (single-group form: from M).
 template <typename P>
@@ -164,13 +169,31 @@ __host__ __device__ inline int full_tiles_total(const GemmArgs& a, int BM) {
 // a given position of successive patches tends to land on the same CU (the
 // CUs finish their tiles in the same order), and without the rotation the
 // same few CUs would draw every group's taller last tile.
+//
+// Position t of XCD y's run (q tiles per XCD) is logical tile xcd_pos(y, t,
+// q, P).  With P = 0 the run is the contiguous range [y q, y q + q).  With
+// P > 0 the whole chunks of P tiles are dealt round-robin (chunk c of XCD y
+// is logical chunk 8c + y) and the q mod P leftover positions of each XCD
+// form contiguous runs after them.  At a given time the XCDs then work on 8
+// neighbouring chunks, mostly one or two groups, so an activation panel that
+// several XCDs read (one per patch of 4 n-tiles) is fetched from HBM once and
+// served to the other XCDs by the shared Infinity Cache; with contiguous
+// runs each XCD streams its own group, and a group's activations are
+// re-read from HBM by each of its patches once they outgrow that cache.
+__host__ __device__ inline int xcd_pos(int y, int t, int q, int P) {
+  if (P <= 0) return y * q + t;
+  const int qc = q / P * P;
+  if (t < qc) return ((t / P) * 8 + y) * P + t % P;
+  return 8 * qc + y * (q - qc) + (t - qc);
+}
+
 template <typename P>
 __host__ __device__ inline void find_tile_2d_p(const GemmArgs& a, const P& pl, int BM, int ntiles,
                                                int h, int real, int& g, int& row0, int& rows,
                                                int& nt) {
   int mt_g, base;
   const int full = real - real % 8;
-  const int L = h < full ? (h % 8) * (full / 8) + h / 8 : h;
+  const int L = h < full ? xcd_pos(h % 8, h / 8, full / 8, a.xcd_chunk) : h;
   if (a.offsets == nullptr) {
     g = 0;
     mt_g = real / ntiles;
@@ -2374,6 +2397,9 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g2.ldc = p.d;
   g2.kseg = p.d_ff;
   g2.b_group_stride = (size_t)p.d * p.d_ff;
+  // the down GEMM's activations (rows x d_ff) are the large operand: XCDs
+  // share them through the Infinity Cache in chunks of one XCD's 32 CUs
+  g2.xcd_chunk = kXcdChunk;
   if ((e = run_gemm(g2, EPI_NONE, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
   if (p.n_shared > 0) {

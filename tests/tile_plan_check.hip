@@ -3,7 +3,8 @@
 // to the launched grid cover every row of every group exactly once per
 // column tile, stay inside their group and within the tile bodies' heights;
 // the persistent launch's queues hand out every tile slot once; and the
-// split-K pieces of the tail tiles cover each tile's k range once.
+// split-K pieces of the tail tiles cover each tile's k range once; and the
+// interleaved XCD order (xcd_pos) is a permutation of each launch's tiles.
 // Built with hipcc as a host program (no GPU needed) by tests/test_tile_plan.py.
 #include "grouped_gemm.hip"
 #include <cstdio>
@@ -11,7 +12,8 @@
 #include <vector>
 #include <random>
 using namespace moe;
-static int check(const std::vector<int>& sizes, int ntiles, bool single, int BM, int tail, int ext) {
+static int check(const std::vector<int>& sizes, int ntiles, bool single, int BM, int tail, int ext,
+                 int chunk = 0) {
   int G = (int)sizes.size();
   std::vector<int32_t> off(G + 1, 0), tiles(G + 2, 0), tails(G + 2, 0);
   for (int g = 0; g < G; ++g) off[g + 1] = off[g] + sizes[g];
@@ -26,6 +28,7 @@ static int check(const std::vector<int>& sizes, int ntiles, bool single, int BM,
   a.tiles = single ? nullptr : tiles.data();
   a.tails = single ? nullptr : tails.data();
   a.tail_rows = tail; a.ext_rows = ext; a.G = G; a.M = single ? sizes[0] : 0;
+  a.xcd_chunk = chunk;
   int R = off[G];
   int mtiles_max;
   if (single) { int f, t; split_rows(R, BM, tail, ext, f, t); mtiles_max = f + t; }
@@ -38,6 +41,10 @@ static int check(const std::vector<int>& sizes, int ntiles, bool single, int BM,
     int g, row0, rows, nt;
     if (h < real) {
       find_tile_2d(a, BM, ntiles, h, real, g, row0, rows, nt);
+      // without extended tiles (the persistent kernel) a group's last full
+      // tile may report the rows up to the group's end; its body computes BM
+      // rows and the tail tile takes the rest
+      if (ext == 0 && rows > BM) rows = BM;
       if (rows <= 0 || rows > BM + ext) { printf("bad rows %d h=%d\n", rows, h); return 1; }
     } else if (find_tail(a, BM, ntiles, h - real, g, row0, rows, nt)) {
       if (rows <= 0 || rows > tail) { printf("bad tail rows %d\n", rows); return 1; }
@@ -94,6 +101,21 @@ static int check_queues(const std::vector<int>& sizes, int ntiles, int blocks, s
   return 0;
 }
 
+// The interleaved XCD order: (y, t) for y < 8, t < q maps onto [0, 8q)
+// one to one, and P = 0 is the contiguous run.
+static int check_xcd_pos(int q, int P) {
+  std::vector<int> seen(8 * (size_t)q, 0);
+  for (int y = 0; y < 8; ++y)
+    for (int t = 0; t < q; ++t) {
+      const int L = xcd_pos(y, t, q, P);
+      if (L < 0 || L >= 8 * q) { printf("xcd_pos(%d,%d,%d,%d)=%d\n", y, t, q, P, L); return 1; }
+      if (P == 0 && L != y * q + t) { printf("xcd_pos contiguous\n"); return 1; }
+      seen[L]++;
+    }
+  for (int L = 0; L < 8 * q; ++L) if (seen[L] != 1) { printf("xcd_pos q=%d P=%d: %d seen %d\n", q, P, L, seen[L]); return 1; }
+  return 0;
+}
+
 // Split-K of the tail tiles: the piece count stays within the partial-sum
 // slots and the blocks, each piece has at least 4 stages, and the pieces of
 // a tile cover its stages 0 .. nk-1 exactly once, in order.
@@ -120,7 +142,11 @@ int main() {
   int fails = 0, n = 0;
   std::vector<std::vector<int>> fixed = {{257, 320, 321, 300, 0, 255, 1, 600}, {2057, 1968, 2004, 2073, 2088, 2072, 2032, 2090},
                                          {64, 65, 576, 512, 0, 0, 1, 319}, {2048, 2048}, {1}, {0, 0, 5}};
-  for (auto& s : fixed) for (int nt : {1, 3, 4, 5, 16, 112}) { fails += check(s, nt, false, 256, 64, 64); ++n; }
+  for (auto& s : fixed)
+    for (int nt : {1, 3, 4, 5, 16, 112})
+      for (int chunk : {0, 32, 7}) { fails += check(s, nt, false, 256, 64, 64, chunk); ++n; }
+  for (int q : {0, 1, 5, 31, 32, 33, 64, 100, 128, 1000})
+    for (int P : {0, 1, 7, 32, 64}) { fails += check_xcd_pos(q, P); ++n; }
   for (int M : {1, 26, 64, 65, 255, 256, 257, 320, 321, 1050, 8192, 16384, 16448, 16449})
     for (int nt : {1, 4, 7, 16}) { fails += check({M}, nt, true, 256, 64, 64); ++n; }
   for (int it = 0; it < 3000; ++it) {
@@ -129,6 +155,7 @@ int main() {
     for (auto& x : s) { int k = rng() % 4; x = k == 0 ? rng() % 70 : k == 1 ? 256 * (rng() % 9) + rng() % 80 : rng() % 3000; }
     int nt = 1 + rng() % 40;
     fails += check(s, nt, false, 256, 64, 64); ++n;
+    fails += check(s, nt, false, 256, 64, 0, 32); ++n;
     fails += check(s, nt, false, 128, 0, 0); ++n;
     fails += check(s, nt, false, 32, 0, 0); ++n;
   }
