@@ -75,6 +75,10 @@ struct GemmArgs {
   // run of the patch order per XCD; P > 0 = runs dealt in chunks of P tiles
   // round-robin, so the 8 XCDs work on neighbouring chunks at once
   int xcd_chunk;
+  // persistent grouped launches without split-K: each group's tail tiles
+  // run after the full tiles of their 32 columns (find_tile_fold_p) instead
+  // of after all full tiles
+  int fold_tails;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -144,6 +148,7 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int bx, int BM, int
 
 constexpr int kPatchN = 4;   // n-tiles per patch: an XCD works on m-tiles x 4 n-tiles of one group
 constexpr int kXcdChunk = 32;   // chunk of the interleaved XCD order: one XCD's 32 CUs
+constexpr int kTailRows = 64;   // rows of a tail tile of the 256-row kernels
 
 // Full-height tiles of all groups (single-group form: from M).
 template <typename P>
@@ -259,6 +264,60 @@ __host__ __device__ inline bool find_tail_p(const GemmArgs& a, const P& pl, int 
 __host__ __device__ inline bool find_tail(const GemmArgs& a, int BM, int ntiles, int h, int& g,
                                           int& row0, int& rows, int& nt) {
   return find_tail_p(a, ptr_plan(a), BM, ntiles, h, g, row0, rows, nt);
+}
+
+// The 256-row plan of a grouped launch with the tail tiles folded in: group
+// g owns (full_g + tail_g) x ntiles consecutive logical tiles, walked in
+// runs of 8 patches (32 n-tiles): the full tiles of the run's patches (each
+// patch full_g x kPatchN tiles, rotated as in find_tile_2d_p), then the
+// run's tail tiles, one per n-tile.  A run's full tiles are 8 chunks of 32
+// tiles when full_g = 8; dealt to the 8 XCDs (xcd_chunk = 32) they run at
+// once, and the tail chunk comes next, so a tail tile reads its weight panel
+// shortly after the full tiles of its column did, from the Infinity Cache,
+// instead of streaming it from HBM after every full tile has run.  Slot h of
+// [0, span), span = all full and tail tiles x ntiles.  bm is 256 or
+// kTailRows; rows as in find_tile_2d_p and find_tail_p.  Returns false when
+// the tile holds no rows.
+constexpr int kFoldRun = 8 * kPatchN;
+template <typename P>
+__host__ __device__ inline bool find_tile_fold_p(const GemmArgs& a, const P& pl, int ntiles, int h,
+                                                 int span, int& g, int& row0, int& rows, int& nt,
+                                                 int& bm) {
+  const int full = span - span % 8;
+  const int L = h < full ? xcd_pos(h % 8, h / 8, full / 8, a.xcd_chunk) : h;
+  int lo = 0, hi = a.G;   // (tiles+tails)[lo]*ntiles <= L < (tiles+tails)[hi]*ntiles
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((pl.tile(mid) + pl.tail(mid)) * ntiles <= L) lo = mid;
+    else hi = mid;
+  }
+  g = lo;
+  const int mt_g = pl.tile(g + 1) - pl.tile(g);
+  const int rg = mt_g + pl.tail(g + 1) - pl.tail(g);
+  const int l = L - (pl.tile(g) + pl.tail(g)) * ntiles;
+  const int run = l / (rg * kFoldRun);              // runs before the last are kFoldRun wide
+  const int c0 = run * kFoldRun;
+  const int width = ntiles - c0 < kFoldRun ? ntiles - c0 : kFoldRun;
+  const int r = l - run * rg * kFoldRun;
+  const int end = pl.offset(g + 1);
+  if (r < mt_g * width) {
+    const int pi = r / (mt_g * kPatchN);            // patches before the last are kPatchN wide
+    const int rem = r - pi * mt_g * kPatchN;
+    const int nb = c0 / kPatchN + pi;
+    const int nbe = ntiles - nb * kPatchN < kPatchN ? ntiles - nb * kPatchN : kPatchN;
+    const int mt = (rem / nbe + nb) % mt_g;
+    nt = nb * kPatchN + rem % nbe;
+    row0 = pl.offset(g) + mt * 256;
+    rows = end - row0;
+    if (mt < mt_g - 1 && rows > 256) rows = 256;
+    bm = 256;
+  } else {
+    nt = c0 + (r - mt_g * width);
+    row0 = pl.offset(g) + mt_g * 256;
+    rows = end - row0;
+    bm = kTailRows;
+  }
+  return rows > 0;
 }
 
 // ------------------------------------------------------------ bf16 MFMA
@@ -1034,7 +1093,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
 // last tile grows to 320 rows (160x64 per wave) when the group ends at most
 // 64 rows past a multiple of 256, and groups of at most 64 rows get a 64-row
 // tail tile (32x64 per wave).
-constexpr int kTailRows = 64;
 constexpr int kExtRows = 64;
 
 template <int EPI, bool BT = false>
@@ -1489,7 +1547,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   // that about one piece per block remains (S * tail_tiles <= kSplitSlots).
   const int S = EPI == EPI_NONE && a.split_part != nullptr ? split_pieces(tail_tiles, gridDim.x, nk) : 1;
   const int total = real + tail_tiles * S;
-  const int full = real - real % 8;
+  // without split-K, a grouped launch may run its tail tiles among the full
+  // tiles: the patch order then spans every tile
+  const bool fold = a.fold_tails != 0 && S == 1 && a.offsets != nullptr;
+  const int span = fold ? total : real;
+  const int full = span - span % 8;
   const int q = full / 8;
   const int rest = total - full;
   const int xcd = blockIdx.x & 7;
@@ -1519,7 +1581,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   auto decode = [&](int h, int& g, int& row0, int& rows, int& by, int& bm, KRange& kr) -> bool {
     bool ok = true;
     kr = KRange{0, nk, 1, 0, 0};
-    if (h < real) {
+    if (fold) {
+      ok = find_tile_fold_p(a, pl, ntiles, h, span, g, row0, rows, by, bm);
+    } else if (h < real) {
       find_tile_2d_p(a, pl, 256, ntiles, h, real, g, row0, rows, by);
       bm = 256;
     } else {
@@ -2375,6 +2439,10 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g1.b_group_stride = (size_t)p.d_ff * p.d;
   g1.P = bf16 ? pre : nullptr;
   g1.ldp = gu * p.d_ff;
+  // the gate/up GEMM runs its tail tiles right after the full tiles of their
+  // columns, with the 8 XCDs on neighbouring chunks of one group
+  g1.fold_tails = 1;
+  g1.xcd_chunk = kXcdChunk;
   if ((e = run_gemm(g1, epi1, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
   // the down GEMMs may split their tail tiles' k range (one after the other,
@@ -2383,6 +2451,7 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   int32_t* split_cnt = queues + kQueueSets * kQueueInts;
   GemmArgs g2 = g1;
   g2.P = nullptr;
+  g2.fold_tails = 0;
   g2.split_part = bf16 ? split : nullptr;
   g2.split_cnt = split_cnt;
   g2.A = act;

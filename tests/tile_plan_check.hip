@@ -101,6 +101,40 @@ static int check_queues(const std::vector<int>& sizes, int ntiles, int blocks, s
   return 0;
 }
 
+// The persistent plan with the tail tiles folded in (find_tile_fold_p): the
+// slots [0, span) cover every row of every group once per column tile, full
+// tiles computing 256 rows and tail tiles at most kTailRows, each inside its
+// group.
+static int check_fold(const std::vector<int>& sizes, int ntiles, int chunk) {
+  int G = (int)sizes.size();
+  std::vector<int32_t> off(G + 1, 0), tiles(G + 2, 0), tails(G + 2, 0);
+  for (int g = 0; g < G; ++g) off[g + 1] = off[g] + sizes[g];
+  for (int g = 0; g < G; ++g) {
+    int f, t;
+    split_rows(sizes[g], 256, kTailRows, 0, f, t);
+    tiles[g + 1] = tiles[g] + f;
+    tails[g + 1] = tails[g] + t;
+  }
+  GemmArgs a{};
+  a.offsets = off.data(); a.tiles = tiles.data(); a.tails = tails.data();
+  a.tail_rows = kTailRows; a.ext_rows = 0; a.G = G; a.xcd_chunk = chunk; a.fold_tails = 1;
+  const PtrPlan pl = ptr_plan(a);
+  const int R = off[G];
+  const int span = (full_tiles_total(a, 256) + tail_tiles_total(a, 256)) * ntiles;
+  std::vector<int> cover((size_t)R * ntiles, 0);
+  for (int h = 0; h < span; ++h) {
+    int g, row0, rows, nt, bm;
+    if (!find_tile_fold_p(a, pl, ntiles, h, span, g, row0, rows, nt, bm)) { printf("fold: empty slot %d\n", h); return 1; }
+    if (bm == 256 && rows > 256) rows = 256;   // the tile body computes 256 rows
+    if (bm != 256 && (bm != kTailRows || rows > kTailRows)) { printf("fold: bm %d rows %d\n", bm, rows); return 1; }
+    if (rows <= 0 || nt < 0 || nt >= ntiles) { printf("fold: rows %d nt %d\n", rows, nt); return 1; }
+    if (row0 < off[g] || row0 + rows > off[g + 1]) { printf("fold: tile outside group %d\n", g); return 1; }
+    for (int r = row0; r < row0 + rows; ++r) cover[(size_t)r * ntiles + nt]++;
+  }
+  for (size_t i = 0; i < cover.size(); ++i) if (cover[i] != 1) { printf("fold: row %zu covered %d times\n", i / ntiles, cover[i]); return 1; }
+  return 0;
+}
+
 // The interleaved XCD order: (y, t) for y < 8, t < q maps onto [0, 8q)
 // one to one, and P = 0 is the contiguous run.
 static int check_xcd_pos(int q, int P) {
@@ -145,6 +179,9 @@ int main() {
   for (auto& s : fixed)
     for (int nt : {1, 3, 4, 5, 16, 112})
       for (int chunk : {0, 32, 7}) { fails += check(s, nt, false, 256, 64, 64, chunk); ++n; }
+  for (auto& s : fixed)
+    for (int nt : {1, 3, 4, 5, 16, 31, 32, 33, 40, 112})
+      for (int chunk : {0, 32}) { fails += check_fold(s, nt, chunk); ++n; }
   for (int q : {0, 1, 5, 31, 32, 33, 64, 100, 128, 1000})
     for (int P : {0, 1, 7, 32, 64}) { fails += check_xcd_pos(q, P); ++n; }
   for (int M : {1, 26, 64, 65, 255, 256, 257, 320, 321, 1050, 8192, 16384, 16448, 16449})
@@ -156,6 +193,7 @@ int main() {
     int nt = 1 + rng() % 40;
     fails += check(s, nt, false, 256, 64, 64); ++n;
     fails += check(s, nt, false, 256, 64, 0, 32); ++n;
+    fails += check_fold(s, 1 + rng() % 120, rng() % 2 ? 32 : 0); ++n;
     fails += check(s, nt, false, 128, 0, 0); ++n;
     fails += check(s, nt, false, 32, 0, 0); ++n;
   }
