@@ -2782,6 +2782,9 @@ hipError_t launch_grouped_ffn_backward(const moe_problem_t& p, int rows_alloc, c
   n2.Ndim = d;
   n2.C = b.dx_perm;
   n2.ldc = d;
+  // [dG dU] (rows x 2 d_ff) is the large operand, as the activations are in
+  // the forward down GEMM: the XCDs share it through the Infinity Cache
+  n2.xcd_chunk = kXcdChunk;
   if ((e = launch_bf16<EPI_NONE, true>(n2, bm, mtiles_max, s)) != hipSuccess) return e;
   const int gu = swiglu ? 2 : 1;
   // shared experts' data gradients over all T tokens, dY = d_out
