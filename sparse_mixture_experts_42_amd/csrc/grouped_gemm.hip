@@ -267,38 +267,46 @@ __host__ __device__ inline bool find_tail(const GemmArgs& a, int BM, int ntiles,
 }
 
 // The 256-row plan of a grouped launch with the tail tiles folded in: group
-// g owns (full_g + tail_g) x ntiles consecutive logical tiles, walked in
-// runs of 8 patches (32 n-tiles): the full tiles of the run's patches (each
-// patch full_g x kPatchN tiles, rotated as in find_tile_2d_p), then the
-// run's tail tiles, one per n-tile.  A run's full tiles are 8 chunks of 32
-// tiles when full_g = 8; dealt to the 8 XCDs (xcd_chunk = 32) they run at
-// once, and the tail chunk comes next, so a tail tile reads its weight panel
-// shortly after the full tiles of its column did, from the Infinity Cache,
-// instead of streaming it from HBM after every full tile has run.  Slot h of
-// [0, span), span = all full and tail tiles x ntiles.  bm is 256 or
-// kTailRows; rows as in find_tile_2d_p and find_tail_p.  Returns false when
-// the tile holds no rows.
+// g walks its n-tiles in runs of 8 patches (kFoldRun = 32 n-tiles): the full
+// tiles of the run's patches (each patch full_g x kPatchN tiles, rotated as
+// in find_tile_2d_p), then, if the group has a tail tile, the run's tail
+// tiles, one per n-tile, padded with empty slots to kFoldRun.  A run's full
+// tiles are 8 chunks of 32 tiles when full_g = 8 and its tail tiles one more,
+// so the chunks stay aligned; dealt to the 8 XCDs (xcd_chunk = 32) a run's
+// full tiles run at once and its tail chunk comes next, so a tail tile reads
+// its weight panel shortly after the full tiles of its column did, from the
+// Infinity Cache, instead of streaming it from HBM after every full tile has
+// run.  Slot h of [0, fold_span()).  bm is 256 or kTailRows; rows as in
+// find_tile_2d_p and find_tail_p.  Returns false for a padding slot.
 constexpr int kFoldRun = 8 * kPatchN;
+__host__ __device__ inline int fold_tail_slots(int ntiles) {
+  return (ntiles + kFoldRun - 1) / kFoldRun * kFoldRun;
+}
+template <typename P>
+__host__ __device__ inline int fold_span(const P& pl, int G, int ntiles) {
+  return pl.tile(G) * ntiles + pl.tail(G) * fold_tail_slots(ntiles);
+}
 template <typename P>
 __host__ __device__ inline bool find_tile_fold_p(const GemmArgs& a, const P& pl, int ntiles, int h,
                                                  int span, int& g, int& row0, int& rows, int& nt,
                                                  int& bm) {
   const int full = span - span % 8;
   const int L = h < full ? xcd_pos(h % 8, h / 8, full / 8, a.xcd_chunk) : h;
-  int lo = 0, hi = a.G;   // (tiles+tails)[lo]*ntiles <= L < (tiles+tails)[hi]*ntiles
+  const int ts = fold_tail_slots(ntiles);
+  int lo = 0, hi = a.G;   // slots before group lo <= L < slots before group hi
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((pl.tile(mid) + pl.tail(mid)) * ntiles <= L) lo = mid;
+    if (pl.tile(mid) * ntiles + pl.tail(mid) * ts <= L) lo = mid;
     else hi = mid;
   }
   g = lo;
   const int mt_g = pl.tile(g + 1) - pl.tile(g);
-  const int rg = mt_g + pl.tail(g + 1) - pl.tail(g);
-  const int l = L - (pl.tile(g) + pl.tail(g)) * ntiles;
-  const int run = l / (rg * kFoldRun);              // runs before the last are kFoldRun wide
+  const int t_g = pl.tail(g + 1) - pl.tail(g);
+  const int l = L - (pl.tile(g) * ntiles + pl.tail(g) * ts);
+  const int run = l / ((mt_g + t_g) * kFoldRun);    // runs before the last are kFoldRun wide
   const int c0 = run * kFoldRun;
   const int width = ntiles - c0 < kFoldRun ? ntiles - c0 : kFoldRun;
-  const int r = l - run * rg * kFoldRun;
+  const int r = l - run * (mt_g + t_g) * kFoldRun;
   const int end = pl.offset(g + 1);
   if (r < mt_g * width) {
     const int pi = r / (mt_g * kPatchN);            // patches before the last are kPatchN wide
@@ -311,13 +319,14 @@ __host__ __device__ inline bool find_tile_fold_p(const GemmArgs& a, const P& pl,
     rows = end - row0;
     if (mt < mt_g - 1 && rows > 256) rows = 256;
     bm = 256;
-  } else {
-    nt = c0 + (r - mt_g * width);
-    row0 = pl.offset(g) + mt_g * 256;
-    rows = end - row0;
-    bm = kTailRows;
+    return rows > 0;
   }
-  return rows > 0;
+  const int j = r - mt_g * width;
+  nt = c0 + j;
+  row0 = pl.offset(g) + mt_g * 256;
+  rows = end - row0;
+  bm = kTailRows;
+  return j < width && rows > 0;
 }
 
 // ------------------------------------------------------------ bf16 MFMA
@@ -1550,10 +1559,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   // without split-K, a grouped launch may run its tail tiles among the full
   // tiles: the patch order then spans every tile
   const bool fold = a.fold_tails != 0 && S == 1 && a.offsets != nullptr;
-  const int span = fold ? total : real;
+  const int span = fold ? fold_span(pl, a.G, ntiles) : real;
   const int full = span - span % 8;
   const int q = full / 8;
-  const int rest = total - full;
+  const int rest = (fold ? span : total) - full;
   const int xcd = blockIdx.x & 7;
   int32_t* queue = a.queue;
 
@@ -2440,9 +2449,13 @@ hipError_t launch_grouped_ffn(const moe_problem_t& p, int rows_alloc, const void
   g1.P = bf16 ? pre : nullptr;
   g1.ldp = gu * p.d_ff;
   // the gate/up GEMM runs its tail tiles right after the full tiles of their
-  // columns, with the 8 XCDs on neighbouring chunks of one group
-  g1.fold_tails = 1;
-  g1.xcd_chunk = kXcdChunk;
+  // columns, with the 8 XCDs on neighbouring chunks of one group, when the
+  // groups average 8 row tiles or more, so that a patch fills the 32 CUs of
+  // an XCD; with fewer, the patches do not line up with the chunks anyway
+  // and the padded tail slots cost more than the re-read weight panels
+  const bool fold1 = bm == 256 && rows_alloc >= 8 * 256 * p.N;
+  g1.fold_tails = fold1 ? 1 : 0;
+  g1.xcd_chunk = fold1 ? kXcdChunk : 0;
   if ((e = run_gemm(g1, epi1, bf16, bm, mtiles_max, s)) != hipSuccess) return e;
 
   // the down GEMMs may split their tail tiles' k range (one after the other,

@@ -267,9 +267,9 @@ def test_grouped_ffn_ragged(T, N, K, d, dff, act, shared):
 TILE_SIZES = [257, 320, 321, 300, 0, 255, 1, 600, 64, 65, 576, 512]
 
 
-def _tile_case(act, T, want_tile, want_shared_tile, d=128, dff=192, dffs=128, repeat=False):
+def _tile_case(act, T, want_tile, want_shared_tile, d=128, dff=192, dffs=128, repeat=False,
+               sizes=TILE_SIZES):
     K = 4
-    sizes = TILE_SIZES
     w = W.Workload("tails", T=T, d=d, N=len(sizes), K=K, d_ff=dff, act=act, n_shared=1,
                    d_ff_shared=dffs, seed=77, dtype="bf16")
     # the launch's tile height follows the mean group size T*K/N
@@ -328,6 +328,25 @@ def test_grouped_ffn_256_row_tiles_split_k(act):
     splits its 2 tail tiles in 2.  Every row is checked, and a second call
     gives the same bits."""
     _tile_case(act, 3100, 256, 256, d=384, dff=1024, dffs=512, repeat=True)
+
+
+# Groups of about 8 row tiles: 1, 44 and 64 rows past 2048 (tail tiles after
+# 8 full tiles), 9 full tiles, an empty group, an exact 2048, groups of 1, 64
+# and 65 rows, one row short of 2048, and 10 full tiles plus a partly filled
+# one.
+FOLD_SIZES = [2049, 2092, 2112, 2304, 0, 2048, 1, 64, 65, 2047, 2600, 1800]
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_grouped_ffn_256_row_tiles_folded_tails(act):
+    """6200 tokens x top-4 over 12 experts: a mean group of 2066 rows (at
+    least 8 row tiles), so the gate/up GEMM runs its tail tiles inside the
+    tile order, after the full tiles of each run of 32 column tiles, with
+    the tail part of each run padded to 32 slots.  d_ff = 8448 gives 66
+    column tiles for SwiGLU (runs of 32, 32 and 2) and 33 for ReLU (32 and
+    1).  Every row is checked."""
+    assert 6200 * 4 >= 2048 * len(FOLD_SIZES)   # the launch folds the tail tiles
+    _tile_case(act, 6200, 256, 256, d=64, dff=8448, dffs=128, sizes=FOLD_SIZES)
 
 
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
