@@ -338,15 +338,18 @@ FOLD_SIZES = [2049, 2092, 2112, 2304, 0, 2048, 1, 64, 65, 2047, 2600, 1800]
 
 
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
-def test_grouped_ffn_256_row_tiles_folded_tails(act):
+@pytest.mark.parametrize("d,dff", [(64, 8448), (1024, 64)])
+def test_grouped_ffn_256_row_tiles_folded_tails(act, d, dff):
     """6200 tokens x top-4 over 12 experts: a mean group of 2066 rows (at
     least 8 row tiles), so the gate/up GEMM runs its tail tiles inside the
     tile order, after the full tiles of each run of 32 column tiles, with
     the tail part of each run padded to 32 slots.  d_ff = 8448 gives 66
     column tiles for SwiGLU (runs of 32, 32 and 2) and 33 for ReLU (32 and
-    1).  Every row is checked."""
+    1).  With d = 1024 the down GEMM has 67 row tiles x 4 column tiles, 33
+    a run per XCD, so its 32-tile chunks are dealt round-robin.  Every row
+    is checked."""
     assert 6200 * 4 >= 2048 * len(FOLD_SIZES)   # the launch folds the tail tiles
-    _tile_case(act, 6200, 256, 256, d=64, dff=8448, dffs=128, sizes=FOLD_SIZES)
+    _tile_case(act, 6200, 256, 256, d=d, dff=dff, dffs=128, sizes=FOLD_SIZES)
 
 
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
