@@ -1571,18 +1571,26 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_ring_kernel(GemmArgs ga
   // the own run requested at the previous claim (-1: none), whose value is
   // used one tile later, when it has long arrived
   int cur = 0, pending = -1;
+  // Only thread 0 claims.  The compiler cannot tell, and would aggregate
+  // each atomic over the wave: it then rebuilds a per-lane result from the
+  // returned value right after the atomic, so the reservation one tile ahead
+  // would be waited for at once.  An offset it cannot prove uniform (zero at
+  // run time) keeps the atomics plain; the reserved position is then waited
+  // for only where it is used, a tile later.
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
   auto claim = [&]() -> int {
     int spec = pending;
     int h = -1;
     while (cur < 9) {
       const int y = cur < 8 ? (xcd + cur) & 7 : 8;
-      const int t = (cur == 0 && spec >= 0) ? spec : atomicAdd(&queue[y], 1);
+      const int t = (cur == 0 && spec >= 0) ? spec : atomicAdd(&queue[y + zero], 1);
       spec = -1;
       h = queue_slot(y, t, q, full, rest);
       if (h >= 0) break;
       ++cur;
     }
-    pending = cur == 0 ? atomicAdd(&queue[xcd], 1) : -1;
+    pending = cur == 0 ? atomicAdd(&queue[xcd + zero], 1) : -1;
     return h;
   };
   // a tile of the 1-D space: coordinates, height class (256, 64) and k
