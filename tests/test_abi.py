@@ -361,3 +361,19 @@ def test_noalloc_scratch_size_and_refusal():
     assert call(good(T=0)) == M.MOE_OK
     assert L.moe_layer_forward_noalloc(ctypes.byref(good()), fake(1), None, None, ctypes.byref(outs),
                                        fake(2), None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU: asked for more (by flag or by a
+    launcher's WORLD_SIZE) it exits with status 2 and says so, before it
+    touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for extra_env, args in (({}, ["--gpus", "2"]), ({"WORLD_SIZE": "4"}, [])):
+        env = dict(os.environ, **extra_env)
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + args, env=env,
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU" in r.stderr
+        assert r.stdout == ""
