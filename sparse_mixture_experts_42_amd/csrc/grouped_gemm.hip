@@ -2566,20 +2566,23 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(const float* P, int ldp, c
                                                       int ldc2) {
   const long long R = nrows_dev != nullptr ? *nrows_dev : nrows;
   const int cpr = dff / 8;
-  const long long total = R * cpr;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (long long)gridDim.x * 256) {
-    const long long r = i / cpr;
-    const int c = (int)(i - r * cpr) * 8;
+  // 8 columns of one row per item; P and dA are read once, so their loads
+  // are non-temporal
+  auto item = [&](long long r, int c) {
     const float* pg = P + r * ldp + c;
     float g[8], v[8], da[8];
-    *reinterpret_cast<float4*>(&g[0]) = *reinterpret_cast<const float4*>(pg);
-    *reinterpret_cast<float4*>(&g[4]) = *reinterpret_cast<const float4*>(pg + 4);
+    auto ld4 = [](const float* q, float* out) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(x[j]);
+    };
+    ld4(pg, &g[0]);
+    ld4(pg + 4, &g[4]);
     if constexpr (SWIGLU) {
-      *reinterpret_cast<float4*>(&v[0]) = *reinterpret_cast<const float4*>(pg + dff);
-      *reinterpret_cast<float4*>(&v[4]) = *reinterpret_cast<const float4*>(pg + dff + 4);
+      ld4(pg + dff, &v[0]);
+      ld4(pg + dff + 4, &v[4]);
     }
-    const u32x4 dq = *reinterpret_cast<const u32x4*>(dA + r * ldd + c);
+    const u32x4 dq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dA + r * ldd + c));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       da[2 * q] = __uint_as_float(dq[q] << 16);
@@ -2605,6 +2608,22 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(const float* P, int ldp, c
     *reinterpret_cast<u32x4*>(dgu + r * ldc2 + c) = u32x4{wg[0], wg[1], wg[2], wg[3]};
     if constexpr (SWIGLU)
       *reinterpret_cast<u32x4*>(dgu + r * ldc2 + dff + c) = u32x4{wu[0], wu[1], wu[2], wu[3]};
+  };
+  const long long total = R * cpr;
+  if (total + (long long)gridDim.x * 256 < (1ll << 31)) {
+    // 32-bit item index (the stride cannot overflow it): the division by
+    // cpr stays a short 32-bit sequence
+    const int tot = (int)total;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < tot; i += gridDim.x * 256) {
+      const int r = i / cpr;
+      item(r, (i - r * cpr) * 8);
+    }
+  } else {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256) {
+      const long long r = i / cpr;
+      item(r, (int)(i - r * cpr) * 8);
+    }
   }
 }
 
